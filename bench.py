@@ -1,0 +1,188 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused MoE-LoRA layer (align + forward) on one MI355X.
+
+Prints ONE JSON line: tokens/s of the whole layer, the roofline position of
+the dominant kernel (HIP-event durations measured inside the timed region),
+and the CPU reference timed on the host cores as a baseline.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
+
+Default workload: the pages' illustrative expert (hidden 4096, intermediate
+11008, rank 32), 8 experts top-2, 8 adapters, 16 decode tokens.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-LoRA layer tokens/s at 1 GPU; % HBM roofline (decode) / % MFMA peak (prefill)"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=2, help="synthetic workload number 1..5")
+    ap.add_argument("--block-m", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="target CPU time of the reference baseline sample")
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="only run a plain device copy of this many MB (counter calibration)")
+    return ap.parse_args()
+
+
+def stage_bytes_flops(wl, work):
+    """Algorithmic bytes and flops of each kernel stage for this instance."""
+    T, H, I, k, r = wl.T, wl.H, wl.I, wl.topk, wl.r
+    b = work["bytes_parts"]
+    P, P_l = work["P"], work["P_l"]
+    return {
+        "gemm_gate_up": dict(bytes=b["W_gu"] + b["B_gu"] + T * H * 2 + P_l * r * 4 + P * I * 2,
+                             flops=2 * P * 2 * I * H + 2 * P_l * 2 * I * r),
+        "gemm_down": dict(bytes=b["W_down"] + b["B_down"] + P * I * 2 + P_l * r * 4 + P * H * 4,
+                          flops=2 * P * H * I + 2 * P_l * H * r),
+        "shrink_gate_up": dict(bytes=b["A_gu"] + P_l * H * 2 + P_l * r * 4, flops=2 * P_l * r * H),
+        "shrink_down": dict(bytes=b["A_down"] + P_l * I * 2 + P_l * r * 4, flops=2 * P_l * r * I),
+        "combine": dict(bytes=P * H * 4 + T * H * 2, flops=P * H),
+    }
+
+
+def copy_probe(mb):
+    import torch
+    n = mb * (1 << 20) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4,
+                      "launches": 5}), flush=True)
+
+
+def cpu_baseline(inp, target_s):
+    """The fp64 reference on the host cores over a bounded sample of the same
+    workload's tokens; returns tokens/s and what was run."""
+    import numpy as np
+
+    import oracle
+    import synth
+    wl = inp.wl
+    nthreads = oracle.default_threads()
+    o = oracle.Oracle()
+    # calibrate with one token per thread, then size the sample for ~target_s
+    n0 = min(wl.T, nthreads)
+    toks = np.arange(n0, dtype=np.int32)
+    synth.host_slabs_for_tokens(inp, np.arange(wl.T))
+    t0 = time.perf_counter()
+    oracle.layer_from_inputs(inp, tokens=toks, oracle=o, nthreads=nthreads)
+    dt = time.perf_counter() - t0
+    n = n0 * max(1, int(round(target_s / max(dt, 1e-3))))
+    toks = (np.arange(n) % wl.T).astype(np.int32)
+    t0 = time.perf_counter()
+    oracle.layer_from_inputs(inp, tokens=toks, oracle=o, nthreads=nthreads)
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
+            "sample": f"{n} token evaluations of workload {wl.name} (tokens cycled 0..{wl.T - 1}),"
+                      f" fp64, {dt:.1f} s wall"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(collectives and sharding are out of scope); rerun with --gpus 1.",
+              file=sys.stderr, flush=True)
+        sys.exit(2)
+    import torch
+
+    if args.copy_probe_mb:
+        copy_probe(args.copy_probe_mb)
+        return
+    import lora_moe_amd as lm
+    import synth
+
+    lm.load_library()
+    wl = synth.WORKLOADS[args.workload]
+    print(f"bench: generating workload {args.workload} ({wl.name}) on the device", file=sys.stderr,
+          flush=True)
+    dev, inp = synth.device_inputs(wl, touched_only=True)
+    work = synth.algorithmic_work(wl, inp.topk_ids, inp.lora_ids)
+    shape = lm.make_shape(wl.T, wl.H, wl.I, wl.E, wl.topk, wl.L, wl.r, args.block_m, wl.scale)
+    ws = lm.alloc_workspace(shape)
+    y = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        lm.moe_lora_align(shape, dev["topk_ids"], dev["lora_ids"], ws, stream)
+        lm.moe_lora_forward(shape, dev["x"], dev["topk_ids"], dev["topk_weights"], dev["lora_ids"],
+                            dev["W_gu"], dev["W_down"], dev["A_gu"], dev["B_gu"], dev["A_down"],
+                            dev["B_down"], ws, y, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"bench: warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+
+    lm.moe_lora_profile_begin(args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    stage_ms, calls = lm.moe_lora_profile_end()
+    print(f"bench: timed {args.steps} steps in {elapsed:.3f} s", file=sys.stderr, flush=True)
+
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = wl.T * args.steps / elapsed
+    per_stage = {k: v / max(calls, 1) for k, v in stage_ms.items()}
+    sbf = stage_bytes_flops(wl, work)
+    dom = max(sbf, key=lambda s: per_stage.get(s, 0.0))
+    dur_s = per_stage[dom] * 1e-3
+    ai = sbf[dom]["flops"] / max(sbf[dom]["bytes"], 1)
+    ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if ai < ridge:
+        achieved = sbf[dom]["bytes"] / dur_s / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS}
+    else:
+        achieved = sbf[dom]["flops"] / dur_s / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS}
+    roof.update({"kernel": dom, "avg_launch_ms": per_stage[dom],
+                 "alg_bytes_per_launch": sbf[dom]["bytes"], "alg_flops_per_launch": sbf[dom]["flops"],
+                 "traffic": None})
+    layer_s = ms_per_step * 1e-3
+    out = {
+        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "I": wl.I, "E": wl.E,
+                   "topk": wl.topk, "L": wl.L, "r": wl.r,
+                   "block_m": lm.moe_lora_resolve_block_m(shape), "seed": wl.seed},
+        "roofline": roof,
+        "layer": {"alg_bytes": work["bytes"], "alg_flops": work["flops"],
+                  "hbm_frac": work["bytes"] / layer_s / (HBM_PEAK_GBS * 1e9),
+                  "mfma_frac": work["flops"] / layer_s / (MFMA_BF16_PEAK_TFLOPS * 1e12),
+                  "experts_touched": work["experts_touched"],
+                  "adapter_expert_pairs_touched": work["pairs_touched"]},
+        "stages_ms": per_stage,
+    }
+    if not args.no_cpu_baseline:
+        print("bench: timing the CPU reference", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,160 @@
+/* moe_lora.h -- C ABI of the fused MoE-LoRA layer for AMD MI355X (gfx950).
+ *
+ * The layer (vLLM blog "Multi-LoRA for MoE models", vllm.com.cn, 2026-02-26,
+ * section "Implementing multi-LoRA inference for MoE models in vLLM",
+ * Figure 1 and the equation y = xW + xAB): every token t is routed to topk
+ * experts with weights w[t][j] and carries the adapter id of its request.
+ * For each routed pair (t, e) with adapter l:
+ *     g  = x[t] W_gu[e]  + s * (x[t] A_gu[l][e]) B_gu[l][e]      (gate_up, 2I wide)
+ *     h  = silu(g[0:I]) * g[I:2I]                                 (SiLU gate)
+ *     d  = h W_down[e]   + s * (h A_down[l][e]) B_down[l][e]      (down, H wide)
+ *     y[t] = sum_j w[t][j] * d(t, e_j)                            (top-k combine)
+ * The products with A are the LoRA "shrink" ops (h_in -> r) and the products
+ * with B the "expand" ops (r -> h_out), four per expert (same section).  The
+ * adapter is skipped for tokens whose id is -1.
+ *
+ * Conventions for every call:
+ *   - Pointers named as device pointers must point to device memory of the
+ *     current HIP device; `stream` is a hipStream_t (NULL = default stream).
+ *   - Calls that take a stream are asynchronous: host-side checks run first
+ *     and return an error code WITHOUT launching anything; otherwise the work
+ *     is enqueued and the call returns MOE_LORA_OK.  Nothing allocates device
+ *     memory; all scratch lives in the caller's workspace.
+ *   - The caller owns every buffer and must keep it alive until the stream
+ *     has passed the call.  Two calls that share a workspace must be ordered
+ *     on one stream.
+ *   - bf16 tensors are passed as uint16_t bit patterns.  Weights are stored
+ *     with the reduction index contiguous, i.e. as the transposes of the
+ *     pages' h_in x h_out matrices:
+ *         W_gu   [E][2I][H]    rows 0..I-1 = gate, rows I..2I-1 = up
+ *         W_down [E][H][I]
+ *         A_gu   [L][E][r][H]      B_gu   [L][E][2I][r]
+ *         A_down [L][E][r][I]      B_down [L][E][H][r]
+ *   - H, I and r must be multiples of 8 and every tensor pointer 16-byte
+ *     aligned (whole 16-byte vector loads).
+ */
+#ifndef MOE_LORA_H
+#define MOE_LORA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define MOE_LORA_OK 0
+#define MOE_LORA_EINVAL (-1)       /* null pointer, negative or zero size, topk > E, bad block_m */
+#define MOE_LORA_EALIGN (-2)       /* pointer not 16-byte aligned, H or I not a multiple of 8    */
+#define MOE_LORA_EWORKSPACE (-3)   /* workspace smaller than moe_lora_workspace_bytes()          */
+#define MOE_LORA_EUNSUPPORTED (-4) /* r not a multiple of 8 or r > 128; E*(L+1) > 14336          */
+#define MOE_LORA_EHIP (-5)         /* a HIP runtime call or kernel launch failed                 */
+
+/* Layer sizes.  T may be 0 (every call is then a no-op). */
+typedef struct moe_lora_shape {
+  int32_t T;        /* tokens                                                     */
+  int32_t H;        /* hidden size: h_in of gate_up, h_out of down                */
+  int32_t I;        /* per-expert intermediate size; gate_up produces 2I values   */
+  int32_t E;        /* experts                                                    */
+  int32_t topk;     /* experts per token, 1 <= topk <= E                          */
+  int32_t L;        /* adapters resident in the A/B stacks (>= 1)                 */
+  int32_t r;        /* adapter rank                                               */
+  int32_t block_m;  /* rows per block shared by every op of the layer: one of     */
+                    /* 16, 32, 64, 128, 256, or 0 to choose it from the shape     */
+  float lora_scale; /* s above                                                    */
+} moe_lora_shape;
+
+/* Device pointers into a workspace (see moe_lora_workspace_view). */
+typedef struct moe_lora_views {
+  int32_t* sorted_ids;   /* [cap_rows] pair id p = t*topk + j per row; sentinel P = T*topk   */
+  int32_t* expert_off;   /* [E+1] first row of each expert's run (runs padded to block_m)    */
+  int32_t* seg_start;    /* [E*(L+1)] first row of (expert e, slot s) at e*(L+1)+s; slot = l  */
+  int32_t* seg_cnt;      /* [E*(L+1)] pairs in that segment; slot L = tokens without adapter */
+  int32_t* block_expert; /* [cap_blocks] expert of each block_m-row block, -1 when unused    */
+  int32_t* pos_of_pair;  /* [T*topk] row of each pair, -1 when its expert id is invalid      */
+  int32_t* num_padded;   /* [1] rows in use = expert_off[E]                                  */
+  int32_t* err_count;    /* [1] invalid expert ids (per pair) + invalid adapter ids (per token) */
+  float* z_gu;           /* [cap_rows][r] gate_up shrink result per row (adapter rows only)  */
+  float* z_down;         /* [cap_rows][r] down shrink result per row (adapter rows only)     */
+  uint16_t* h;           /* [cap_rows][I] bf16 SiLU-gate output per row                      */
+  float* d;              /* [cap_rows][H] down output per row, already times w[t][j]         */
+  int64_t cap_rows;      /* T*topk + E*(block_m-1)                                           */
+  int64_t cap_blocks;    /* ceil(cap_rows / block_m)                                         */
+  int32_t block_m;       /* block size in effect (resolved when the shape says 0)           */
+} moe_lora_views;
+
+/* block_m used for this shape (the shape's own value when non-zero), or a
+ * negative status when the shape is invalid.  Host only, pure. */
+int moe_lora_resolve_block_m(const moe_lora_shape* shape);
+
+/* Bytes of device workspace that moe_lora_align / moe_lora_forward need for
+ * this shape, or 0 when the shape is invalid.  Host only, pure. */
+size_t moe_lora_workspace_bytes(const moe_lora_shape* shape);
+
+/* (expert, adapter) align: a stable counting sort of the T*topk (token, slot)
+ * pairs by key (expert, adapter slot), slot = adapter id or L for "no
+ * adapter".  Each expert's pairs form one run, adapter groups within it are
+ * contiguous segments in adapter order (no-adapter last), pairs keep
+ * ascending p = t*topk + j inside a segment, and each run is padded to a
+ * multiple of block_m with the sentinel T*topk.  One block size is shared by
+ * every op of the layer (vLLM blog, section "Tuning kernel configurations for
+ * Amazon SageMaker AI and Amazon Bedrock": the four LoRA ops share
+ * BLOCK_SIZE_M).  The adapter dimension of the sort is the pages' extra grid
+ * dimension over active adapters (section "Implementing multi-LoRA ...").
+ *
+ *   topk_ids  device [T][topk] int32 expert ids; ids outside [0,E) drop the pair
+ *   lora_ids  device [T] int32 adapter ids; -1 = none; ids outside [-1,L) are
+ *             treated as none
+ *   workspace device, ws_bytes >= moe_lora_workspace_bytes(shape)
+ * Writes the align outputs into the workspace (bit-exact, deterministic) and
+ * clears the shrink accumulators.  Invalid ids are counted (see
+ * moe_lora_device_errors), never fatal. */
+int moe_lora_align(const moe_lora_shape* shape, const int32_t* topk_ids, const int32_t* lora_ids,
+                   void* workspace, size_t ws_bytes, void* stream);
+
+/* Typed device pointers into `workspace` for this shape (host only, no GPU
+ * work).  For tests and tools that inspect the align or intermediates. */
+int moe_lora_workspace_view(const moe_lora_shape* shape, void* workspace, moe_lora_views* out);
+
+/* The layer forward.  Requires a preceding moe_lora_align with the same
+ * shape, ids and workspace on the same stream.
+ *   x            device [T][H] bf16
+ *   topk_ids     device [T][topk] int32 (as given to the align)
+ *   topk_weights device [T][topk] float
+ *   lora_ids     device [T] int32 (as given to the align)
+ *   W_gu, W_down, A_gu, B_gu, A_down, B_down   device bf16, layouts above
+ *   y            device [T][H] bf16 output, overwritten (round to nearest even)
+ * Accumulation is fp32 everywhere; the gate_up result stays fp32 through the
+ * SiLU; h is stored bf16.  With split-K shrinks the fp32 sums are added with
+ * atomics, so y may differ between runs in the last bits. */
+int moe_lora_forward(const moe_lora_shape* shape, const uint16_t* x, const int32_t* topk_ids,
+                     const float* topk_weights, const int32_t* lora_ids, const uint16_t* W_gu,
+                     const uint16_t* W_down, const uint16_t* A_gu, const uint16_t* B_gu,
+                     const uint16_t* A_down, const uint16_t* B_down, void* workspace,
+                     size_t ws_bytes, uint16_t* y, void* stream);
+
+/* Number of invalid ids the last align on `workspace` met.  Synchronises
+ * `stream` (the only call here that waits for the GPU). */
+int moe_lora_device_errors(const moe_lora_shape* shape, const void* workspace,
+                           int32_t* host_count, void* stream);
+
+/* Human-readable name of a status code (static string). */
+const char* moe_lora_status_str(int status);
+
+/* Stage timing with HIP events, for benchmarks.  moe_lora_profile_begin
+ * creates events for up to max_calls align+forward calls and starts
+ * recording around every kernel launch of later calls (on their streams);
+ * moe_lora_profile_end waits for the recorded events, writes the summed time
+ * of each stage in milliseconds to stage_ms[0..n) (n <= moe_lora_stage_count())
+ * and the number of recorded calls to *calls, then stops recording.
+ * Process-wide state: not for concurrent use from several host threads. */
+int moe_lora_stage_count(void);
+const char* moe_lora_stage_name(int stage);
+int moe_lora_profile_begin(int max_calls);
+int moe_lora_profile_end(float* stage_ms, int n, int* calls);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_LORA_H */

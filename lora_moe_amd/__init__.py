@@ -1,0 +1,243 @@
+"""Python binding of the MoE-LoRA C ABI (``include/moe_lora.h``).
+
+Argument marshalling only: every step of the layer runs in the HIP kernels of
+``libmoe_lora.so``.  Functions carry the C names; tensors are torch tensors on
+the current HIP device (PyTorch supplies device memory and streams).  Loading
+fails loudly when the library has not been built -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmoe_lora.so")
+
+MOE_LORA_OK = 0
+MOE_LORA_EINVAL = -1
+MOE_LORA_EALIGN = -2
+MOE_LORA_EWORKSPACE = -3
+MOE_LORA_EUNSUPPORTED = -4
+MOE_LORA_EHIP = -5
+
+_lib = None
+
+
+class MoeLoraError(RuntimeError):
+    def __init__(self, func: str, code: int):
+        self.code = code
+        super().__init__(f"{func} failed: {moe_lora_status_str(code)} ({code})")
+
+
+class moe_lora_shape(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("H", ctypes.c_int32), ("I", ctypes.c_int32),
+                ("E", ctypes.c_int32), ("topk", ctypes.c_int32), ("L", ctypes.c_int32),
+                ("r", ctypes.c_int32), ("block_m", ctypes.c_int32),
+                ("lora_scale", ctypes.c_float)]
+
+    def __repr__(self):
+        return ("moe_lora_shape(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_)
+                + ")")
+
+
+class moe_lora_views(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "sorted_ids", "expert_off", "seg_start", "seg_cnt", "block_expert", "pos_of_pair",
+        "num_padded", "err_count", "z_gu", "z_down", "h", "d")] + [
+        ("cap_rows", ctypes.c_int64), ("cap_blocks", ctypes.c_int64), ("block_m", ctypes.c_int32)]
+
+
+def make_shape(T, H, I, E, topk, L, r, block_m=0, lora_scale=1.0) -> moe_lora_shape:
+    return moe_lora_shape(int(T), int(H), int(I), int(E), int(topk), int(L), int(r), int(block_m),
+                          float(lora_scale))
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libmoe_lora.so (raises when it is missing: build it first)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} not found: build the HIP library first "
+                           "(python -c 'import __graft_entry__ as g; g.build()')")
+    lib = ctypes.CDLL(path)
+    vp, sp = ctypes.c_void_p, ctypes.POINTER(moe_lora_shape)
+    i32 = ctypes.c_int
+    lib.moe_lora_resolve_block_m.argtypes = [sp]
+    lib.moe_lora_resolve_block_m.restype = i32
+    lib.moe_lora_workspace_bytes.argtypes = [sp]
+    lib.moe_lora_workspace_bytes.restype = ctypes.c_size_t
+    lib.moe_lora_align.argtypes = [sp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.moe_lora_align.restype = i32
+    lib.moe_lora_workspace_view.argtypes = [sp, vp, ctypes.POINTER(moe_lora_views)]
+    lib.moe_lora_workspace_view.restype = i32
+    lib.moe_lora_forward.argtypes = [sp] + [vp] * 11 + [ctypes.c_size_t, vp, vp]
+    lib.moe_lora_forward.restype = i32
+    lib.moe_lora_device_errors.argtypes = [sp, vp, ctypes.POINTER(ctypes.c_int32), vp]
+    lib.moe_lora_device_errors.restype = i32
+    lib.moe_lora_status_str.argtypes = [i32]
+    lib.moe_lora_status_str.restype = ctypes.c_char_p
+    lib.moe_lora_stage_count.argtypes = []
+    lib.moe_lora_stage_count.restype = i32
+    lib.moe_lora_stage_name.argtypes = [i32]
+    lib.moe_lora_stage_name.restype = ctypes.c_char_p
+    lib.moe_lora_profile_begin.argtypes = [i32]
+    lib.moe_lora_profile_begin.restype = i32
+    lib.moe_lora_profile_end.argtypes = [ctypes.POINTER(ctypes.c_float), i32,
+                                         ctypes.POINTER(ctypes.c_int)]
+    lib.moe_lora_profile_end.restype = i32
+    _lib = lib
+    return lib
+
+
+def _check(func: str, code: int):
+    if code != MOE_LORA_OK:
+        raise MoeLoraError(func, code)
+
+
+def _ptr(t, name: str):
+    """Device address of a contiguous tensor (None -> NULL)."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def moe_lora_status_str(code: int) -> str:
+    return load_library().moe_lora_status_str(int(code)).decode()
+
+
+def moe_lora_resolve_block_m(shape: moe_lora_shape) -> int:
+    return load_library().moe_lora_resolve_block_m(ctypes.byref(shape))
+
+
+def moe_lora_workspace_bytes(shape: moe_lora_shape) -> int:
+    return int(load_library().moe_lora_workspace_bytes(ctypes.byref(shape)))
+
+
+def alloc_workspace(shape: moe_lora_shape, device="cuda"):
+    import torch
+    n = moe_lora_workspace_bytes(shape)
+    if n == 0:
+        raise MoeLoraError("moe_lora_workspace_bytes", MOE_LORA_EINVAL)
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def moe_lora_align(shape, topk_ids, lora_ids, workspace, stream=None) -> None:
+    _check("moe_lora_align", load_library().moe_lora_align(
+        ctypes.byref(shape), _ptr(topk_ids, "topk_ids"), _ptr(lora_ids, "lora_ids"),
+        _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
+
+
+def moe_lora_forward(shape, x, topk_ids, topk_weights, lora_ids, W_gu, W_down, A_gu, B_gu,
+                     A_down, B_down, workspace, y, stream=None) -> None:
+    _check("moe_lora_forward", load_library().moe_lora_forward(
+        ctypes.byref(shape), _ptr(x, "x"), _ptr(topk_ids, "topk_ids"),
+        _ptr(topk_weights, "topk_weights"), _ptr(lora_ids, "lora_ids"), _ptr(W_gu, "W_gu"),
+        _ptr(W_down, "W_down"), _ptr(A_gu, "A_gu"), _ptr(B_gu, "B_gu"), _ptr(A_down, "A_down"),
+        _ptr(B_down, "B_down"), _ptr(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _ptr(y, "y"), _stream(stream)))
+
+
+def moe_lora_workspace_view(shape, workspace) -> moe_lora_views:
+    v = moe_lora_views()
+    _check("moe_lora_workspace_view", load_library().moe_lora_workspace_view(
+        ctypes.byref(shape), _ptr(workspace, "workspace"), ctypes.byref(v)))
+    return v
+
+
+def workspace_tensors(shape, workspace) -> dict:
+    """The workspace regions of ``moe_lora_workspace_view`` as torch views of
+    ``workspace`` (a uint8 device tensor)."""
+    import torch
+    v = moe_lora_workspace_view(shape, workspace)
+    base = workspace.data_ptr()
+    P = shape.T * shape.topk
+    NB = shape.E * (shape.L + 1)
+    cap, capb = v.cap_rows, v.cap_blocks
+
+    def region(addr, n, dtype):
+        nbytes = n * torch.empty((), dtype=dtype).element_size()
+        off = addr - base
+        return workspace[off:off + nbytes].view(dtype)
+
+    return dict(
+        sorted_ids=region(v.sorted_ids, cap, torch.int32),
+        expert_off=region(v.expert_off, shape.E + 1, torch.int32),
+        seg_start=region(v.seg_start, NB, torch.int32),
+        seg_cnt=region(v.seg_cnt, NB, torch.int32),
+        block_expert=region(v.block_expert, capb, torch.int32),
+        pos_of_pair=region(v.pos_of_pair, P, torch.int32),
+        num_padded=region(v.num_padded, 1, torch.int32),
+        err_count=region(v.err_count, 1, torch.int32),
+        z_gu=region(v.z_gu, cap * shape.r, torch.float32).view(cap, shape.r),
+        z_down=region(v.z_down, cap * shape.r, torch.float32).view(cap, shape.r),
+        h=region(v.h, cap * shape.I, torch.bfloat16).view(cap, shape.I),
+        d=region(v.d, cap * shape.H, torch.float32).view(cap, shape.H),
+        cap_rows=cap, cap_blocks=capb, block_m=v.block_m)
+
+
+def moe_lora_device_errors(shape, workspace, stream=None) -> int:
+    n = ctypes.c_int32(0)
+    _check("moe_lora_device_errors", load_library().moe_lora_device_errors(
+        ctypes.byref(shape), _ptr(workspace, "workspace"), ctypes.byref(n), _stream(stream)))
+    return int(n.value)
+
+
+def moe_lora_stage_count() -> int:
+    return load_library().moe_lora_stage_count()
+
+
+def moe_lora_stage_name(i: int) -> str:
+    return load_library().moe_lora_stage_name(int(i)).decode()
+
+
+def moe_lora_profile_begin(max_calls: int) -> None:
+    _check("moe_lora_profile_begin", load_library().moe_lora_profile_begin(int(max_calls)))
+
+
+def moe_lora_profile_end() -> tuple[dict, int]:
+    """Summed milliseconds per stage name, and the number of recorded calls."""
+    n = moe_lora_stage_count()
+    arr = (ctypes.c_float * n)()
+    calls = ctypes.c_int(0)
+    _check("moe_lora_profile_end", load_library().moe_lora_profile_end(arr, n, ctypes.byref(calls)))
+    return {moe_lora_stage_name(i): float(arr[i]) for i in range(n)}, int(calls.value)
+
+
+def fused_moe_lora(x, topk_ids, topk_weights, lora_ids, W_gu, W_down, A_gu, B_gu, A_down, B_down,
+                   lora_scale=1.0, block_m=0, workspace=None, y=None, stream=None):
+    """Align + forward on the current stream; returns y [T, H] (bf16).
+
+    x [T,H] bf16; topk_ids [T,k] int32; topk_weights [T,k] fp32; lora_ids [T]
+    int32; W_gu [E,2I,H]; W_down [E,H,I]; A_gu [L,E,r,H]; B_gu [L,E,2I,r];
+    A_down [L,E,r,I]; B_down [L,E,H,r] (all bf16)."""
+    import torch
+    T, H = x.shape
+    E, twoI, _ = W_gu.shape
+    L, _, r, _ = A_gu.shape
+    shape = make_shape(T, H, twoI // 2, E, topk_ids.shape[1], L, r, block_m, lora_scale)
+    if workspace is None:
+        workspace = alloc_workspace(shape, x.device)
+    if y is None:
+        y = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    moe_lora_align(shape, topk_ids, lora_ids, workspace, stream)
+    moe_lora_forward(shape, x, topk_ids, topk_weights, lora_ids, W_gu, W_down, A_gu, B_gu, A_down,
+                     B_down, workspace, y, stream)
+    return y
+
+
+__all__ = [n for n in dir() if n.startswith("moe_lora") or n in (
+    "make_shape", "alloc_workspace", "workspace_tensors", "fused_moe_lora", "load_library",
+    "MoeLoraError")]

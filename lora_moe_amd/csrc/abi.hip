@@ -1,0 +1,298 @@
+// C ABI of the MoE-LoRA library: argument checks, workspace layout, stage
+// dispatch and stage timing.  Declarations and contracts: include/moe_lora.h.
+#include <algorithm>
+#include <vector>
+
+#include "internal.h"
+
+namespace moelora {
+
+static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+static int check_shape(const moe_lora_shape* s) {
+  if (!s) return MOE_LORA_EINVAL;
+  if (s->T < 0 || s->H <= 0 || s->I <= 0 || s->E <= 0 || s->topk <= 0 || s->topk > s->E ||
+      s->L <= 0 || s->r <= 0)
+    return MOE_LORA_EINVAL;
+  const int bm = s->block_m;
+  if (!(bm == 0 || bm == 16 || bm == 32 || bm == 64 || bm == 128 || bm == 256)) return MOE_LORA_EINVAL;
+  if (s->H % 8 || s->I % 8) return MOE_LORA_EALIGN;
+  if (s->r % 8 || s->r > 128) return MOE_LORA_EUNSUPPORTED;
+  if ((int64_t)s->E * (s->L + 1) > kAlignMaxBuckets) return MOE_LORA_EUNSUPPORTED;
+  // every index into the row-major buffers must fit the kernels' int arithmetic
+  const int64_t P = (int64_t)s->T * s->topk;
+  const int64_t cap = P + (int64_t)s->E * 255;
+  if (P > (1LL << 30) || cap > (1LL << 30) || (int64_t)s->H * s->I > (1LL << 40))
+    return MOE_LORA_EUNSUPPORTED;
+  return MOE_LORA_OK;
+}
+
+static int resolve_bm(const moe_lora_shape* s) {
+  if (s->block_m) return s->block_m;
+  // rows per touched expert, if routing were even
+  const int64_t P = (int64_t)s->T * s->topk;
+  const int64_t touched = std::max<int64_t>(1, std::min<int64_t>(s->E, P));
+  const int64_t rows = (P + touched - 1) / touched;
+  if (rows <= 16) return 16;
+  if (rows <= 32) return 32;
+  return 64;
+}
+
+int make_layout(const moe_lora_shape* s, Layout* L) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  L->T = s->T;
+  L->H = s->H;
+  L->I = s->I;
+  L->E = s->E;
+  L->k = s->topk;
+  L->L = s->L;
+  L->r = s->r;
+  L->bm = resolve_bm(s);
+  L->s = s->lora_scale;
+  L->P = (int64_t)s->T * s->topk;
+  L->cap_rows = L->P + (int64_t)L->E * (L->bm - 1);
+  L->cap_blocks = (L->cap_rows + L->bm - 1) / L->bm;
+  L->NB = (int64_t)L->E * (L->L + 1);
+  L->C = std::max<int64_t>(1, (L->P + kAlignChunk - 1) / kAlignChunk);
+  L->TS = L->r > 64 ? 16 : std::min(64, std::max(16, L->bm));
+  L->max_tiles = (L->P + L->TS - 1) / L->TS + std::min<int64_t>((int64_t)L->E * L->L, L->P);
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = align_up(o + std::max<size_t>(bytes, 1), 256);
+    return at;
+  };
+  L->off_hdr = take(sizeof(int32_t) * kHdrInts);
+  L->off_sorted = take(sizeof(int32_t) * L->cap_rows);
+  L->off_eoff = take(sizeof(int32_t) * (L->E + 1));
+  L->off_segstart = take(sizeof(int32_t) * L->NB);
+  L->off_segcnt = take(sizeof(int32_t) * L->NB);
+  L->off_bexp = take(sizeof(int32_t) * L->cap_blocks);
+  L->off_pos = take(sizeof(int32_t) * L->P);
+  L->off_chunk = take(sizeof(int32_t) * L->NB * L->C);
+  L->off_chunkerr = take(sizeof(int32_t) * L->C);
+  L->off_rank = take(sizeof(int32_t) * L->P);
+  L->off_tiles = take(sizeof(LoraTile) * L->max_tiles);
+  L->off_zgu = take(sizeof(float) * L->cap_rows * L->r);
+  L->off_zd = take(sizeof(float) * L->cap_rows * L->r);
+  L->off_h = take(sizeof(uint16_t) * L->cap_rows * L->I);
+  L->off_d = take(sizeof(float) * L->cap_rows * L->H);
+  L->total = o;
+  return MOE_LORA_OK;
+}
+
+// ------------------------------------------------------------------ stage timing
+
+namespace {
+struct Profiler {
+  bool on = false;
+  int max_calls = 0;
+  int call = 0;
+  std::vector<hipEvent_t> ev;  // [call][stage][start, stop]
+  std::vector<uint32_t> recorded;
+};
+Profiler g_prof;
+
+void prof_release() {
+  for (hipEvent_t e : g_prof.ev) hipEventDestroy(e);
+  g_prof.ev.clear();
+  g_prof.recorded.clear();
+  g_prof.on = false;
+  g_prof.max_calls = g_prof.call = 0;
+}
+}  // namespace
+
+void prof_stage_begin(int stage, hipStream_t st) {
+  if (!g_prof.on || g_prof.call >= g_prof.max_calls) return;
+  hipEventRecord(g_prof.ev[((size_t)g_prof.call * ST_COUNT + stage) * 2], st);
+}
+
+void prof_stage_end(int stage, hipStream_t st) {
+  if (!g_prof.on || g_prof.call >= g_prof.max_calls) return;
+  hipEventRecord(g_prof.ev[((size_t)g_prof.call * ST_COUNT + stage) * 2 + 1], st);
+  g_prof.recorded[g_prof.call] |= 1u << stage;
+}
+
+void prof_call_done() {
+  if (g_prof.on && g_prof.call < g_prof.max_calls) g_prof.call++;
+}
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+}  // namespace moelora
+
+using namespace moelora;
+
+extern "C" {
+
+int moe_lora_resolve_block_m(const moe_lora_shape* shape) {
+  int rc = check_shape(shape);
+  return rc ? rc : resolve_bm(shape);
+}
+
+size_t moe_lora_workspace_bytes(const moe_lora_shape* shape) {
+  Layout L;
+  if (make_layout(shape, &L)) return 0;
+  return L.total;
+}
+
+int moe_lora_workspace_view(const moe_lora_shape* shape, void* workspace, moe_lora_views* out) {
+  Layout L;
+  int rc = make_layout(shape, &L);
+  if (rc) return rc;
+  if (!workspace || !out) return MOE_LORA_EINVAL;
+  WsPtrs w = ws_ptrs(workspace, L);
+  out->sorted_ids = w.sorted;
+  out->expert_off = w.eoff;
+  out->seg_start = w.segstart;
+  out->seg_cnt = w.segcnt;
+  out->block_expert = w.bexp;
+  out->pos_of_pair = w.pos;
+  out->num_padded = w.hdr + HDR_NUM_PADDED;
+  out->err_count = w.hdr + HDR_ERR;
+  out->z_gu = w.zgu;
+  out->z_down = w.zd;
+  out->h = w.h;
+  out->d = w.d;
+  out->cap_rows = L.cap_rows;
+  out->cap_blocks = L.cap_blocks;
+  out->block_m = L.bm;
+  return MOE_LORA_OK;
+}
+
+int moe_lora_align(const moe_lora_shape* shape, const int32_t* topk_ids, const int32_t* lora_ids,
+                   void* workspace, size_t ws_bytes, void* stream) {
+  Layout L;
+  int rc = make_layout(shape, &L);
+  if (rc) return rc;
+  if (L.T == 0) return MOE_LORA_OK;
+  if (!topk_ids || !lora_ids) return MOE_LORA_EINVAL;
+  if (!workspace || ws_bytes < L.total) return MOE_LORA_EWORKSPACE;
+  if (!aligned16(workspace)) return MOE_LORA_EALIGN;
+  return launch_align(L, topk_ids, lora_ids, workspace, (hipStream_t)stream);
+}
+
+int moe_lora_forward(const moe_lora_shape* shape, const uint16_t* x, const int32_t* topk_ids,
+                     const float* topk_weights, const int32_t* lora_ids, const uint16_t* W_gu,
+                     const uint16_t* W_down, const uint16_t* A_gu, const uint16_t* B_gu,
+                     const uint16_t* A_down, const uint16_t* B_down, void* workspace,
+                     size_t ws_bytes, uint16_t* y, void* stream) {
+  Layout L;
+  int rc = make_layout(shape, &L);
+  if (rc) return rc;
+  if (L.T == 0) {
+    prof_call_done();
+    return MOE_LORA_OK;
+  }
+  const void* ptrs[] = {x, topk_ids, topk_weights, lora_ids, W_gu, W_down, A_gu, B_gu, A_down, B_down, y};
+  for (const void* p : ptrs)
+    if (!p) return MOE_LORA_EINVAL;
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return MOE_LORA_EALIGN;
+  if (!workspace || ws_bytes < L.total) return MOE_LORA_EWORKSPACE;
+  if (!aligned16(workspace)) return MOE_LORA_EALIGN;
+  hipStream_t st = (hipStream_t)stream;
+  WsPtrs w = ws_ptrs(workspace, L);
+
+  prof_stage_begin(ST_SHRINK_GU, st);
+  rc = launch_shrink(L, 0, x, A_gu, w.zgu, workspace, st);
+  prof_stage_end(ST_SHRINK_GU, st);
+  if (rc) return rc;
+  prof_stage_begin(ST_GEMM_GU, st);
+  rc = launch_gemm(L, 0, x, lora_ids, topk_weights, W_gu, B_gu, workspace, st);
+  prof_stage_end(ST_GEMM_GU, st);
+  if (rc) return rc;
+  prof_stage_begin(ST_SHRINK_DOWN, st);
+  rc = launch_shrink(L, 1, w.h, A_down, w.zd, workspace, st);
+  prof_stage_end(ST_SHRINK_DOWN, st);
+  if (rc) return rc;
+  prof_stage_begin(ST_GEMM_DOWN, st);
+  rc = launch_gemm(L, 1, nullptr, lora_ids, topk_weights, W_down, B_down, workspace, st);
+  prof_stage_end(ST_GEMM_DOWN, st);
+  if (rc) return rc;
+  prof_stage_begin(ST_COMBINE, st);
+  rc = launch_combine(L, workspace, y, st);
+  prof_stage_end(ST_COMBINE, st);
+  prof_call_done();
+  return rc;
+}
+
+int moe_lora_device_errors(const moe_lora_shape* shape, const void* workspace, int32_t* host_count,
+                           void* stream) {
+  Layout L;
+  int rc = make_layout(shape, &L);
+  if (rc) return rc;
+  if (!workspace || !host_count) return MOE_LORA_EINVAL;
+  if (L.T == 0) {
+    *host_count = 0;
+    return MOE_LORA_OK;
+  }
+  WsPtrs w = ws_ptrs(const_cast<void*>(workspace), L);
+  hipStream_t st = (hipStream_t)stream;
+  if (hipMemcpyAsync(host_count, w.hdr + HDR_ERR, sizeof(int32_t), hipMemcpyDeviceToHost, st) !=
+      hipSuccess)
+    return MOE_LORA_EHIP;
+  return hipStreamSynchronize(st) == hipSuccess ? MOE_LORA_OK : MOE_LORA_EHIP;
+}
+
+const char* moe_lora_status_str(int status) {
+  switch (status) {
+    case MOE_LORA_OK: return "ok";
+    case MOE_LORA_EINVAL: return "invalid argument";
+    case MOE_LORA_EALIGN: return "misaligned pointer or size";
+    case MOE_LORA_EWORKSPACE: return "workspace too small";
+    case MOE_LORA_EUNSUPPORTED: return "unsupported shape";
+    case MOE_LORA_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int moe_lora_stage_count(void) { return ST_COUNT; }
+
+const char* moe_lora_stage_name(int stage) {
+  static const char* names[ST_COUNT] = {"align_count", "align_place", "shrink_gate_up",
+                                        "gemm_gate_up", "shrink_down", "gemm_down", "combine"};
+  return (stage >= 0 && stage < ST_COUNT) ? names[stage] : "unknown";
+}
+
+int moe_lora_profile_begin(int max_calls) {
+  if (max_calls <= 0) return MOE_LORA_EINVAL;
+  prof_release();
+  g_prof.ev.resize((size_t)max_calls * ST_COUNT * 2);
+  for (auto& e : g_prof.ev)
+    if (hipEventCreate(&e) != hipSuccess) {
+      e = nullptr;
+      prof_release();
+      return MOE_LORA_EHIP;
+    }
+  g_prof.recorded.assign(max_calls, 0u);
+  g_prof.max_calls = max_calls;
+  g_prof.call = 0;
+  g_prof.on = true;
+  return MOE_LORA_OK;
+}
+
+int moe_lora_profile_end(float* stage_ms, int n, int* calls) {
+  if (!stage_ms || n < 0 || n > ST_COUNT) return MOE_LORA_EINVAL;
+  for (int s = 0; s < n; ++s) stage_ms[s] = 0.f;
+  int rc = MOE_LORA_OK;
+  const int ncalls = std::min(g_prof.call, g_prof.max_calls);
+  for (int c = 0; c < ncalls && rc == MOE_LORA_OK; ++c)
+    for (int s = 0; s < n; ++s) {
+      if (!(g_prof.recorded[c] & (1u << s))) continue;
+      hipEvent_t a = g_prof.ev[((size_t)c * ST_COUNT + s) * 2];
+      hipEvent_t b = g_prof.ev[((size_t)c * ST_COUNT + s) * 2 + 1];
+      float ms = 0.f;
+      if (hipEventSynchronize(b) != hipSuccess || hipEventElapsedTime(&ms, a, b) != hipSuccess) {
+        rc = MOE_LORA_EHIP;
+        break;
+      }
+      stage_ms[s] += ms;
+    }
+  if (calls) *calls = ncalls;
+  prof_release();
+  return rc;
+}
+
+}  // extern "C"

@@ -1,0 +1,233 @@
+// (expert, adapter) align: a stable counting sort of the (token, slot) pairs.
+//
+// The pages' kernel adds a grid dimension over the active adapters and shares
+// one BLOCK_SIZE_M across the four LoRA ops (vLLM blog "Multi-LoRA for MoE
+// models", sections "Implementing multi-LoRA inference for MoE models in vLLM"
+// and "Tuning kernel configurations ...").  Here that becomes one sort by key
+// (expert, slot), slot = adapter id or L for "no adapter": every expert's pairs
+// form one run padded to block_m rows, and inside it each adapter's pairs are
+// one contiguous segment, so the base GEMM tiles by expert and the LoRA ops
+// tile by (expert, adapter) segment over the same rows.
+//
+// Four short kernels, all deterministic (no atomic placement):
+//   1. count: per chunk of 512 pairs, an LDS histogram over the E*(L+1) keys
+//      and each pair's rank among earlier same-key pairs of its chunk;
+//   2. bucket scan: per key, exclusive prefix of the chunk counts (one
+//      wavefront per key) and the key total;
+//   3. offsets: one workgroup scans expert sizes (padded to block_m), writes
+//      segment starts, block -> expert map, pad sentinels and the list of
+//      shrink tiles (<= TS rows of one segment each);
+//   4. place: row of pair p = segment start + chunk prefix + rank.
+#include "device_util.h"
+#include "internal.h"
+
+namespace moelora {
+
+namespace {
+
+__device__ __forceinline__ int pair_key(const int32_t* __restrict__ topk_ids,
+                                        const int32_t* __restrict__ lora_ids, int p, int k, int E,
+                                        int L, int* lora_out, int* err) {
+  const int t = p / k;
+  int l = lora_ids[t];
+  if (!(l >= -1 && l < L)) {
+    l = -1;
+    if (err && p - t * k == 0) (*err)++;  // count a bad adapter id once per token
+  }
+  *lora_out = l;
+  const int e = topk_ids[p];
+  if (e < 0 || e >= E) {
+    if (err) (*err)++;
+    return -1;
+  }
+  return e * (L + 1) + (l >= 0 ? l : L);
+}
+
+__global__ __launch_bounds__(kAlignChunk) void align_count_kernel(
+    const int32_t* __restrict__ topk_ids, const int32_t* __restrict__ lora_ids, int P, int k, int E,
+    int L, int NB, int C, int32_t* __restrict__ chunk_cnt, int32_t* __restrict__ chunk_err,
+    int32_t* __restrict__ rank) {
+  extern __shared__ int lds[];
+  int* hist = lds;                 // [NB]
+  int* keys = lds + NB;            // [kAlignChunk]
+  int* errs = keys + kAlignChunk;  // [1]
+  const int tid = threadIdx.x, c = blockIdx.x;
+  for (int b = tid; b < NB; b += blockDim.x) hist[b] = 0;
+  if (tid == 0) errs[0] = 0;
+  const int p = c * kAlignChunk + tid;
+  int key = -1, err = 0, l;
+  if (p < P) key = pair_key(topk_ids, lora_ids, p, k, E, L, &l, &err);
+  keys[tid] = key;
+  __syncthreads();
+  if (key >= 0) atomicAdd(&hist[key], 1);  // counts are order-independent
+  if (err) atomicAdd(&errs[0], err);
+  // rank among earlier pairs of this chunk with the same key (stable order)
+  int rnk = 0;
+  const int wend = ((tid >> 6) + 1) << 6;  // uniform per wavefront
+  for (int j = 0; j < wend; ++j) rnk += (j < tid) & (keys[j] == key);
+  __syncthreads();
+  for (int b = tid; b < NB; b += blockDim.x) chunk_cnt[(size_t)b * C + c] = hist[b];
+  if (p < P) rank[p] = rnk;
+  if (tid == 0) chunk_err[c] = errs[0];
+}
+
+// One wavefront per key: chunk counts -> exclusive prefixes (in place), total.
+__global__ __launch_bounds__(256) void align_bucket_scan_kernel(int NB, int C,
+                                                                int32_t* __restrict__ chunk_cnt,
+                                                                int32_t* __restrict__ segcnt) {
+  const int lane = threadIdx.x & 63;
+  const int b = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (b >= NB) return;
+  int32_t* row = chunk_cnt + (size_t)b * C;
+  int carry = 0;
+  for (int c0 = 0; c0 < C; c0 += 64) {
+    const int c = c0 + lane;
+    const int v = c < C ? row[c] : 0;
+    int x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      int y = __shfl_up(x, o, 64);
+      if (lane >= o) x += y;
+    }
+    if (c < C) row[c] = carry + x - v;
+    carry += __shfl(x, 63, 64);
+  }
+  if (lane == 0) segcnt[b] = carry;
+}
+
+__global__ __launch_bounds__(1024) void align_offsets_kernel(
+    int P, int E, int L, int C, int bm, int64_t cap_rows, int64_t cap_blocks, int TS,
+    const int32_t* __restrict__ chunk_err, const int32_t* __restrict__ segcnt,
+    int32_t* __restrict__ hdr, int32_t* __restrict__ sorted, int32_t* __restrict__ eoff,
+    int32_t* __restrict__ segstart, int32_t* __restrict__ bexp, LoraTile* __restrict__ tiles) {
+  extern __shared__ int lds[];
+  int* scan = lds;          // [16]
+  int* s_eoff = lds + 16;   // [E+1]
+  const int tid = threadIdx.x, nt = blockDim.x, S = L + 1;
+
+  // padded expert sizes, scanned over experts (each thread owns a range)
+  const int per = (E + nt - 1) / nt;
+  const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
+  int local = 0;
+  for (int e = e0; e < e1; ++e) {
+    int n = 0;
+    for (int s = 0; s < S; ++s) n += segcnt[e * S + s];
+    local += (n + bm - 1) / bm * bm;
+  }
+  int total;
+  int at = block_exclusive_scan(local, scan, &total);
+  for (int e = e0; e < e1; ++e) {
+    s_eoff[e] = at;
+    eoff[e] = at;
+    int n = 0;
+    for (int s = 0; s < S; ++s) {
+      segstart[e * S + s] = at + n;
+      n += segcnt[e * S + s];
+    }
+    for (int row = at + n; row < at + (n + bm - 1) / bm * bm; ++row) sorted[row] = P;  // pads
+    at += (n + bm - 1) / bm * bm;
+  }
+  if (tid == 0) {
+    s_eoff[E] = total;
+    eoff[E] = total;
+  }
+  __syncthreads();
+  const int num_padded = total;
+  for (int64_t row = num_padded + tid; row < cap_rows; row += nt) sorted[row] = P;
+  for (int64_t b = tid; b < cap_blocks; b += nt) {
+    const int64_t row = b * bm;
+    int e = -1;
+    if (row < num_padded) {  // the last expert whose run starts at or before row
+      int lo = 0, hi = E - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_eoff[mid] <= row) lo = mid; else hi = mid - 1;
+      }
+      e = lo;
+    }
+    bexp[b] = e;
+  }
+
+  // shrink tiles: segments (e, l < L) cut into pieces of <= TS rows
+  const int NS = E * L;
+  const int perS = (NS + nt - 1) / nt;
+  const int s0 = min(NS, tid * perS), s1 = min(NS, s0 + perS);
+  int lt = 0;
+  for (int i = s0; i < s1; ++i) lt += (segcnt[(i / L) * S + i % L] + TS - 1) / TS;
+  int ntiles;
+  int tb = block_exclusive_scan(lt, scan, &ntiles);
+  __syncthreads();  // segstart written above by other threads
+  for (int i = s0; i < s1; ++i) {
+    const int e = i / L, l = i % L;
+    const int cnt = segcnt[e * S + l], st = segstart[e * S + l];
+    for (int o = 0; o < cnt; o += TS) {
+      LoraTile tl;
+      tl.e = e;
+      tl.l = l;
+      tl.row0 = st + o;
+      tl.n = min(TS, cnt - o);
+      tiles[tb++] = tl;
+    }
+  }
+  if (tid == 0) {
+    int errs = 0;
+    for (int c = 0; c < C; ++c) errs += chunk_err[c];
+    hdr[HDR_NUM_PADDED] = num_padded;
+    hdr[HDR_ERR] = errs;
+    hdr[HDR_NTILES] = ntiles;
+  }
+}
+
+__global__ __launch_bounds__(256) void align_place_kernel(
+    const int32_t* __restrict__ topk_ids, const int32_t* __restrict__ lora_ids, int P, int k, int E,
+    int L, int C, int r, int zero_gu, int zero_d, const int32_t* __restrict__ chunk_cnt,
+    const int32_t* __restrict__ rank, const int32_t* __restrict__ segstart,
+    int32_t* __restrict__ sorted, int32_t* __restrict__ pos, float* __restrict__ zgu,
+    float* __restrict__ zd) {
+  const int p = blockIdx.x * blockDim.x + threadIdx.x;
+  if (p >= P) return;
+  int l;
+  const int key = pair_key(topk_ids, lora_ids, p, k, E, L, &l, nullptr);
+  if (key < 0) {
+    pos[p] = -1;
+    return;
+  }
+  const int c = p / kAlignChunk;
+  const int row = segstart[key] + chunk_cnt[(size_t)key * C + c] + rank[p];
+  sorted[row] = p;
+  pos[p] = row;
+  if (l >= 0) {  // clear the split-K accumulators of adapter rows
+    for (int q = 0; q < r; q += 4) {
+      const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (zero_gu) *reinterpret_cast<float4*>(zgu + (size_t)row * r + q) = z;
+      if (zero_d) *reinterpret_cast<float4*>(zd + (size_t)row * r + q) = z;
+    }
+  }
+}
+
+}  // namespace
+
+int launch_align(const Layout& L, const int32_t* topk_ids, const int32_t* lora_ids, void* ws,
+                 hipStream_t st) {
+  WsPtrs w = ws_ptrs(ws, L);
+  const int P = (int)L.P, NB = (int)L.NB, C = (int)L.C;
+  if (P <= 0) return MOE_LORA_OK;  // no pairs: nothing to sort
+  prof_stage_begin(ST_ALIGN_COUNT, st);
+  align_count_kernel<<<C, kAlignChunk, (NB + kAlignChunk + 1) * sizeof(int), st>>>(
+      topk_ids, lora_ids, P, L.k, L.E, L.L, NB, C, w.chunk, w.chunkerr, w.rank);
+  align_bucket_scan_kernel<<<(NB + 3) / 4, 256, 0, st>>>(NB, C, w.chunk, w.segcnt);
+  prof_stage_end(ST_ALIGN_COUNT, st);
+  prof_stage_begin(ST_ALIGN_PLACE, st);
+  align_offsets_kernel<<<1, 1024, (16 + L.E + 1) * sizeof(int), st>>>(
+      P, L.E, L.L, C, L.bm, L.cap_rows, L.cap_blocks, (int)L.TS, w.chunkerr, w.segcnt, w.hdr,
+      w.sorted, w.eoff, w.segstart, w.bexp, w.tiles);
+  const int zero_gu = plan_shrink(L, L.H).splits > 1;
+  const int zero_d = plan_shrink(L, L.I).splits > 1;
+  align_place_kernel<<<(P + 255) / 256, 256, 0, st>>>(topk_ids, lora_ids, P, L.k, L.E, L.L, C, L.r,
+                                                      zero_gu, zero_d, w.chunk, w.rank, w.segstart,
+                                                      w.sorted, w.pos, w.zgu, w.zd);
+  prof_stage_end(ST_ALIGN_PLACE, st);
+  return hipGetLastError() == hipSuccess ? MOE_LORA_OK : MOE_LORA_EHIP;
+}
+
+}  // namespace moelora

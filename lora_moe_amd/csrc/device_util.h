@@ -1,0 +1,74 @@
+// Device helpers for gfx950 (CDNA4): bf16 conversions, the bf16 MFMA used by
+// every contraction, and workgroup scans.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moelora {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t u) { return __uint_as_float((uint32_t)u << 16); }
+
+// fp32 -> bf16 bits, round to nearest even; NaN stays NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u) return (uint16_t)((u >> 16) | ((u & 0xffffu) ? 0x40u : 0u));
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// D(16x16, fp32) += A(16x32, bf16) * B(32x16, bf16) on one wavefront.
+// Lane l supplies A[m = l%16][k = 8*(l/16) .. +8] and B[k = 8*(l/16) .. +8][n = l%16];
+// it receives D[m = 4*(l/16) + i][n = l%16], i = 0..3.  Only the pairing of
+// A and B k-slots matters for the sum, so callers may permute K freely as
+// long as both operands use the same permutation.
+__device__ __forceinline__ f32x4_t mfma_16x16x32(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ u32x4_t ld16(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }
+
+__device__ __forceinline__ u32x4_t zero4() {
+  u32x4_t z = {0u, 0u, 0u, 0u};
+  return z;
+}
+
+__device__ __forceinline__ float silu_f32(float v) { return v / (1.0f + __expf(-v)); }
+
+// Exclusive scan of one int per thread across a workgroup of `nthreads`
+// (multiple of 64, <= 1024).  `lds` needs 16 ints.  Returns the exclusive
+// prefix; *total receives the workgroup sum.  All threads must call it.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* lds, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) lds[wave] = x;
+  __syncthreads();
+  if (wave == 0) {
+    int w = lane < nw ? lds[lane] : 0;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+      int y = __shfl_up(w, o, 64);
+      if (lane >= o) w += y;
+    }
+    if (lane < nw) lds[lane] = w;  // inclusive wave sums
+  }
+  __syncthreads();
+  int before = wave ? lds[wave - 1] : 0;
+  *total = lds[nw - 1];
+  __syncthreads();
+  return before + x - v;
+}
+
+}  // namespace moelora

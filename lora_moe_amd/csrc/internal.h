@@ -1,0 +1,122 @@
+// Internal declarations shared by the HIP sources of the MoE-LoRA library.
+// Not part of the public ABI (see include/moe_lora.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+#include <algorithm>
+#include <stdint.h>
+
+#include "moe_lora.h"
+
+namespace moelora {
+
+// ------------------------------------------------------------------ sizes
+
+constexpr int kAlignChunk = 512;       // pairs per workgroup in the align count pass
+constexpr int kAlignMaxBuckets = 14336;  // E*(L+1) limit: one int per bucket in LDS
+constexpr int kHdrInts = 64;
+
+// header slots (int32) at the start of the workspace
+enum { HDR_NUM_PADDED = 0, HDR_ERR = 1, HDR_NTILES = 2 };
+
+// Workspace layout for one shape.  Every region starts on a 256-byte boundary.
+struct Layout {
+  int T, H, I, E, k, L, r, bm;
+  float s;
+  int64_t P, cap_rows, cap_blocks, NB, C, TS, max_tiles;
+  size_t off_hdr, off_sorted, off_eoff, off_segstart, off_segcnt, off_bexp, off_pos;
+  size_t off_chunk, off_chunkerr, off_rank, off_tiles, off_zgu, off_zd, off_h, off_d, total;
+};
+
+// Fills `L` from the shape; returns MOE_LORA_OK or an error code.
+int make_layout(const moe_lora_shape* s, Layout* L);
+
+// Shrink tile record: rows [row0, row0 + n) of the sorted order, all in the
+// segment of (expert e, adapter l).
+struct LoraTile {
+  int e, l, row0, n;
+};
+
+// Device pointers derived from a workspace base and a layout.
+struct WsPtrs {
+  int32_t* hdr;
+  int32_t* sorted;
+  int32_t* eoff;
+  int32_t* segstart;
+  int32_t* segcnt;
+  int32_t* bexp;
+  int32_t* pos;
+  int32_t* chunk;
+  int32_t* chunkerr;
+  int32_t* rank;
+  LoraTile* tiles;
+  float* zgu;
+  float* zd;
+  uint16_t* h;
+  float* d;
+};
+
+inline WsPtrs ws_ptrs(void* base, const Layout& L) {
+  char* b = static_cast<char*>(base);
+  WsPtrs w;
+  w.hdr = reinterpret_cast<int32_t*>(b + L.off_hdr);
+  w.sorted = reinterpret_cast<int32_t*>(b + L.off_sorted);
+  w.eoff = reinterpret_cast<int32_t*>(b + L.off_eoff);
+  w.segstart = reinterpret_cast<int32_t*>(b + L.off_segstart);
+  w.segcnt = reinterpret_cast<int32_t*>(b + L.off_segcnt);
+  w.bexp = reinterpret_cast<int32_t*>(b + L.off_bexp);
+  w.pos = reinterpret_cast<int32_t*>(b + L.off_pos);
+  w.chunk = reinterpret_cast<int32_t*>(b + L.off_chunk);
+  w.chunkerr = reinterpret_cast<int32_t*>(b + L.off_chunkerr);
+  w.rank = reinterpret_cast<int32_t*>(b + L.off_rank);
+  w.tiles = reinterpret_cast<LoraTile*>(b + L.off_tiles);
+  w.zgu = reinterpret_cast<float*>(b + L.off_zgu);
+  w.zd = reinterpret_cast<float*>(b + L.off_zd);
+  w.h = reinterpret_cast<uint16_t*>(b + L.off_h);
+  w.d = reinterpret_cast<float*>(b + L.off_d);
+  return w;
+}
+
+// ------------------------------------------------------------------ stage timing
+
+enum Stage {
+  ST_ALIGN_COUNT = 0,
+  ST_ALIGN_PLACE,
+  ST_SHRINK_GU,
+  ST_GEMM_GU,
+  ST_SHRINK_DOWN,
+  ST_GEMM_DOWN,
+  ST_COMBINE,
+  ST_COUNT
+};
+
+// Records stage start/stop events around a launch when profiling is on.
+void prof_stage_begin(int stage, hipStream_t st);
+void prof_stage_end(int stage, hipStream_t st);
+void prof_call_done();
+
+// ------------------------------------------------------------------ launchers
+
+int launch_align(const Layout& L, const int32_t* topk_ids, const int32_t* lora_ids, void* ws,
+                 hipStream_t st);
+
+struct ShrinkPlan {
+  int splits;       // K split count (1 = plain stores)
+  int grid;         // workgroups (grid-stride over tiles x splits)
+};
+ShrinkPlan plan_shrink(const Layout& L, int K);
+
+// mode 0: gate_up shrink from x rows gathered by token; mode 1: down shrink from h rows
+int launch_shrink(const Layout& L, int mode, const uint16_t* in, const uint16_t* A, float* z, void* ws,
+                  hipStream_t st);
+
+// mode 0: gate_up GEMM + expand + SiLU gate -> h; mode 1: down GEMM + expand + weight -> d
+int launch_gemm(const Layout& L, int mode, const uint16_t* x, const int32_t* lora_ids,
+                const float* topk_weights, const uint16_t* W, const uint16_t* B, void* ws,
+                hipStream_t st);
+
+int launch_combine(const Layout& L, void* ws, uint16_t* y, hipStream_t st);
+
+}  // namespace moelora

@@ -1,0 +1,225 @@
+// LoRA shrink: z[row][q] = sum_i in[row][i] * A[l][e][q][i]  (h_in -> r).
+//
+// The pages' shrink computes z = xA with A of shape h_in x r (vLLM blog
+// "Multi-LoRA for MoE models", section "Implementing multi-LoRA inference for
+// MoE models in vLLM").  Each of the r outputs is a long sum over h_in while
+// there are only a few dozen outputs, so the sum is split over K across
+// workgroups and the partial sums are combined with relaxed atomic adds
+// (section "Kernel optimizations", split-K).  Reading A so that neighbouring
+// output columns share cache lines is the pages' CTA-swizzle concern; here A
+// is stored [r][h_in] and one workgroup reads whole [r x K-slice] slabs of it,
+// every row as contiguous 32-byte pieces per lane.
+//
+// One work item = (tile of <= 16*RFS rows of one (expert, adapter) segment,
+// K split).  A workgroup of 4 wavefronts walks the split's 64-wide K steps
+// interleaved by wavefront; each wavefront accumulates the whole tile
+// [16*RFS x 16*NFR] with bf16 MFMA 16x16x32.  The four partial tiles are added
+// through LDS, then one wavefront stores (single split) or atomically adds
+// (several splits) into z.  mode 0 gathers the input rows of x by token
+// (gate_up shrink); mode 1 reads the SiLU-gate output h by row (down shrink).
+#include "device_util.h"
+#include "internal.h"
+
+namespace moelora {
+
+namespace {
+
+struct ShrinkParams {
+  const uint16_t* in;  // mode 0: x [T][K]; mode 1: h [cap_rows][K]
+  const uint16_t* A;   // [L][E][r][K]
+  const int32_t* sorted;
+  const LoraTile* tiles;
+  const int32_t* hdr;
+  float* z;            // [cap_rows][r]
+  int K, E, r, topk, splits, steps_per_split, nsteps, use_atomic;
+};
+
+template <int MODE, int RFS, int NFR, bool EVEN>
+__global__ __launch_bounds__(256) void lora_shrink_kernel(ShrinkParams p) {
+  __shared__ float red[2][RFS * 16][NFR * 16 + 1];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int m = lane & 15, kq = lane >> 4;
+  const int nitems = p.hdr[HDR_NTILES] * p.splits;
+
+  for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
+    const int ti = item / p.splits, sp = item - ti * p.splits;
+    const LoraTile tl = p.tiles[ti];
+
+    const uint16_t* arow[RFS];
+#pragma unroll
+    for (int rf = 0; rf < RFS; ++rf) {
+      const int row = tl.row0 + min(rf * 16 + m, tl.n - 1);  // rows past the tile repeat a valid one
+      if (MODE == 0) {
+        const int t = p.sorted[row] / p.topk;
+        arow[rf] = p.in + (size_t)t * p.K;
+      } else {
+        arow[rf] = p.in + (size_t)row * p.K;
+      }
+    }
+    const uint16_t* brow[NFR];
+#pragma unroll
+    for (int nf = 0; nf < NFR; ++nf) {
+      const int q = min(nf * 16 + m, p.r - 1);  // columns past r repeat a valid one
+      brow[nf] = p.A + (((size_t)tl.l * p.E + tl.e) * p.r + q) * p.K;
+    }
+
+    f32x4_t acc[RFS][NFR];
+#pragma unroll
+    for (int rf = 0; rf < RFS; ++rf)
+#pragma unroll
+      for (int nf = 0; nf < NFR; ++nf) acc[rf][nf] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    const int ks0 = sp * p.steps_per_split;
+    const int ks1 = min(p.nsteps, ks0 + p.steps_per_split);
+    for (int ks = ks0 + wave; ks < ks1; ks += 4) {
+      const int kb = ks * 64 + kq * 16;
+      const bool v0 = EVEN || kb < p.K, v1 = EVEN || kb + 8 < p.K;
+      u32x4_t a0[RFS], a1[RFS], b0[NFR], b1[NFR];
+#pragma unroll
+      for (int rf = 0; rf < RFS; ++rf) {
+        a0[rf] = v0 ? ld16(arow[rf] + kb) : zero4();
+        a1[rf] = v1 ? ld16(arow[rf] + kb + 8) : zero4();
+      }
+#pragma unroll
+      for (int nf = 0; nf < NFR; ++nf) {
+        b0[nf] = v0 ? ld16(brow[nf] + kb) : zero4();
+        b1[nf] = v1 ? ld16(brow[nf] + kb + 8) : zero4();
+      }
+#pragma unroll
+      for (int rf = 0; rf < RFS; ++rf)
+#pragma unroll
+        for (int nf = 0; nf < NFR; ++nf) {
+          acc[rf][nf] = mfma_16x16x32(a0[rf], b0[nf], acc[rf][nf]);
+          acc[rf][nf] = mfma_16x16x32(a1[rf], b1[nf], acc[rf][nf]);
+        }
+    }
+
+    // add the four wavefronts' partial tiles: (2,3) -> (0,1) -> 0
+    if (wave >= 2) {
+#pragma unroll
+      for (int rf = 0; rf < RFS; ++rf)
+#pragma unroll
+        for (int nf = 0; nf < NFR; ++nf)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) red[wave - 2][rf * 16 + 4 * kq + i][nf * 16 + m] = acc[rf][nf][i];
+    }
+    __syncthreads();
+    if (wave < 2) {
+#pragma unroll
+      for (int rf = 0; rf < RFS; ++rf)
+#pragma unroll
+        for (int nf = 0; nf < NFR; ++nf)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[rf][nf][i] += red[wave][rf * 16 + 4 * kq + i][nf * 16 + m];
+    }
+    __syncthreads();
+    if (wave == 1) {
+#pragma unroll
+      for (int rf = 0; rf < RFS; ++rf)
+#pragma unroll
+        for (int nf = 0; nf < NFR; ++nf)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) red[0][rf * 16 + 4 * kq + i][nf * 16 + m] = acc[rf][nf][i];
+    }
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+      for (int rf = 0; rf < RFS; ++rf)
+#pragma unroll
+        for (int nf = 0; nf < NFR; ++nf)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int row = rf * 16 + 4 * kq + i, q = nf * 16 + m;
+            if (row < tl.n && q < p.r) {
+              const float v = acc[rf][nf][i] + red[0][row][q];
+              float* dst = p.z + (size_t)(tl.row0 + row) * p.r + q;
+              if (p.use_atomic)
+                __hip_atomic_fetch_add(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              else
+                *dst = v;
+            }
+          }
+    }
+    __syncthreads();  // red is reused by the next item
+  }
+}
+
+template <int MODE, int RFS, int NFR>
+void launch_t(const ShrinkParams& sp, bool even, int grid, hipStream_t st) {
+  if (even)
+    lora_shrink_kernel<MODE, RFS, NFR, true><<<grid, 256, 0, st>>>(sp);
+  else
+    lora_shrink_kernel<MODE, RFS, NFR, false><<<grid, 256, 0, st>>>(sp);
+}
+
+template <int MODE, int RFS>
+void launch_nfr(const ShrinkParams& sp, bool even, int grid, hipStream_t st) {
+  switch ((sp.r + 15) / 16) {
+    case 1: launch_t<MODE, RFS, 1>(sp, even, grid, st); break;
+    case 2: launch_t<MODE, RFS, 2>(sp, even, grid, st); break;
+    case 3: launch_t<MODE, RFS, 3>(sp, even, grid, st); break;
+    case 4: launch_t<MODE, RFS, 4>(sp, even, grid, st); break;
+    case 5: launch_t<MODE, 1, 5>(sp, even, grid, st); break;
+    case 6: launch_t<MODE, 1, 6>(sp, even, grid, st); break;
+    case 7: launch_t<MODE, 1, 7>(sp, even, grid, st); break;
+    default: launch_t<MODE, 1, 8>(sp, even, grid, st); break;
+  }
+}
+
+}  // namespace
+
+// Tiles are at most TS rows; ranks above 64 use 16-row tiles (LDS budget).
+static int shrink_row_frags(const Layout& L) {
+  if (L.r > 64) return 1;
+  return (int)(L.TS / 16);
+}
+
+ShrinkPlan plan_shrink(const Layout& L, int K) {
+  ShrinkPlan sp;
+  const int nsteps = (K + 63) / 64;
+  // expected number of shrink tiles: at most one per touched (expert, adapter)
+  // segment plus one per TS adapter rows
+  const int64_t est = std::max<int64_t>(1, std::min<int64_t>(L.max_tiles, std::min<int64_t>(L.P, (int64_t)L.E * L.L)));
+  int splits = (int)std::max<int64_t>(1, 2048 / est);
+  splits = std::min(splits, std::max(1, nsteps / 4));  // >= 4 steps: one per wavefront
+  sp.splits = splits;
+  const int64_t items = L.max_tiles * splits;
+  sp.grid = (int)std::max<int64_t>(1, std::min<int64_t>(items, 4096));
+  return sp;
+}
+
+int launch_shrink(const Layout& L, int mode, const uint16_t* in, const uint16_t* A, float* z, void* ws,
+                  hipStream_t st) {
+  WsPtrs w = ws_ptrs(ws, L);
+  const int K = mode == 0 ? L.H : L.I;
+  ShrinkPlan pl = plan_shrink(L, K);
+  ShrinkParams sp;
+  sp.in = in;
+  sp.A = A;
+  sp.sorted = w.sorted;
+  sp.tiles = w.tiles;
+  sp.hdr = w.hdr;
+  sp.z = z;
+  sp.K = K;
+  sp.E = L.E;
+  sp.r = L.r;
+  sp.topk = L.k;
+  sp.splits = pl.splits;
+  sp.nsteps = (K + 63) / 64;
+  sp.steps_per_split = (sp.nsteps + pl.splits - 1) / pl.splits;
+  sp.use_atomic = pl.splits > 1;
+  const bool even = (K % 64) == 0;
+  const int rfs = shrink_row_frags(L);
+  if (mode == 0) {
+    if (rfs == 4) launch_nfr<0, 4>(sp, even, pl.grid, st);
+    else if (rfs == 2) launch_nfr<0, 2>(sp, even, pl.grid, st);
+    else launch_nfr<0, 1>(sp, even, pl.grid, st);
+  } else {
+    if (rfs == 4) launch_nfr<1, 4>(sp, even, pl.grid, st);
+    else if (rfs == 2) launch_nfr<1, 2>(sp, even, pl.grid, st);
+    else launch_nfr<1, 1>(sp, even, pl.grid, st);
+  }
+  return hipGetLastError() == hipSuccess ? MOE_LORA_OK : MOE_LORA_EHIP;
+}
+
+}  // namespace moelora

@@ -208,35 +208,125 @@ def make_inputs(wl, seed: int | None = None, T: int | None = None, touched_only:
     x = np.empty((T, H), dtype=np.uint16)
     normal_bf16_into(stream_key(wl.seed, 3, 0, 0), x.reshape(-1), wl.x_std)
 
-    used_e = np.zeros(E, dtype=bool)
-    used_le = np.zeros((L, E), dtype=bool)
-    if T > 0:
-        used_e[np.unique(topk_ids)] = True
-        for l in range(L):
-            sel = topk_ids[lora_ids == l]
-            if sel.size:
-                used_le[l, np.unique(sel)] = True
+    arrays = {}
+    for name, shp in weight_shapes(wl).items():
+        arrays[name] = np.zeros(shp, dtype=np.uint16)
+    for spec in slab_specs(wl, topk_ids, lora_ids, touched_only):
+        fill_slab(spec, arrays[spec.name][spec.index].reshape(-1))
+    W_gu, W_down = arrays["W_gu"], arrays["W_down"]
+    A_gu, B_gu, A_down, B_down = arrays["A_gu"], arrays["B_gu"], arrays["A_down"], arrays["B_down"]
+    return Inputs(wl, x, topk_ids, topk_weights, lora_ids, W_gu, W_down, A_gu, B_gu, A_down, B_down)
 
-    def slab_stack(tag, shape_per, outer):
-        arr = np.zeros(outer + shape_per, dtype=np.uint16)
+
+# weight stacks: (stream tag, per-slab shape, outer (slab) dims)
+def weight_layout(wl: Workload) -> dict:
+    T, H, I, E, L, r = wl.T, wl.H, wl.I, wl.E, wl.L, wl.r
+    return {"W_gu": (4, (2 * I, H), (E,)), "W_down": (5, (H, I), (E,)),
+            "A_gu": (6, (r, H), (L, E)), "B_gu": (7, (2 * I, r), (L, E)),
+            "A_down": (8, (r, I), (L, E)), "B_down": (9, (H, r), (L, E))}
+
+
+def weight_shapes(wl: Workload) -> dict:
+    return {n: outer + per for n, (tag, per, outer) in weight_layout(wl).items()}
+
+
+@dataclass(frozen=True)
+class SlabSpec:
+    name: str
+    index: tuple
+    size: int
+    key: int
+    std: float
+
+
+def touched(wl: Workload, topk_ids: np.ndarray, lora_ids: np.ndarray):
+    """Experts and (adapter, expert) pairs that some (token, slot) pair reads."""
+    used_e = np.zeros(wl.E, dtype=bool)
+    used_le = np.zeros((wl.L, wl.E), dtype=bool)
+    ok = (topk_ids >= 0) & (topk_ids < wl.E)
+    used_e[np.unique(topk_ids[ok])] = True
+    for l in range(wl.L):
+        sel = topk_ids[(lora_ids == l)[:, None] & ok]
+        if sel.size:
+            used_le[l, np.unique(sel)] = True
+    return used_e, used_le
+
+
+def slab_specs(wl: Workload, topk_ids, lora_ids, touched_only: bool = False, only=None):
+    """Every weight slab to draw: (stack name, slab index, element count, stream key).
+    ``only`` optionally restricts to a set of expert ids."""
+    used_e, used_le = touched(wl, topk_ids, lora_ids)
+    out = []
+    for name, (tag, per, outer) in weight_layout(wl).items():
+        size = int(np.prod(per))
         for idx in np.ndindex(*outer):
-            if touched_only:
-                if len(idx) == 1 and not used_e[idx[0]]:
-                    continue
-                if len(idx) == 2 and not used_le[idx[0], idx[1]]:
-                    continue
+            e = idx[-1]
+            if only is not None and e not in only:
+                continue
+            if touched_only and (not used_e[e] if len(idx) == 1 else not used_le[idx[0], e]):
+                continue
             a = idx[0]
             b = idx[1] if len(idx) > 1 else 0
-            normal_bf16_into(stream_key(wl.seed, tag, a, b), arr[idx].reshape(-1), wl.w_std)
-        return arr
+            out.append(SlabSpec(name, idx, size, stream_key(wl.seed, tag, a, b), wl.w_std))
+    return out
 
-    W_gu = slab_stack(4, (2 * I, H), (E,))
-    W_down = slab_stack(5, (H, I), (E,))
-    A_gu = slab_stack(6, (r, H), (L, E))
-    B_gu = slab_stack(7, (2 * I, r), (L, E))
-    A_down = slab_stack(8, (r, I), (L, E))
-    B_down = slab_stack(9, (H, r), (L, E))
-    return Inputs(wl, x, topk_ids, topk_weights, lora_ids, W_gu, W_down, A_gu, B_gu, A_down, B_down)
+
+def fill_slab(spec: SlabSpec, out: np.ndarray) -> None:
+    normal_bf16_into(spec.key, out, spec.std)
+
+
+def device_inputs(wl, seed=None, touched_only=True, device="cuda", keep_host=False, **overrides):
+    """Generate a workload straight into device tensors, slab by slab through a
+    pinned staging buffer (the largest shape has ~28 GB of weights).  Returns
+    (dict of device tensors, host Inputs).  The host Inputs hold the ids, x
+    and router outputs; its weight stacks are zero-filled placeholders unless
+    ``keep_host`` is set (lazily allocated, so untouched pages cost nothing)."""
+    import torch
+    if isinstance(wl, int):
+        wl = WORKLOADS[wl]
+    if seed is not None:
+        overrides["seed"] = seed
+    if overrides:
+        wl = replace(wl, **overrides)
+    topk_ids, topk_weights = make_routing(wl)
+    lora_ids = adapter_ids(wl)
+    x = np.empty((wl.T, wl.H), dtype=np.uint16)
+    normal_bf16_into(stream_key(wl.seed, 3, 0, 0), x.reshape(-1), wl.x_std)
+    dev = dict(
+        x=torch.from_numpy(x.view(np.int16)).to(device).view(torch.bfloat16),
+        topk_ids=torch.from_numpy(topk_ids).to(device),
+        topk_weights=torch.from_numpy(topk_weights).to(device),
+        lora_ids=torch.from_numpy(lora_ids).to(device))
+    host_w = {}
+    for name, shp in weight_shapes(wl).items():
+        dev[name] = torch.zeros(shp, dtype=torch.bfloat16, device=device)
+        host_w[name] = np.zeros(shp, dtype=np.uint16)
+    specs = slab_specs(wl, topk_ids, lora_ids, touched_only)
+    biggest = max((s.size for s in specs), default=1)
+    stage = torch.empty(biggest, dtype=torch.int16, pin_memory=True)
+    stage_np = stage.numpy().view(np.uint16)
+    for spec in specs:
+        buf = stage_np[:spec.size]
+        fill_slab(spec, buf)
+        dst = dev[spec.name][spec.index].view(-1).view(torch.int16)
+        dst.copy_(stage[:spec.size], non_blocking=True)
+        torch.cuda.current_stream().synchronize()  # the staging buffer is reused
+        if keep_host:
+            host_w[spec.name][spec.index].reshape(-1)[:] = buf
+    inp = Inputs(wl, x, topk_ids, topk_weights, lora_ids, **host_w)
+    return dev, inp
+
+
+def host_slabs_for_tokens(inp: Inputs, tokens) -> None:
+    """Fill the host weight stacks of ``inp`` with the slabs that the given
+    tokens read (for a CPU reference on a sample of tokens)."""
+    wl = inp.wl
+    ids = inp.topk_ids[tokens]
+    lids = inp.lora_ids[tokens]
+    arrays = dict(W_gu=inp.W_gu, W_down=inp.W_down, A_gu=inp.A_gu, B_gu=inp.B_gu,
+                  A_down=inp.A_down, B_down=inp.B_down)
+    for spec in slab_specs(wl, ids, lids, touched_only=True):
+        fill_slab(spec, arrays[spec.name][spec.index].reshape(-1))
 
 
 def algorithmic_work(wl: Workload, topk_ids: np.ndarray, lora_ids: np.ndarray) -> dict:

@@ -1,0 +1,114 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol, and
+its host-side checks return the documented codes without touching a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import lora_moe_amd as lm
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = set()
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", fn)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names |= set(re.findall(r"\b(moe_lora_\w+)\s*\(", src))
+    return sorted(names)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return lm.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) >= 10
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_status_strings(lib):
+    assert lm.moe_lora_status_str(0) == "ok"
+    assert "workspace" in lm.moe_lora_status_str(lm.MOE_LORA_EWORKSPACE)
+    assert lm.moe_lora_status_str(-99) == "unknown status"
+
+
+def shape_of(wl, bm=0):
+    return lm.make_shape(wl.T, wl.H, wl.I, wl.E, wl.topk, wl.L, wl.r, bm, wl.scale)
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5])
+def test_workspace_and_block_m(lib, n):
+    wl = synth.WORKLOADS[n]
+    s = shape_of(wl)
+    bm = lm.moe_lora_resolve_block_m(s)
+    assert bm in (16, 32, 64, 128, 256)
+    ws = lm.moe_lora_workspace_bytes(s)
+    P = wl.T * wl.topk
+    cap = P + wl.E * (bm - 1)
+    # at least the intermediates h (bf16) and d (fp32) for every row
+    assert ws >= cap * (2 * wl.I + 4 * wl.H)
+    s2 = shape_of(wl, 64)
+    assert lm.moe_lora_resolve_block_m(s2) == 64
+
+
+def test_bad_shapes(lib):
+    good = dict(T=4, H=64, I=32, E=4, topk=2, L=2, r=8)
+    cases = [
+        (dict(T=-1), lm.MOE_LORA_EINVAL), (dict(H=0), lm.MOE_LORA_EINVAL),
+        (dict(topk=5), lm.MOE_LORA_EINVAL), (dict(L=0), lm.MOE_LORA_EINVAL),
+        (dict(block_m=48), lm.MOE_LORA_EINVAL), (dict(H=60), lm.MOE_LORA_EALIGN),
+        (dict(I=36), lm.MOE_LORA_EALIGN), (dict(r=12), lm.MOE_LORA_EUNSUPPORTED),
+        (dict(r=136), lm.MOE_LORA_EUNSUPPORTED), (dict(E=8000, L=2), lm.MOE_LORA_EUNSUPPORTED),
+    ]
+    for over, code in cases:
+        args = dict(good, **over)
+        s = lm.make_shape(**args)
+        assert lm.moe_lora_resolve_block_m(s) == code, over
+        assert lm.moe_lora_workspace_bytes(s) == 0, over
+        rc = lib.moe_lora_align(ctypes.byref(s), None, None, None, 0, None)
+        assert rc == code, over
+
+
+def test_null_and_workspace_checks_do_not_launch(lib):
+    s = lm.make_shape(4, 64, 32, 4, 2, 2, 8)
+    need = lm.moe_lora_workspace_bytes(s)
+    buf = ctypes.create_string_buffer(64)
+    p = ctypes.addressof(buf)
+    p16 = (p + 15) // 16 * 16
+    assert lib.moe_lora_align(ctypes.byref(s), None, p16, p16, need, None) == lm.MOE_LORA_EINVAL
+    assert lib.moe_lora_align(ctypes.byref(s), p16, p16, p16, need - 1, None) == lm.MOE_LORA_EWORKSPACE
+    assert lib.moe_lora_align(ctypes.byref(s), p16, p16, p16 + 4, need, None) == lm.MOE_LORA_EALIGN
+    args = [p16] * 11
+    assert lib.moe_lora_forward(ctypes.byref(s), *args, need - 1, p16, None) == lm.MOE_LORA_EWORKSPACE
+    bad = list(args)
+    bad[4] = p16 + 2  # W_gu misaligned
+    assert lib.moe_lora_forward(ctypes.byref(s), *bad[:10], p16, need, bad[10], None) == lm.MOE_LORA_EALIGN
+    bad = list(args)
+    bad[0] = None
+    assert lib.moe_lora_forward(ctypes.byref(s), *bad[:10], p16, need, bad[10], None) == lm.MOE_LORA_EINVAL
+    # T = 0 is a no-op that succeeds without any device call
+    s0 = lm.make_shape(0, 64, 32, 4, 2, 2, 8)
+    assert lib.moe_lora_align(ctypes.byref(s0), None, None, None, 0, None) == 0
+    n = ctypes.c_int32(7)
+    assert lib.moe_lora_device_errors(ctypes.byref(s0), p16, ctypes.byref(n), None) == 0
+    assert n.value == 0
+
+
+def test_view_offsets_are_aligned_and_disjoint(lib):
+    wl = synth.WORKLOADS[3]
+    s = shape_of(wl)
+    v = lm.moe_lora_workspace_view(s, type("T", (), {
+        "is_cuda": True, "is_contiguous": lambda self: True, "data_ptr": lambda self: 1 << 20})())
+    addrs = sorted(getattr(v, n) for n in ("sorted_ids", "expert_off", "seg_start", "seg_cnt",
+                                            "block_expert", "pos_of_pair", "z_gu", "z_down", "h", "d"))
+    assert all(a % 256 == 0 for a in addrs)
+    assert len(set(addrs)) == len(addrs)
+    assert v.d - (1 << 20) + v.cap_rows * wl.H * 4 <= lm.moe_lora_workspace_bytes(s)

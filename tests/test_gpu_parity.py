@@ -1,0 +1,201 @@
+"""Parity of the HIP path with the fp64 CPU reference (needs an MI355X).
+
+Align outputs are compared bit-exactly; layer outputs element-wise within
+|gpu - ref| <= 1e-2 + 1e-2*|ref| (bf16 inputs, fp32 accumulation), plus a
+relative-L2 bound and an adapter-delta check (the element-wise tolerance alone
+cannot see a dropped adapter on the small shapes)."""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+
+import synth
+from gpu_common import (compare, compare_delta, gpu_views, log, oracle_tokens, run_gpu,
+                        sample_tokens, shape_for, to_device)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import lora_moe_amd as lm
+    lm.load_library()
+
+
+# ------------------------------------------------------------------ align
+
+def align_gpu(T, k, E, L, bm, ids, lids):
+    import lora_moe_amd as lm
+    shape = lm.make_shape(T, 64, 64, E, k, L, 8, bm)
+    ws = lm.alloc_workspace(shape)
+    lm.moe_lora_align(shape, torch.from_numpy(np.ascontiguousarray(ids, np.int32)).cuda(),
+                      torch.from_numpy(np.ascontiguousarray(lids, np.int32)).cuda(), ws)
+    torch.cuda.synchronize()
+    return gpu_views(shape, ws), lm.moe_lora_device_errors(shape, ws)
+
+
+def check_align_exact(T, k, E, L, bm, ids, lids, what):
+    import oracle
+    log(f"align {what}: T={T} k={k} E={E} L={L} bm={bm}")
+    got, errs = align_gpu(T, k, E, L, bm, ids, lids)
+    want = oracle.Oracle().align(T, k, E, L, bm, ids, lids, got["cap_rows"], got["cap_blocks"])
+    assert got["num_padded"] == want["num_padded"], what
+    assert got["err_count"] == want["err_count"] == errs, what
+    for n in ("sorted_ids", "expert_off", "seg_start", "seg_cnt", "block_expert", "pos_of_pair"):
+        np.testing.assert_array_equal(got[n], want[n], err_msg=f"{what}: {n}")
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("bm", [16, 64, 256])
+def test_align_bitexact_workloads(n, bm):
+    wl = synth.WORKLOADS[n]
+    ids, _ = synth.make_routing(wl)
+    lids = synth.adapter_ids(wl)
+    check_align_exact(wl.T, wl.topk, wl.E, wl.L, bm, ids, lids, f"workload {n}")
+
+
+def test_align_adversarial():
+    import pins
+    for name, T, k, E, L, bm, ids, lids in pins.align_cases():
+        if T == 0:
+            continue
+        for b in sorted({bm, 16, 32, 128}):
+            check_align_exact(T, k, E, L, b, ids, lids, f"{name} bm={b}")
+    rng = np.random.default_rng(9)
+    # many chunks, one hot expert, ragged P
+    T, k, E, L = 3001, 3, 40, 5
+    ids = np.where(rng.random((T, k)) < 0.7, 7, rng.integers(0, E, (T, k))).astype(np.int32)
+    lids = rng.integers(-1, L, T).astype(np.int32)
+    check_align_exact(T, k, E, L, 64, ids, lids, "hot expert, 18 chunks")
+    check_align_exact(1, 1, 1, 1, 16, np.zeros((1, 1), np.int32), np.zeros(1, np.int32), "T=1")
+
+
+def test_align_deterministic():
+    wl = synth.WORKLOADS[4]
+    ids, _ = synth.make_routing(wl)
+    lids = synth.adapter_ids(wl)
+    a, _ = align_gpu(wl.T, wl.topk, wl.E, wl.L, 64, ids, lids)
+    b, _ = align_gpu(wl.T, wl.topk, wl.E, wl.L, 64, ids, lids)
+    for n in ("sorted_ids", "pos_of_pair", "block_expert"):
+        np.testing.assert_array_equal(a[n], b[n])
+
+
+# ------------------------------------------------------------------ layer, small shapes
+
+def full_check(inp, block_m=0, what="", scale=None):
+    if scale is not None:
+        inp = synth.Inputs(replace(inp.wl, scale=scale), **{k: v for k, v in inp.arrays().items()})
+    wl = inp.wl
+    log(f"layer {what}: T={wl.T} H={wl.H} I={wl.I} E={wl.E} k={wl.topk} L={wl.L} r={wl.r} bm={block_m}")
+    dev = to_device(inp)
+    y, shape, ws = run_gpu(dev, wl, block_m)
+    ref = oracle_tokens(inp, None)
+    compare(y, ref, what)
+    if (inp.lora_ids >= 0).any():
+        none = torch.full_like(dev["lora_ids"], -1)
+        y0, _, _ = run_gpu(dev, wl, block_m, lora_ids=none, workspace=ws)
+        ref0 = oracle_tokens(inp, None, lora_ids=np.full_like(inp.lora_ids, -1))
+        compare(y0, ref0, what + " (no adapters)")
+        compare_delta(y, y0, ref, ref0, what)
+    return y, ref
+
+
+@pytest.mark.parametrize("bm", [0, 16, 32, 64, 128, 256])
+def test_tiny_workload(bm):
+    inp = synth.make_inputs(1)
+    full_check(inp, bm, f"tiny bm={bm}")
+
+
+def test_tiny_scale_and_seed():
+    inp = synth.make_inputs(1, seed=3)
+    full_check(inp, 0, "tiny seed 3 scale 0.5", scale=0.5)
+
+
+@pytest.mark.parametrize("H,I,r", [(104, 104, 8), (104, 1000, 24), (1000, 104, 16), (2880, 2880, 64),
+                                   (256, 512, 128), (64, 40, 8)])
+def test_ragged_tails(H, I, r):
+    """K and N tails (the pages' K = 100 vs BLOCK_SIZE_K = 64 example, here
+    104 = 64 + 40) and every rank family."""
+    wl = synth.Workload("tail", T=37, H=H, I=I, E=5, topk=2, L=3, r=r,
+                        lora_mode="uniform_with_none", w_std=0.05)
+    full_check(synth.make_inputs(wl), 0, f"tails H={H} I={I} r={r}")
+
+
+def test_edge_cases():
+    base = synth.Workload("edge", T=50, H=256, I=128, E=6, topk=3, L=3, r=16,
+                          lora_mode="uniform_with_none", w_std=0.05)
+    # every token without adapter
+    inp = synth.make_inputs(replace(base, lora_mode="none"))
+    full_check(inp, 0, "no adapters")
+    # one token
+    full_check(synth.make_inputs(replace(base, T=1)), 0, "T=1")
+    # every token on the same three experts with the same adapter
+    inp = synth.make_inputs(replace(base, lora_mode="uniform"))
+    inp.topk_ids[:] = np.array([2, 4, 0], np.int32)
+    inp.lora_ids[:] = 1
+    full_check(inp, 16, "three hot buckets")
+    # invalid expert and adapter ids are dropped / treated as none and counted
+    inp = synth.make_inputs(base)
+    inp.topk_ids[3, 1] = 99
+    inp.topk_ids[7, 0] = -2
+    inp.lora_ids[5] = 17
+    inp.lora_ids[9] = -4
+    y, ref = full_check(inp, 0, "invalid ids")
+    import lora_moe_amd as lm
+    dev = to_device(inp)
+    _, shape, ws = run_gpu(dev, inp.wl)
+    assert lm.moe_lora_device_errors(shape, ws) == 4
+
+
+def test_shrink_stage_matches_reference():
+    """z = x A for every adapter row, against the reference's shrink output."""
+    import lora_moe_amd as lm
+    import oracle
+    inp = synth.make_inputs(1)
+    wl = inp.wl
+    dev = to_device(inp)
+    _, shape, ws = run_gpu(dev, wl)
+    t = lm.workspace_tensors(shape, ws)
+    zg = t["z_gu"].cpu().numpy()
+    pos = t["pos_of_pair"].cpu().numpy()
+    o = oracle.Oracle()
+    checked = 0
+    for tok in range(wl.T):
+        if inp.lora_ids[tok] < 0:
+            continue
+        for j in range(wl.topk):
+            st = o.pair((wl.T, wl.H, wl.I, wl.E, wl.topk, wl.L, wl.r), inp.x, inp.topk_ids,
+                        inp.lora_ids, inp.W_gu, inp.W_down, inp.A_gu, inp.B_gu, inp.A_down,
+                        inp.B_down, tok, j, scale=wl.scale)
+            got = zg[pos[tok * wl.topk + j]]
+            np.testing.assert_allclose(got, st["zg"], rtol=1e-4, atol=1e-4)
+            checked += 1
+    assert checked > 20
+
+
+# ------------------------------------------------------------------ full-size workloads
+
+@pytest.mark.parametrize("n,ntok", [(2, 16), (3, 24), (4, 24), (5, 8)])
+def test_workload_full_size_sampled(n, ntok):
+    """The benchmarked launch configuration at full size; the reference runs on
+    a sample of tokens."""
+    wl = synth.WORKLOADS[n]
+    log(f"workload {n} ({wl.name}): generating on device")
+    dev, inp = synth.device_inputs(wl, touched_only=True)
+    toks = sample_tokens(wl.T, ntok)
+    synth.host_slabs_for_tokens(inp, toks)
+    y, shape, ws = run_gpu(dev, wl)
+    ref = oracle_tokens(inp, toks)
+    compare(y[toks], ref, f"workload {n}")
+    none = torch.full_like(dev["lora_ids"], -1)
+    y0, _, _ = run_gpu(dev, wl, lora_ids=none, workspace=ws)
+    ref0 = oracle_tokens(inp, toks, lora_ids=np.full_like(inp.lora_ids, -1))
+    compare(y0[toks], ref0, f"workload {n} (no adapters)")
+    compare_delta(y[toks], y0[toks], ref, ref0, f"workload {n}")
+    assert np.all(np.isfinite(y))
+    del dev, ws
+    torch.cuda.empty_cache()
