@@ -35,7 +35,8 @@ static int resolve_bm(const moe_lora_shape* s) {
   const int64_t rows = (P + touched - 1) / touched;
   if (rows <= 16) return 16;
   if (rows <= 32) return 32;
-  return 64;
+  if (rows < 96) return 64;
+  return 128;  // LDS-tiled GEMM family
 }
 
 int make_layout(const moe_lora_shape* s, Layout* L) {
@@ -261,7 +262,9 @@ int moe_lora_profile_begin(int max_calls) {
   prof_release();
   g_prof.ev.resize((size_t)max_calls * ST_COUNT * 2);
   for (auto& e : g_prof.ev)
-    if (hipEventCreate(&e) != hipSuccess) {
+    // no system-scope fence: a plain event between two kernels adds a
+    // ~10 us bubble, which would distort the stages it brackets
+    if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) {
       e = nullptr;
       prof_release();
       return MOE_LORA_EHIP;

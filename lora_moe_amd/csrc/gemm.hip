@@ -32,21 +32,6 @@ namespace moelora {
 
 namespace {
 
-struct GemmParams {
-  const uint16_t* in;      // mode 0: x [T][K]; mode 1: h [cap_rows][K]
-  const uint16_t* W;       // [E][N][K]
-  const uint16_t* B;       // [L][E][N][r]
-  const float* z;          // [cap_rows][r]
-  const int32_t* sorted;
-  const int32_t* bexp;
-  const int32_t* hdr;
-  const int32_t* lora_ids;
-  const float* topk_w;
-  uint16_t* h_out;         // mode 0: [cap_rows][I]
-  float* d_out;            // mode 1: [cap_rows][H]
-  int K, N, I, H, E, L, r, topk, P, bm, nsteps;
-  float s;
-};
 
 // s * sum_q z[q] * B[q] with z fp32 and B a bf16 row of length r (r % 8 == 0)
 __device__ __forceinline__ float expand_dot(const float* __restrict__ z,
@@ -236,6 +221,8 @@ int launch_gemm(const Layout& L, int mode, const uint16_t* in, const int32_t* lo
   gp.z = mode == 0 ? w.zgu : w.zd;
   gp.sorted = w.sorted;
   gp.bexp = w.bexp;
+  gp.segstart = w.segstart;
+  gp.segcnt = w.segcnt;
   gp.hdr = w.hdr;
   gp.lora_ids = lora_ids;
   gp.topk_w = topk_weights;
@@ -253,6 +240,10 @@ int launch_gemm(const Layout& L, int mode, const uint16_t* in, const int32_t* lo
   gp.bm = L.bm;
   gp.nsteps = (gp.K + 63) / 64;
   gp.s = L.s;
+  if (L.bm >= 128) {
+    launch_gemm_tiled(gp, mode, L.cap_rows, st);
+    return hipGetLastError() == hipSuccess ? MOE_LORA_OK : MOE_LORA_EHIP;
+  }
   const int RF = L.bm >= 64 ? 4 : L.bm / 16;
   const int MT = RF * 16;
   const int ncol = mode == 0 ? (L.I + 31) / 32 : (L.H + 63) / 64;

@@ -79,6 +79,25 @@ inline WsPtrs ws_ptrs(void* base, const Layout& L) {
   return w;
 }
 
+// Arguments of the grouped GEMM kernels (both families).
+struct GemmParams {
+  const uint16_t* in;      // mode 0: x [T][K]; mode 1: h [cap_rows][K]
+  const uint16_t* W;       // [E][N][K]
+  const uint16_t* B;       // [L][E][N][r]
+  const float* z;          // [cap_rows][r]
+  const int32_t* sorted;
+  const int32_t* bexp;
+  const int32_t* segstart;  // [E][L+1] first row of each (expert, slot) segment
+  const int32_t* segcnt;    // [E][L+1] rows in it
+  const int32_t* hdr;
+  const int32_t* lora_ids;
+  const float* topk_w;
+  uint16_t* h_out;         // mode 0: [cap_rows][I]
+  float* d_out;            // mode 1: [cap_rows][H]
+  int K, N, I, H, E, L, r, topk, P, bm, nsteps;
+  float s;
+};
+
 // ------------------------------------------------------------------ stage timing
 
 enum Stage {
@@ -116,6 +135,9 @@ int launch_shrink(const Layout& L, int mode, const uint16_t* in, const uint16_t*
 int launch_gemm(const Layout& L, int mode, const uint16_t* x, const int32_t* lora_ids,
                 const float* topk_weights, const uint16_t* W, const uint16_t* B, void* ws,
                 hipStream_t st);
+
+// The LDS-tiled family, used when block_m >= 128 (defined in gemm_tiled.hip).
+void launch_gemm_tiled(const GemmParams& gp, int mode, int64_t cap_rows, hipStream_t st);
 
 int launch_combine(const Layout& L, void* ws, uint16_t* y, hipStream_t st);
 

@@ -115,14 +115,16 @@ def test_tiny_scale_and_seed():
     full_check(inp, 0, "tiny seed 3 scale 0.5", scale=0.5)
 
 
+@pytest.mark.parametrize("bm", [0, 128])
 @pytest.mark.parametrize("H,I,r", [(104, 104, 8), (104, 1000, 24), (1000, 104, 16), (2880, 2880, 64),
                                    (256, 512, 128), (64, 40, 8)])
-def test_ragged_tails(H, I, r):
+def test_ragged_tails(H, I, r, bm):
     """K and N tails (the pages' K = 100 vs BLOCK_SIZE_K = 64 example, here
-    104 = 64 + 40) and every rank family."""
+    104 = 64 + 40) and every rank family, on both GEMM families (block_m 128
+    selects the LDS-tiled one)."""
     wl = synth.Workload("tail", T=37, H=H, I=I, E=5, topk=2, L=3, r=r,
                         lora_mode="uniform_with_none")
-    full_check(synth.make_inputs(wl), 0, f"tails H={H} I={I} r={r}")
+    full_check(synth.make_inputs(wl), bm, f"tails H={H} I={I} r={r} bm={bm}")
 
 
 def test_edge_cases():
