@@ -22,7 +22,11 @@ static int check_shape(const moe_lora_shape* s) {
   // every index into the row-major buffers must fit the kernels' int arithmetic
   const int64_t P = (int64_t)s->T * s->topk;
   const int64_t cap = P + (int64_t)s->E * 255;
-  if (P > (1LL << 30) || cap > (1LL << 30) || (int64_t)s->H * s->I > (1LL << 40))
+  if (P > (1LL << 30) || cap > (1LL << 30)) return MOE_LORA_EUNSUPPORTED;
+  // the streaming GEMM addresses one expert's weights, x and the intermediate
+  // rows with 32-bit element offsets
+  const int64_t lim = 1LL << 32;
+  if ((int64_t)2 * s->I * s->H >= lim || (int64_t)s->T * s->H >= lim || cap * s->I >= lim)
     return MOE_LORA_EUNSUPPORTED;
   return MOE_LORA_OK;
 }

@@ -15,16 +15,11 @@
 // mode 1 (down): a workgroup owns 64 output columns; the epilogue adds the
 //   expand and multiplies by the pair's top-k weight; d is stored fp32.
 //
-// A workgroup (4 wavefronts) takes one tile of 16*RF rows -- rows of a single
-// expert, since expert runs are padded to block_m, a multiple of the tile --
-// by 64 columns.  The wavefronts split K in interleaved 64-wide steps and each
-// accumulates the whole tile with bf16 MFMA 16x16x32; operands come straight
-// from global memory into registers (every weight element is used by exactly
-// one workgroup per row tile, so staging them in LDS buys nothing at decode
-// row counts).  Each lane loads 32 contiguous bytes of a row per step and
-// feeds them to two MFMAs, so the K order inside a step is permuted
-// identically for both operands.  Partial tiles are added through LDS and
-// wavefront 0 runs the epilogue.
+// This family serves small row counts per expert (block_m <= 64, decode):
+// every weight byte is used by one row tile only, so the kernel is a weight
+// stream and is organised around HBM efficiency -- see the kernel comment.
+// Row tiles hold 16 or 32 rows of a single expert (expert runs are padded to
+// block_m, a multiple of the tile).
 #include "device_util.h"
 #include "internal.h"
 
@@ -48,119 +43,148 @@ __device__ __forceinline__ float expand_dot(const float* __restrict__ z,
   return acc;
 }
 
-template <int MODE, int RF, bool EVEN>
+#ifndef MOELORA_STREAM_ROTATE
+#define MOELORA_STREAM_ROTATE 1  // stagger the K start per wavefront
+#endif
+
+// Tile: 16*RF rows x 64 weight rows per workgroup, 16 weight rows per
+// wavefront.  mode 0: wavefront w owns gate rows j0+8w..j0+8w+7 and the
+// matching up rows I+j0+8w.., so one MFMA column fragment holds 8 gate and 8
+// up columns; mode 1: wavefront w owns output columns n0+16w..n0+16w+15.
+//
+// The kernel is a weight stream, and HBM only reaches its bandwidth with many
+// requests outstanding and spread over its channels:
+//  * each wavefront streams its 16 weight rows in chunks of KC = 128 K
+//    elements; a load instruction covers 4 rows x 256 contiguous bytes (whole
+//    128-byte lines); DEPTH chunks are in flight in registers; each chunk is
+//    written to a wavefront-private LDS slice with its 16-byte pieces
+//    XOR-swizzled (piece ^ row), so the MFMA fragment reads (16 rows, same K
+//    piece) spread over all banks.  The slice is private, so no workgroup
+//    barrier is needed: LDS operations of one wavefront complete in order.
+//    The next chunk's loads are issued before this chunk's MFMAs; deeper
+//    register prefetch measured slower (it costs occupancy);
+//  * each wavefront starts at its own K chunk and wraps around: weight rows
+//    lie K*2 bytes apart, so wavefronts walking K in lockstep would hit the
+//    same HBM channels at once (staggering measured +18% on this pattern);
+//  * row fragments (x gathered by token, or h) come from L2 with the weight
+//    chunk they meet; padding rows point at the tile's first row, so their
+//    loads coalesce with it (their outputs are dropped);
+//  * steady-state loads are unconditional (full chunks; the K remainder is
+//    one masked chunk at the end): a load under a branch makes the compiler
+//    drain all outstanding loads before it.
+template <int MODE, int RF>
 __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmParams p) {
-  constexpr int MT = RF * 16;
-  __shared__ float red[2][MT][64 + 1];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  constexpr int KC = 128;
+  __shared__ __attribute__((aligned(16))) uint16_t wl[4][16 * KC];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps chunk math scalar
   const int m = lane & 15, kq = lane >> 4;
-  const int row0 = blockIdx.y * MT;
+  const int row0 = blockIdx.y * (RF * 16);
   if (row0 >= p.hdr[HDR_NUM_PADDED]) return;
   const int e = p.bexp[row0 / p.bm];
 
-  // operand rows
-  const uint16_t* arow[RF];
+  // weight row held by fragment column c (0..15) of this wavefront
+  auto wrow_of = [&](int c) -> int {
+    if (MODE == 0) {
+      const int j = min((int)blockIdx.x * 32 + wave * 8 + (c & 7), p.I - 1);
+      return c < 8 ? j : p.I + j;
+    }
+    return min((int)blockIdx.x * 64 + wave * 16 + c, p.N - 1);
+  };
+  const uint16_t* __restrict__ Wexp = p.W + (size_t)e * p.N * p.K;
+  // instruction i covers fragment rows 4i..4i+3 (16 lanes x 16 bytes per
+  // row); element offsets from the expert's base fit 32 bits
+  const int piece = lane & 15;
+  uint32_t woff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) woff[i] = (uint32_t)wrow_of(4 * i + (lane >> 4)) * (uint32_t)p.K;
+
+  // row offsets (elements) from p.in; they fit 32 bits (checked on the host)
+  uint32_t aoff[RF];
 #pragma unroll
   for (int rf = 0; rf < RF; ++rf) {
-    const int row = row0 + rf * 16 + m;
-    if (MODE == 0) {
-      const int pr = p.sorted[row];
-      const int t = pr < p.P ? pr / p.topk : 0;  // pad rows read token 0; their output is dropped
-      arow[rf] = p.in + (size_t)t * p.K;
-    } else {
-      arow[rf] = p.in + (size_t)row * p.K;
+    int row = row0 + rf * 16 + m;
+    int pr = p.sorted[row];
+    if (pr >= p.P) {  // padding row: read the tile's first row instead
+      row = row0;
+      pr = p.sorted[row0];
     }
-  }
-  const uint16_t* wrow[4];
-  const uint16_t* Wexp = p.W + (size_t)e * p.N * p.K;
-#pragma unroll
-  for (int f = 0; f < 4; ++f) {
-    int n;
-    if (MODE == 0) {
-      const int j = min(blockIdx.x * 32 + (f & 1) * 16 + m, p.I - 1);
-      n = (f < 2) ? j : p.I + j;
-    } else {
-      n = min(blockIdx.x * 64 + f * 16 + m, p.N - 1);
-    }
-    wrow[f] = Wexp + (size_t)n * p.K;
+    if (MODE == 0)
+      aoff[rf] = (uint32_t)(pr < p.P ? pr / p.topk : 0) * (uint32_t)p.K;
+    else
+      aoff[rf] = (uint32_t)row * (uint32_t)p.K;
   }
 
-  f32x4_t acc[RF][4];
-#pragma unroll
-  for (int rf = 0; rf < RF; ++rf)
-#pragma unroll
-    for (int f = 0; f < 4; ++f) acc[rf][f] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // full 128-wide chunks run unmasked in rotated order; a K remainder (a
+  // multiple of 8 below 128) is one masked chunk at the end
+  const int nfull = p.K / KC, krem = p.K - nfull * KC;
+  const int rot = (MOELORA_STREAM_ROTATE && nfull) ? (int)((blockIdx.x * 4u + wave) * 7u % (unsigned)nfull) : 0;
 
-  constexpr int U = 2;  // K steps in flight per wavefront
-  for (int ks = wave; ks < p.nsteps; ks += 4 * U) {
-    u32x4_t a0[U][RF], a1[U][RF], b0[U][4], b1[U][4];
+  u32x4_t rw[4], rx[RF][4];
+  auto load = [&](int k0, bool masked) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int kb = (ks + 4 * u) * 64 + kq * 16;
-      const bool live = ks + 4 * u < p.nsteps;
-      const bool v0 = live && (EVEN || kb < p.K), v1 = live && (EVEN || kb + 8 < p.K);
-#pragma unroll
-      for (int rf = 0; rf < RF; ++rf) {
-        a0[u][rf] = v0 ? ld16(arow[rf] + kb) : zero4();
-        a1[u][rf] = v1 ? ld16(arow[rf] + kb + 8) : zero4();
-      }
-#pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        b0[u][f] = v0 ? ld16(wrow[f] + kb) : zero4();
-        b1[u][f] = v1 ? ld16(wrow[f] + kb + 8) : zero4();
-      }
+    for (int i = 0; i < 4; ++i) {
+      const bool ok = !masked || piece * 8 < krem;
+      rw[i] = ok ? ld16(Wexp + (woff[i] + (uint32_t)(k0 + piece * 8))) : zero4();
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+    for (int s = 0; s < 4; ++s) {
+      const int kk = (4 * s + kq) * 8;
+      const bool ok = !masked || kk < krem;
 #pragma unroll
       for (int rf = 0; rf < RF; ++rf)
-#pragma unroll
-        for (int f = 0; f < 4; ++f) {
-          acc[rf][f] = mfma_16x16x32(a0[u][rf], b0[u][f], acc[rf][f]);
-          acc[rf][f] = mfma_16x16x32(a1[u][rf], b1[u][f], acc[rf][f]);
-        }
-  }
+        rx[rf][s] = ok ? ld16(p.in + (aoff[rf] + (uint32_t)(k0 + kk))) : zero4();
+    }
+  };
+  uint16_t* slice = wl[wave];
 
-  // add the four partial tiles: (2,3) -> (0,1) -> 0
-  if (wave >= 2) {
+  f32x4_t acc[RF];
 #pragma unroll
-    for (int rf = 0; rf < RF; ++rf)
-#pragma unroll
-      for (int f = 0; f < 4; ++f)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) red[wave - 2][rf * 16 + 4 * kq + i][f * 16 + m] = acc[rf][f][i];
-  }
-  __syncthreads();
-  if (wave < 2) {
-#pragma unroll
-    for (int rf = 0; rf < RF; ++rf)
-#pragma unroll
-      for (int f = 0; f < 4; ++f)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[rf][f][i] += red[wave][rf * 16 + 4 * kq + i][f * 16 + m];
-  }
-  __syncthreads();
-  if (wave == 1) {
-#pragma unroll
-    for (int rf = 0; rf < RF; ++rf)
-#pragma unroll
-      for (int f = 0; f < 4; ++f)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) red[0][rf * 16 + 4 * kq + i][f * 16 + m] = acc[rf][f][i];
-  }
-  __syncthreads();
-  if (wave != 0) return;
-#pragma unroll
-  for (int rf = 0; rf < RF; ++rf)
-#pragma unroll
-    for (int f = 0; f < 4; ++f)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[rf][f][i] += red[0][rf * 16 + 4 * kq + i][f * 16 + m];
+  for (int rf = 0; rf < RF; ++rf) acc[rf] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // epilogue: rows rf*16 + 4*kq + i, columns f*16 + m
+  // the chunk in registers: weight pieces -> LDS slice (swizzled), row
+  // fragments kept aside, then the next chunk's loads are issued before the
+  // MFMAs of this one
+  auto consume = [&](int next_k0, int next_kind) {  // kind: 0 none, 1 full, 2 masked remainder
 #pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int fr = 4 * i + (lane >> 4);
+      *reinterpret_cast<u32x4_t*>(&slice[fr * KC + ((piece ^ fr) << 3)]) = rw[i];
+    }
+    u32x4_t xa[RF][4];
+#pragma unroll
+    for (int rf = 0; rf < RF; ++rf)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) xa[rf][s] = rx[rf][s];
+    if (next_kind) load(next_k0, next_kind == 2);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const u32x4_t b =
+          *reinterpret_cast<const u32x4_t*>(&slice[m * KC + (((4 * s + kq) ^ m) << 3)]);
+#pragma unroll
+      for (int rf = 0; rf < RF; ++rf) acc[rf] = mfma_16x16x32(xa[rf][s], b, acc[rf]);
+    }
+  };
+
+  if (nfull > 0) {
+    load(rot * KC, false);
+    int c = rot;
+    for (int q = 0; q + 1 < nfull; ++q) {  // steady state: unconditional refills
+      c = c + 1 == nfull ? 0 : c + 1;
+      consume(c * KC, 1);
+    }
+    consume(nfull * KC, krem ? 2 : 0);
+  } else {
+    load(0, true);
+  }
+  if (krem) consume(0, 0);
+
+  // epilogue: lane (m, kq) holds rows rf*16 + 4*kq + i of fragment column m,
+  // i.e. weight row wrow_of(m); the expand is added per lane for that row
+  const int wr = wrow_of(m);
+#pragma unroll 1
   for (int rf = 0; rf < RF; ++rf)
-#pragma unroll
+#pragma unroll 1
     for (int i = 0; i < 4; ++i) {
       const int row = row0 + rf * 16 + 4 * kq + i;
       const int pr = p.sorted[row];
@@ -170,42 +194,27 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmParams p) {
         l = p.lora_ids[pr / p.topk];
         if (!(l >= 0 && l < p.L)) l = -1;
       }
-      const float* zr = p.z + (size_t)row * p.r;
-      const uint16_t* Bl = l >= 0 ? p.B + ((size_t)l * p.E + e) * p.N * p.r : nullptr;
+      float v = acc[rf][i];
+      if (l >= 0)
+        v += p.s * expand_dot(p.z + (size_t)row * p.r,
+                              p.B + (((size_t)l * p.E + e) * p.N + wr) * p.r, p.r);
       if (MODE == 0) {
-#pragma unroll
-        for (int f = 0; f < 2; ++f) {
-          const int j = blockIdx.x * 32 + f * 16 + m;
-          if (j >= p.I) continue;
-          float gate = acc[rf][f][i], up = acc[rf][f + 2][i];
-          if (l >= 0) {
-            gate += p.s * expand_dot(zr, Bl + (size_t)j * p.r, p.r);
-            up += p.s * expand_dot(zr, Bl + (size_t)(p.I + j) * p.r, p.r);
-          }
-          const float hv = real ? silu_f32(gate) * up : 0.f;
-          p.h_out[(size_t)row * p.I + j] = f32_to_bf16(hv);
-        }
+        const float up = __shfl_xor(v, 8, 64);  // lane m < 8: gate; m + 8: its up
+        const int j = blockIdx.x * 32 + wave * 8 + m;
+        if (m < 8 && j < p.I)
+          p.h_out[(size_t)row * p.I + j] = f32_to_bf16(real ? silu_f32(v) * up : 0.f);
       } else {
-        if (!real) continue;
-        const float w = p.topk_w[pr];
-#pragma unroll
-        for (int f = 0; f < 4; ++f) {
-          const int n = blockIdx.x * 64 + f * 16 + m;
-          if (n >= p.N) continue;
-          float v = acc[rf][f][i];
-          if (l >= 0) v += p.s * expand_dot(zr, Bl + (size_t)n * p.r, p.r);
-          p.d_out[(size_t)row * p.H + n] = v * w;
-        }
+        const int n = blockIdx.x * 64 + wave * 16 + m;
+        if (real && n < p.N) p.d_out[(size_t)row * p.H + n] = v * p.topk_w[pr];
       }
     }
 }
 
 template <int MODE, int RF>
-void launch_t(const GemmParams& gp, bool even, dim3 grid, hipStream_t st) {
-  if (even)
-    grouped_gemm_kernel<MODE, RF, true><<<grid, 256, 0, st>>>(gp);
-  else
-    grouped_gemm_kernel<MODE, RF, false><<<grid, 256, 0, st>>>(gp);
+void launch_rf(const GemmParams& gp, int64_t cap_rows, hipStream_t st) {
+  const int ncol = MODE == 0 ? (gp.I + 31) / 32 : (gp.H + 63) / 64;
+  dim3 grid(ncol, (unsigned)((cap_rows + RF * 16 - 1) / (RF * 16)));
+  grouped_gemm_kernel<MODE, RF><<<grid, 256, 0, st>>>(gp);
 }
 
 }  // namespace
@@ -244,19 +253,14 @@ int launch_gemm(const Layout& L, int mode, const uint16_t* in, const int32_t* lo
     launch_gemm_tiled(gp, mode, L.cap_rows, st);
     return hipGetLastError() == hipSuccess ? MOE_LORA_OK : MOE_LORA_EHIP;
   }
-  const int RF = L.bm >= 64 ? 4 : L.bm / 16;
-  const int MT = RF * 16;
-  const int ncol = mode == 0 ? (L.I + 31) / 32 : (L.H + 63) / 64;
-  dim3 grid(ncol, (unsigned)((L.cap_rows + MT - 1) / MT));
-  const bool even = gp.K % 64 == 0;
+  // 16- or 32-row tiles (a 64-row block is two tiles of one expert)
+  const int RF = L.bm >= 32 ? 2 : 1;
   if (mode == 0) {
-    if (RF == 4) launch_t<0, 4>(gp, even, grid, st);
-    else if (RF == 2) launch_t<0, 2>(gp, even, grid, st);
-    else launch_t<0, 1>(gp, even, grid, st);
+    if (RF == 2) launch_rf<0, 2>(gp, L.cap_rows, st);
+    else launch_rf<0, 1>(gp, L.cap_rows, st);
   } else {
-    if (RF == 4) launch_t<1, 4>(gp, even, grid, st);
-    else if (RF == 2) launch_t<1, 2>(gp, even, grid, st);
-    else launch_t<1, 1>(gp, even, grid, st);
+    if (RF == 2) launch_rf<1, 2>(gp, L.cap_rows, st);
+    else launch_rf<1, 1>(gp, L.cap_rows, st);
   }
   return hipGetLastError() == hipSuccess ? MOE_LORA_OK : MOE_LORA_EHIP;
 }
