@@ -37,10 +37,12 @@ static int resolve_bm(const moe_lora_shape* s) {
   const int64_t P = (int64_t)s->T * s->topk;
   const int64_t touched = std::max<int64_t>(1, std::min<int64_t>(s->E, P));
   const int64_t rows = (P + touched - 1) / touched;
+  // up to ~24 rows per expert the weight stream dominates (streaming GEMM
+  // family); beyond that a 128-row tile reads each expert's weights once
+  // (LDS-tiled family)
   if (rows <= 16) return 16;
-  if (rows <= 32) return 32;
-  if (rows < 96) return 64;
-  return 128;  // LDS-tiled GEMM family
+  if (rows <= 24) return 32;
+  return 128;
 }
 
 int make_layout(const moe_lora_shape* s, Layout* L) {

@@ -18,6 +18,8 @@
 //      segment starts, block -> expert map, pad sentinels and the list of
 //      shrink tiles (<= TS rows of one segment each);
 //   4. place: row of pair p = segment start + chunk prefix + rank.
+// Small batches (at most 1024 pairs, decode) run all of it in one
+// single-workgroup kernel instead, with the counts and offsets in LDS.
 #include "device_util.h"
 #include "internal.h"
 
@@ -205,6 +207,151 @@ __global__ __launch_bounds__(256) void align_place_kernel(
   }
 }
 
+constexpr int kSmallMaxPairs = 1024;
+constexpr int kSmallMaxBuckets = 6144;  // keeps the LDS use under 64 KB
+
+// The whole align for P <= 1024 in one workgroup of 1024 threads (thread =
+// pair), same outputs as the four-kernel path.
+__global__ __launch_bounds__(1024) void align_small_kernel(
+    const int32_t* __restrict__ topk_ids, const int32_t* __restrict__ lora_ids, int P, int k, int E,
+    int L, int bm, int64_t cap_rows, int64_t cap_blocks, int TS, int r, int zero_gu, int zero_d,
+    int32_t* __restrict__ hdr, int32_t* __restrict__ sorted, int32_t* __restrict__ eoff,
+    int32_t* __restrict__ segstart, int32_t* __restrict__ segcnt, int32_t* __restrict__ bexp,
+    int32_t* __restrict__ pos, LoraTile* __restrict__ tiles, float* __restrict__ zgu,
+    float* __restrict__ zd) {
+  extern __shared__ int lds[];
+  const int S = L + 1, NB = E * S;
+  int* cnt = lds;                    // [NB]
+  int* sst = cnt + NB;               // [NB] segment starts
+  int* s_eoff = sst + NB;            // [E+1]
+  int* scan = s_eoff + E + 1;        // [16]
+  int* errs = scan + 16;             // [1]
+  const int tid = threadIdx.x, nt = blockDim.x;
+  for (int b = tid; b < NB; b += nt) cnt[b] = 0;
+  if (tid == 0) errs[0] = 0;
+  int key = -1, err = 0, l = -1;
+  if (tid < P) key = pair_key(topk_ids, lora_ids, tid, k, E, L, &l, &err);
+  // Stable rank = earlier pairs with the same key.  Inside a wavefront:
+  // group lanes by key with ballots (one round per distinct key); across
+  // wavefronts: the wavefronts take turns reading and advancing the per-key
+  // running count, in order, so the result is deterministic.
+  const int lane = tid & 63, wave = tid >> 6;
+  const unsigned long long below = (1ull << lane) - 1ull;
+  unsigned long long todo = __ballot(key >= 0);
+  int rin = 0, gsize = 0;
+  bool leader = false;
+  while (todo) {
+    const int src = __ffsll((long long)todo) - 1;
+    const int kk = __shfl(key, src, 64);
+    const unsigned long long grp = __ballot(key == kk) & todo;
+    if (key == kk && key >= 0) {
+      rin = __popcll(grp & below);
+      gsize = __popcll(grp);
+      leader = lane == src;
+    }
+    todo &= ~grp;
+  }
+  __syncthreads();  // cnt and errs cleared
+  if (err) atomicAdd(&errs[0], err);
+  int rnk = 0;
+  const int nw = (min(P, nt) + 63) >> 6;
+  for (int w = 0; w < nw; ++w) {
+    if (wave == w && key >= 0) {
+      const int base = cnt[key];  // every lane reads before the leaders write (in-order LDS)
+      rnk = base + rin;
+      if (leader) cnt[key] = base + gsize;
+    }
+    __syncthreads();
+  }
+
+  // padded expert sizes, scanned over experts (each thread owns a range)
+  const int per = (E + nt - 1) / nt;
+  const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
+  int local = 0;
+  for (int e = e0; e < e1; ++e) {
+    int n = 0;
+    for (int s = 0; s < S; ++s) n += cnt[e * S + s];
+    local += (n + bm - 1) / bm * bm;
+  }
+  int total;
+  int at = block_exclusive_scan(local, scan, &total);
+  for (int e = e0; e < e1; ++e) {
+    s_eoff[e] = at;
+    eoff[e] = at;
+    int n = 0;
+    for (int s = 0; s < S; ++s) {
+      sst[e * S + s] = at + n;
+      segstart[e * S + s] = at + n;
+      segcnt[e * S + s] = cnt[e * S + s];
+      n += cnt[e * S + s];
+    }
+    for (int row = at + n; row < at + (n + bm - 1) / bm * bm; ++row) sorted[row] = P;  // pads
+    at += (n + bm - 1) / bm * bm;
+  }
+  if (tid == 0) {
+    s_eoff[E] = total;
+    eoff[E] = total;
+  }
+  __syncthreads();
+  const int num_padded = total;
+  for (int64_t row = num_padded + tid; row < cap_rows; row += nt) sorted[row] = P;
+  for (int64_t b = tid; b < cap_blocks; b += nt) {
+    const int64_t row = b * bm;
+    int e = -1;
+    if (row < num_padded) {  // the last expert whose run starts at or before row
+      int lo = 0, hi = E - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_eoff[mid] <= row) lo = mid; else hi = mid - 1;
+      }
+      e = lo;
+    }
+    bexp[b] = e;
+  }
+  if (tid < P) {
+    if (key < 0) {
+      pos[tid] = -1;
+    } else {
+      const int row = sst[key] + rnk;
+      sorted[row] = tid;
+      pos[tid] = row;
+      if (l >= 0) {
+        for (int q = 0; q < r; q += 4) {
+          const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+          if (zero_gu) *reinterpret_cast<float4*>(zgu + (size_t)row * r + q) = z;
+          if (zero_d) *reinterpret_cast<float4*>(zd + (size_t)row * r + q) = z;
+        }
+      }
+    }
+  }
+
+  // shrink tiles: segments (e, l < L) cut into pieces of <= TS rows
+  const int NS = E * L;
+  const int perS = (NS + nt - 1) / nt;
+  const int s0 = min(NS, tid * perS), s1 = min(NS, s0 + perS);
+  int lt = 0;
+  for (int i = s0; i < s1; ++i) lt += (cnt[(i / L) * S + i % L] + TS - 1) / TS;
+  int ntiles;
+  int tb = block_exclusive_scan(lt, scan, &ntiles);
+  for (int i = s0; i < s1; ++i) {
+    const int e = i / L, ll = i % L;
+    const int c = cnt[e * S + ll], st = sst[e * S + ll];
+    for (int o = 0; o < c; o += TS) {
+      LoraTile tl;
+      tl.e = e;
+      tl.l = ll;
+      tl.row0 = st + o;
+      tl.n = min(TS, c - o);
+      tiles[tb++] = tl;
+    }
+  }
+  if (tid == 0) {
+    hdr[HDR_NUM_PADDED] = num_padded;
+    hdr[HDR_ERR] = errs[0];
+    hdr[HDR_NTILES] = ntiles;
+  }
+}
+
 }  // namespace
 
 int launch_align(const Layout& L, const int32_t* topk_ids, const int32_t* lora_ids, void* ws,
@@ -212,6 +359,17 @@ int launch_align(const Layout& L, const int32_t* topk_ids, const int32_t* lora_i
   WsPtrs w = ws_ptrs(ws, L);
   const int P = (int)L.P, NB = (int)L.NB, C = (int)L.C;
   if (P <= 0) return MOE_LORA_OK;  // no pairs: nothing to sort
+  const int zero_gu = plan_shrink(L, L.H).splits > 1;
+  const int zero_d = plan_shrink(L, L.I).splits > 1;
+  if (P <= kSmallMaxPairs && NB <= kSmallMaxBuckets) {
+    prof_stage_begin(ST_ALIGN_PLACE, st);
+    const size_t lds = sizeof(int) * (2 * NB + L.E + 1 + 16 + 1);
+    align_small_kernel<<<1, kSmallMaxPairs, lds, st>>>(
+        topk_ids, lora_ids, P, L.k, L.E, L.L, L.bm, L.cap_rows, L.cap_blocks, (int)L.TS, L.r, zero_gu,
+        zero_d, w.hdr, w.sorted, w.eoff, w.segstart, w.segcnt, w.bexp, w.pos, w.tiles, w.zgu, w.zd);
+    prof_stage_end(ST_ALIGN_PLACE, st);
+    return hipGetLastError() == hipSuccess ? MOE_LORA_OK : MOE_LORA_EHIP;
+  }
   prof_stage_begin(ST_ALIGN_COUNT, st);
   align_count_kernel<<<C, kAlignChunk, (NB + kAlignChunk + 1) * sizeof(int), st>>>(
       topk_ids, lora_ids, P, L.k, L.E, L.L, NB, C, w.chunk, w.chunkerr, w.rank);
@@ -221,8 +379,6 @@ int launch_align(const Layout& L, const int32_t* topk_ids, const int32_t* lora_i
   align_offsets_kernel<<<1, 1024, (16 + L.E + 1) * sizeof(int), st>>>(
       P, L.E, L.L, C, L.bm, L.cap_rows, L.cap_blocks, (int)L.TS, w.chunkerr, w.segcnt, w.hdr,
       w.sorted, w.eoff, w.segstart, w.bexp, w.tiles);
-  const int zero_gu = plan_shrink(L, L.H).splits > 1;
-  const int zero_d = plan_shrink(L, L.I).splits > 1;
   align_place_kernel<<<(P + 255) / 256, 256, 0, st>>>(topk_ids, lora_ids, P, L.k, L.E, L.L, C, L.r,
                                                       zero_gu, zero_d, w.chunk, w.rank, w.segstart,
                                                       w.sorted, w.pos, w.zgu, w.zd);

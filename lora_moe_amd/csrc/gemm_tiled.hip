@@ -11,10 +11,11 @@
 //     a 2 x 2 grid, each owning 64 x 64 = 2 x 2 tiles of the bf16 MFMA
 //     32x32x16;
 //   * A (gathered x rows or h rows) and W tiles go global -> registers ->
-//     LDS, double-buffered, so the loads of step k+1 are in flight while step
-//     k multiplies; each 128-byte LDS row stores its eight 16-byte chunks in
-//     XOR-swizzled order (chunk ^ (row & 7)) so that both the row-wise stores
-//     and the column-wise 16-byte fragment reads are free of bank conflicts;
+//     LDS: tile q multiplies from one LDS buffer while tile q+1 waits in
+//     registers and tile q+2 is in flight; each 128-byte LDS row stores its
+//     eight 16-byte chunks XOR-swizzled (chunk ^ (row & 7)) so that both the
+//     row-wise stores and the column-wise fragment reads avoid bank
+//     conflicts; the K remainder is one masked tile;
 //   * the expand runs as extra MFMAs over the rank dimension after the main
 //     loop: for each (expert, adapter) segment that meets the wavefront's rows,
 //     the A operand is z of those rows (zero elsewhere) and the B operand the
@@ -44,12 +45,56 @@ __device__ __forceinline__ f32x16_t mfma_32x32x16(u32x4_t a, u32x4_t b, f32x16_t
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+#ifndef MOELORA_TILED_ROTATE
+#define MOELORA_TILED_ROTATE 0  // rotate the K-tile order per workgroup
+#endif
+
 constexpr int TBM = 128, TBN = 128, TBK = 64;
 constexpr int ROW_BYTES = TBK * 2;              // one tile row in LDS
 constexpr int TILE_BYTES = TBM * ROW_BYTES;     // 16 KB (A and B tiles alike)
 
+// A 16-lane phase of a 16-byte LDS access covers 64 banks; rows are 32
+// banks wide, so rows 2i and 2i+1 sit on the two bank halves and chunk c of
+// row r goes to slot c ^ ((r >> 1) & 7): sixteen consecutive rows reading the
+// same chunk (MFMA fragments) and two rows written chunk by chunk (tile
+// stores) both hit sixteen different 4-bank groups.
+#ifndef MOELORA_TILED_SWZ
+#define MOELORA_TILED_SWZ 1
+#endif
 __device__ __forceinline__ int swz(int row, int chunk) {
+#if MOELORA_TILED_SWZ
+  return row * ROW_BYTES + ((chunk ^ ((row >> 1) & 7)) << 4);
+#else
   return row * ROW_BYTES + ((chunk ^ (row & 7)) << 4);
+#endif
+}
+
+#ifndef MOELORA_TILED_GROUP_M
+#define MOELORA_TILED_GROUP_M 0  // 0: plain order; n: groups of n row tiles per XCD range
+#endif
+
+// Workgroup -> (row tile, column tile).  Consecutive workgroup ids land on
+// different XCDs (each with its own L2), so ids are first regrouped so that
+// every XCD owns a contiguous range of the logical order; the logical order
+// then walks groups of GROUP_M row tiles column by column, so the workgroups
+// that run together on one XCD share a few A tiles and a few W tiles.
+__device__ __forceinline__ void tile_of(int ncol, int nrow, int* mt, int* nt) {
+  const int total = ncol * nrow;
+  const int id = blockIdx.x;
+  if (MOELORA_TILED_GROUP_M == 0) {  // plain order: column tiles of one row tile in a row
+    *mt = id / ncol;
+    *nt = id - *mt * ncol;
+    return;
+  }
+  const int per = total / 8;
+  const int logical = id < per * 8 ? (id % 8) * per + id / 8 : id;
+  const int GM = MOELORA_TILED_GROUP_M > 0 ? MOELORA_TILED_GROUP_M : 1;
+  const int gsz = GM * ncol;
+  const int g = logical / gsz, in = logical - g * gsz;
+  const int first = g * GM;
+  const int gm = min(GM, nrow - first);
+  *mt = first + in % gm;
+  *nt = in / gm;
 }
 
 // 8 fp32 values -> bf16 hi and lo parts, packed two per word
@@ -64,13 +109,15 @@ __device__ __forceinline__ void split8(const float* v, u32x4_t& hi, u32x4_t& lo)
   }
 }
 
-template <int MODE, bool EVEN>
+template <int MODE>
 __global__ __launch_bounds__(256, 2) void grouped_gemm_tiled_kernel(GemmParams p) {
   __shared__ __attribute__((aligned(16))) char lds[2][2][TILE_BYTES];  // [buffer][A, W]
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 1, wn = wave & 1;
   const int l32 = lane & 31, khalf = lane >> 5;
-  const int row0 = blockIdx.y * TBM;
+  int mtile, ntile_col;
+  tile_of(p.ncol, p.nrowt, &mtile, &ntile_col);
+  const int row0 = mtile * TBM;
   if (row0 >= p.hdr[HDR_NUM_PADDED]) return;
   const int e = p.bexp[row0 / p.bm];
 
@@ -79,10 +126,10 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_tiled_kernel(GemmParams p
   auto tile_col = [&](int c) -> int {
     if (MODE == 0) {
       const int w = c >> 6, ni = (c >> 5) & 1;
-      const int j = min(blockIdx.x * 64 + w * 32 + (c & 31), p.I - 1);
+      const int j = min(ntile_col * 64 + w * 32 + (c & 31), p.I - 1);
       return ni ? p.I + j : j;
     }
-    return min(blockIdx.x * TBN + c, p.N - 1);
+    return min(ntile_col * TBN + c, p.N - 1);
   };
 
   // global -> LDS assignment: 16-byte chunk c = tid + 256*i (i < 4) is tile
@@ -105,22 +152,36 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_tiled_kernel(GemmParams p
     b_src[i] = Wexp + (size_t)tile_col(r) * p.K + kc * 8;
   }
 
-  u32x4_t ra[4], rb[4];
-  auto load = [&](int kt) {
-    const int k = kt * TBK;
-    const bool ok = EVEN || k + kc * 8 < p.K;
+  // K tiles: the full 64-wide tiles (optionally in an order rotated per
+  // workgroup, which spreads HBM channels but desynchronises workgroups that
+  // share an A or W tile in L2), then the remainder tile (K % 64, a multiple
+  // of 8) masked
+  const int nfull = p.K / TBK, krem = p.K - nfull * TBK;
+  const int ntile = nfull + (krem ? 1 : 0);
+  const int rot = (MOELORA_TILED_ROTATE && nfull) ? (int)((ntile_col * 7u + mtile * 3u) % (unsigned)nfull) : 0;
+  auto tile_k0 = [&](int q) { return q < nfull ? ((q + rot) % nfull) * TBK : nfull * TBK; };
+
+  // two register stages; loads are unconditional (a remainder piece past K
+  // reads a clamped address and is replaced by zeros) so that waiting for
+  // one stage never drains the other
+  u32x4_t ra[2][4], rb[2][4];
+  auto load = [&](int q, int set) {
+    const int k = tile_k0(q) + kc * 8;
+    const bool ok = k < p.K;
+    const int koff = (ok ? k : p.K - 8) - kc * 8;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      ra[i] = ok ? ld16(a_src[i] + k) : zero4();
-      rb[i] = ok ? ld16(b_src[i] + k) : zero4();
+      u32x4_t va = ld16(a_src[i] + koff), vb = ld16(b_src[i] + koff);
+      ra[set][i] = ok ? va : zero4();
+      rb[set][i] = ok ? vb : zero4();
     }
   };
-  auto store = [&](int buf) {
+  auto store = [&](int set, int buf) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = (tid + 256 * i) >> 3;
-      *reinterpret_cast<u32x4_t*>(&lds[buf][0][swz(r, kc)]) = ra[i];
-      *reinterpret_cast<u32x4_t*>(&lds[buf][1][swz(r, kc)]) = rb[i];
+      *reinterpret_cast<u32x4_t*>(&lds[buf][0][swz(r, kc)]) = ra[set][i];
+      *reinterpret_cast<u32x4_t*>(&lds[buf][1][swz(r, kc)]) = rb[set][i];
     }
   };
 
@@ -133,32 +194,59 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_tiled_kernel(GemmParams p
       for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.f;
 
   const bool live = p.sorted[row0 + wm * 64] < p.P;  // any real row in this wavefront's 64
-  const int nkt = (p.K + TBK - 1) / TBK;
-  load(0);
-  store(0);
-  __syncthreads();
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nkt) load(kt + 1);
-    if (live) {
+  auto mma = [&](int buf) {
+    if (!live) return;
 #pragma unroll
-      for (int kk = 0; kk < TBK / 16; ++kk) {
-        const int ch = 2 * kk + khalf;
-        u32x4_t af[2], bf[2];
+    for (int kk = 0; kk < TBK / 16; ++kk) {
+      const int ch = 2 * kk + khalf;
+      u32x4_t af[2], bf[2];
 #pragma unroll
-        for (int mi = 0; mi < 2; ++mi)
-          af[mi] = *reinterpret_cast<const u32x4_t*>(&lds[cur][0][swz(wm * 64 + mi * 32 + l32, ch)]);
+      for (int mi = 0; mi < 2; ++mi)
+        af[mi] = *reinterpret_cast<const u32x4_t*>(&lds[buf][0][swz(wm * 64 + mi * 32 + l32, ch)]);
 #pragma unroll
-        for (int ni = 0; ni < 2; ++ni)
-          bf[ni] = *reinterpret_cast<const u32x4_t*>(&lds[cur][1][swz(wn * 64 + ni * 32 + l32, ch)]);
+      for (int ni = 0; ni < 2; ++ni)
+        bf[ni] = *reinterpret_cast<const u32x4_t*>(&lds[buf][1][swz(wn * 64 + ni * 32 + l32, ch)]);
 #pragma unroll
-        for (int mi = 0; mi < 2; ++mi)
+      for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-          for (int ni = 0; ni < 2; ++ni) acc[mi][ni] = mfma_32x32x16(af[mi], bf[ni], acc[mi][ni]);
-      }
+        for (int ni = 0; ni < 2; ++ni) acc[mi][ni] = mfma_32x32x16(af[mi], bf[ni], acc[mi][ni]);
     }
-    if (kt + 1 < nkt) store(cur ^ 1);
+  };
+
+  // pipeline: tile q multiplies from LDS buffer q&1 while tile q+1 waits in
+  // registers and tile q+2 is being loaded
+  load(0, 0);
+  if (ntile > 1) load(1, 1);
+  store(0, 0);
+  __syncthreads();
+  int q = 0;
+  for (; q + 3 < ntile; q += 2) {  // steady state, two tiles per trip (static register sets)
+    load(q + 2, 0);
+    mma(0);
+    store(1, 1);
     __syncthreads();
+    load(q + 3, 1);
+    mma(1);
+    store(0, 0);
+    __syncthreads();
+  }
+  // the last (at most three) tiles; q is even here
+  if (q + 2 < ntile) {
+    load(q + 2, 0);
+    mma(0);
+    store(1, 1);
+    __syncthreads();
+    mma(1);
+    store(0, 0);
+    __syncthreads();
+    mma(0);
+  } else if (q + 1 < ntile) {
+    mma(0);
+    store(1, 1);
+    __syncthreads();
+    mma(1);
+  } else {
+    mma(0);
   }
   if (!live) return;
 
@@ -214,14 +302,14 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_tiled_kernel(GemmParams p
       const int pr = p.sorted[row];
       if (pr >= p.P) continue;  // padding row
       if (MODE == 0) {
-        const int j = blockIdx.x * 64 + wn * 32 + l32;
+        const int j = ntile_col * 64 + wn * 32 + l32;
         if (j < p.I)
           p.h_out[(size_t)row * p.I + j] = f32_to_bf16(silu_f32(acc[mi][0][v]) * acc[mi][1][v]);
       } else {
         const float w = p.topk_w[pr];
 #pragma unroll
         for (int ni = 0; ni < 2; ++ni) {
-          const int n = blockIdx.x * TBN + wn * 64 + ni * 32 + l32;
+          const int n = ntile_col * TBN + wn * 64 + ni * 32 + l32;
           if (n < p.N) p.d_out[(size_t)row * p.H + n] = acc[mi][ni][v] * w;
         }
       }
@@ -230,17 +318,15 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_tiled_kernel(GemmParams p
 
 }  // namespace
 
-void launch_gemm_tiled(const GemmParams& gp, int mode, int64_t cap_rows, hipStream_t st) {
-  const int ncol = mode == 0 ? (gp.I + 63) / 64 : (gp.N + TBN - 1) / TBN;
-  dim3 grid(ncol, (unsigned)((cap_rows + TBM - 1) / TBM));
-  const bool even = gp.K % TBK == 0;
-  if (mode == 0) {
-    if (even) grouped_gemm_tiled_kernel<0, true><<<grid, 256, 0, st>>>(gp);
-    else grouped_gemm_tiled_kernel<0, false><<<grid, 256, 0, st>>>(gp);
-  } else {
-    if (even) grouped_gemm_tiled_kernel<1, true><<<grid, 256, 0, st>>>(gp);
-    else grouped_gemm_tiled_kernel<1, false><<<grid, 256, 0, st>>>(gp);
-  }
+void launch_gemm_tiled(const GemmParams& gp_in, int mode, int64_t cap_rows, hipStream_t st) {
+  GemmParams gp = gp_in;
+  gp.ncol = mode == 0 ? (gp.I + 63) / 64 : (gp.N + TBN - 1) / TBN;
+  gp.nrowt = (int)((cap_rows + TBM - 1) / TBM);
+  const unsigned grid = (unsigned)gp.ncol * (unsigned)gp.nrowt;
+  if (mode == 0)
+    grouped_gemm_tiled_kernel<0><<<grid, 256, 0, st>>>(gp);
+  else
+    grouped_gemm_tiled_kernel<1><<<grid, 256, 0, st>>>(gp);
 }
 
 }  // namespace moelora

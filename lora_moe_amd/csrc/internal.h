@@ -95,6 +95,7 @@ struct GemmParams {
   uint16_t* h_out;         // mode 0: [cap_rows][I]
   float* d_out;            // mode 1: [cap_rows][H]
   int K, N, I, H, E, L, r, topk, P, bm, nsteps;
+  int ncol, nrowt;  // tiled family: column tiles and row tiles of the launch
   float s;
 };
 
