@@ -13,6 +13,7 @@ Default workload: the pages' illustrative expert (hidden 4096, intermediate
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -55,6 +56,36 @@ def stage_bytes_flops(wl, work):
         "shrink_down": dict(bytes=b["A_down"] + P_l * I * 2 + P_l * r * 4, flops=2 * P_l * r * I),
         "combine": dict(bytes=P * H * 4 + T * H * 2, flops=P * H),
     }
+
+
+def kernel_source_sha() -> str:
+    """Hash of the sources the GEMM kernels are built from; HBM traffic taken
+    from counters is reported only while it still matches."""
+    h = hashlib.sha256()
+    for name in ("gemm.hip", "gemm_tiled.hip", "device_util.h", "internal.h"):
+        with open(os.path.join(ROOT, "lora_moe_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    (FETCH_SIZE and WRITE_SIZE runs, each scaled by what the counter reads for
+    a plain copy of known size), or None when absent or stale."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and not line.startswith(("#", " ", "`")):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    try:
+        return float(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def copy_probe(mb):
@@ -161,7 +192,7 @@ def main():
                 "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS}
     roof.update({"kernel": dom, "avg_launch_ms": per_stage[dom],
                  "alg_bytes_per_launch": sbf[dom]["bytes"], "alg_flops_per_launch": sbf[dom]["flops"],
-                 "traffic": None})
+                 "traffic": measured_traffic(dom, wl.name), "kernel_source_sha": kernel_source_sha()})
     layer_s = ms_per_step * 1e-3
     out = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
