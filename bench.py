@@ -62,7 +62,7 @@ def kernel_source_sha() -> str:
     """Hash of the sources the GEMM kernels are built from; HBM traffic taken
     from counters is reported only while it still matches."""
     h = hashlib.sha256()
-    for name in ("gemm.hip", "gemm_tiled.hip", "device_util.h", "internal.h"):
+    for name in ("gemm.hip", "gemm_tiled.hip", "gemm_prefill.hip", "device_util.h", "internal.h"):
         with open(os.path.join(ROOT, "lora_moe_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]

@@ -42,7 +42,8 @@ static int resolve_bm(const moe_lora_shape* s) {
   // (LDS-tiled family)
   if (rows <= 16) return 16;
   if (rows <= 24) return 32;
-  return 128;
+  if (rows < 192) return 128;
+  return 256;  // 256 x 256 tiles for prefill-sized batches
 }
 
 int make_layout(const moe_lora_shape* s, Layout* L) {

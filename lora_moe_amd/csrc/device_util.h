@@ -33,11 +33,33 @@ __device__ __forceinline__ f32x4_t mfma_16x16x32(u32x4_t a, u32x4_t b, f32x4_t c
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// D(32x32, fp32) += A(32x16) * B(16x32), bf16.  Lane l supplies
+// A[m = l%32][k = 8*(l/32) .. +8] and B[k = 8*(l/32) .. +8][n = l%32] and
+// receives D[8*(v/4) + 4*(l/32) + v%4][l%32] in element v = 0..15.
+__device__ __forceinline__ f32x16_t mfma_32x32x16(u32x4_t a, u32x4_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
 __device__ __forceinline__ u32x4_t ld16(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }
 
 __device__ __forceinline__ u32x4_t zero4() {
   u32x4_t z = {0u, 0u, 0u, 0u};
   return z;
+}
+
+// 8 fp32 values -> bf16 hi and lo parts, packed two per word
+__device__ __forceinline__ void split8(const float* v, u32x4_t& hi, u32x4_t& lo) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint16_t h0 = f32_to_bf16(v[2 * i]), h1 = f32_to_bf16(v[2 * i + 1]);
+    const uint16_t l0 = f32_to_bf16(v[2 * i] - bf16_to_f32(h0));
+    const uint16_t l1 = f32_to_bf16(v[2 * i + 1] - bf16_to_f32(h1));
+    hi[i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+    lo[i] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+  }
 }
 
 __device__ __forceinline__ float silu_f32(float v) { return v / (1.0f + __expf(-v)); }

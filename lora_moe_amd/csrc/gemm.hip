@@ -249,6 +249,11 @@ int launch_gemm(const Layout& L, int mode, const uint16_t* in, const int32_t* lo
   gp.bm = L.bm;
   gp.nsteps = (gp.K + 63) / 64;
   gp.s = L.s;
+  if (L.bm >= 256) {
+    const int rc = launch_gemm_prefill(gp, mode, L.cap_rows, st);
+    if (rc) return rc;
+    return hipGetLastError() == hipSuccess ? MOE_LORA_OK : MOE_LORA_EHIP;
+  }
   if (L.bm >= 128) {
     launch_gemm_tiled(gp, mode, L.cap_rows, st);
     return hipGetLastError() == hipSuccess ? MOE_LORA_OK : MOE_LORA_EHIP;

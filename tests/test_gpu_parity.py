@@ -115,7 +115,7 @@ def test_tiny_scale_and_seed():
     full_check(inp, 0, "tiny seed 3 scale 0.5", scale=0.5)
 
 
-@pytest.mark.parametrize("bm", [0, 64, 128])
+@pytest.mark.parametrize("bm", [0, 64, 128, 256])
 @pytest.mark.parametrize("H,I,r", [(104, 104, 8), (104, 1000, 24), (1000, 104, 16), (2880, 2880, 64),
                                    (256, 512, 128), (64, 40, 8)])
 def test_ragged_tails(H, I, r, bm):
