@@ -58,17 +58,30 @@ def stage_bytes_flops(wl, work):
     }
 
 
-def kernel_source_sha() -> str:
-    """Hash of the sources the GEMM kernels are built from; HBM traffic taken
-    from counters is reported only while it still matches."""
+def kernel_sources(stage: str, block_m: int) -> list:
+    """Source files the kernel of `stage` is built from at this block_m."""
+    if stage.startswith("gemm"):
+        fam = "gemm.hip" if block_m <= 64 else "gemm_tiled.hip" if block_m == 128 else "gemm_prefill.hip"
+    elif stage.startswith("shrink"):
+        fam = "shrink.hip"
+    elif stage.startswith("align"):
+        fam = "align.hip"
+    else:
+        fam = "combine.hip"
+    return [fam, "device_util.h", "internal.h"]
+
+
+def kernel_source_sha(stage: str, block_m: int) -> str:
+    """Hash of the sources of the stage's kernel; HBM traffic taken from
+    counters is reported only while it still matches."""
     h = hashlib.sha256()
-    for name in ("gemm.hip", "gemm_tiled.hip", "gemm_prefill.hip", "device_util.h", "internal.h"):
+    for name in kernel_sources(stage, block_m):
         with open(os.path.join(ROOT, "lora_moe_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel: str, workload: str):
+def measured_traffic(kernel: str, workload: str, block_m: int):
     """HBM bytes per launch of `kernel` from the committed counter summary
     (FETCH_SIZE and WRITE_SIZE runs, each scaled by what the counter reads for
     a plain copy of known size), or None when absent or stale."""
@@ -80,7 +93,7 @@ def measured_traffic(kernel: str, workload: str):
         if ":" in line and not line.startswith(("#", " ", "`")):
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
-    if vals.get("kernel_source_sha") != kernel_source_sha():
+    if vals.get("kernel_source_sha") != kernel_source_sha(kernel, block_m):
         return None
     try:
         return float(vals["traffic_bytes_per_launch"])
@@ -149,6 +162,7 @@ def main():
     dev, inp = synth.device_inputs(wl, touched_only=True)
     work = synth.algorithmic_work(wl, inp.topk_ids, inp.lora_ids)
     shape = lm.make_shape(wl.T, wl.H, wl.I, wl.E, wl.topk, wl.L, wl.r, args.block_m, wl.scale)
+    bm = lm.moe_lora_resolve_block_m(shape)
     ws = lm.alloc_workspace(shape)
     y = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda")
     stream = torch.cuda.current_stream()
@@ -164,22 +178,34 @@ def main():
     torch.cuda.synchronize()
     print(f"bench: warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
 
-    lm.moe_lora_profile_begin(args.steps)
+    # untimed pass with events around every stage: the per-stage breakdown,
+    # and which stage dominates
+    nbreak = max(1, min(args.steps, 10))
+    lm.moe_lora_profile_begin(nbreak)
+    for _ in range(nbreak):
+        step()
+    torch.cuda.synchronize()
+    stage_ms, calls = lm.moe_lora_profile_end()
+    per_stage = {k: v / max(calls, 1) for k, v in stage_ms.items()}
+    sbf = stage_bytes_flops(wl, work)
+    dom = max(sbf, key=lambda s: per_stage.get(s, 0.0))
+
+    # timed region: events only around the dominant stage's kernel (two event
+    # records per step on the launch stream)
+    lm.moe_lora_profile_begin(args.steps, [dom])
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    stage_ms, calls = lm.moe_lora_profile_end()
+    dom_ms, dom_calls = lm.moe_lora_profile_end()
     print(f"bench: timed {args.steps} steps in {elapsed:.3f} s", file=sys.stderr, flush=True)
 
     ms_per_step = elapsed * 1e3 / args.steps
     value = wl.T * args.steps / elapsed
-    per_stage = {k: v / max(calls, 1) for k, v in stage_ms.items()}
-    sbf = stage_bytes_flops(wl, work)
-    dom = max(sbf, key=lambda s: per_stage.get(s, 0.0))
-    dur_s = per_stage[dom] * 1e-3
+    dom_avg_ms = dom_ms[dom] / max(dom_calls, 1)
+    dur_s = dom_avg_ms * 1e-3
     ai = sbf[dom]["flops"] / max(sbf[dom]["bytes"], 1)
     ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
     if ai < ridge:
@@ -190,9 +216,10 @@ def main():
         achieved = sbf[dom]["flops"] / dur_s / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS}
-    roof.update({"kernel": dom, "avg_launch_ms": per_stage[dom],
+    roof.update({"kernel": dom, "avg_launch_ms": dom_avg_ms,
                  "alg_bytes_per_launch": sbf[dom]["bytes"], "alg_flops_per_launch": sbf[dom]["flops"],
-                 "traffic": measured_traffic(dom, wl.name), "kernel_source_sha": kernel_source_sha()})
+                 "traffic": measured_traffic(dom, wl.name, bm),
+                 "kernel_source_sha": kernel_source_sha(dom, bm)})
     layer_s = ms_per_step * 1e-3
     out = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -200,7 +227,7 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "I": wl.I, "E": wl.E,
                    "topk": wl.topk, "L": wl.L, "r": wl.r,
-                   "block_m": lm.moe_lora_resolve_block_m(shape), "seed": wl.seed},
+                   "block_m": bm, "seed": wl.seed},
         "roofline": roof,
         "layer": {"alg_bytes": work["bytes"], "alg_flops": work["flops"],
                   "hbm_frac": work["bytes"] / layer_s / (HBM_PEAK_GBS * 1e9),
@@ -208,6 +235,7 @@ def main():
                   "experts_touched": work["experts_touched"],
                   "adapter_expert_pairs_touched": work["pairs_touched"]},
         "stages_ms": per_stage,
+        "stages_ms_note": f"average of {calls} untimed calls with events around every stage",
     }
     if not args.no_cpu_baseline:
         print("bench: timing the CPU reference", file=sys.stderr, flush=True)

@@ -144,14 +144,17 @@ const char* moe_lora_status_str(int status);
 
 /* Stage timing with HIP events, for benchmarks.  moe_lora_profile_begin
  * creates events for up to max_calls align+forward calls and starts
- * recording around every kernel launch of later calls (on their streams);
+ * recording around the kernel launches of the stages whose bit is set in
+ * stage_mask (bit s = stage s; 0xffffffff for all) in later calls, on their
+ * streams.  Each recorded stage adds two event records to the stream, so a
+ * timed region that brackets one stage perturbs the rest the least;
  * moe_lora_profile_end waits for the recorded events, writes the summed time
  * of each stage in milliseconds to stage_ms[0..n) (n <= moe_lora_stage_count())
  * and the number of recorded calls to *calls, then stops recording.
  * Process-wide state: not for concurrent use from several host threads. */
 int moe_lora_stage_count(void);
 const char* moe_lora_stage_name(int stage);
-int moe_lora_profile_begin(int max_calls);
+int moe_lora_profile_begin(int max_calls, uint32_t stage_mask);
 int moe_lora_profile_end(float* stage_ms, int n, int* calls);
 
 #ifdef __cplusplus

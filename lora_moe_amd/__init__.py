@@ -81,7 +81,7 @@ def load_library(path: str = LIB_PATH):
     lib.moe_lora_stage_count.restype = i32
     lib.moe_lora_stage_name.argtypes = [i32]
     lib.moe_lora_stage_name.restype = ctypes.c_char_p
-    lib.moe_lora_profile_begin.argtypes = [i32]
+    lib.moe_lora_profile_begin.argtypes = [i32, ctypes.c_uint32]
     lib.moe_lora_profile_begin.restype = i32
     lib.moe_lora_profile_end.argtypes = [ctypes.POINTER(ctypes.c_float), i32,
                                          ctypes.POINTER(ctypes.c_int)]
@@ -203,8 +203,16 @@ def moe_lora_stage_name(i: int) -> str:
     return load_library().moe_lora_stage_name(int(i)).decode()
 
 
-def moe_lora_profile_begin(max_calls: int) -> None:
-    _check("moe_lora_profile_begin", load_library().moe_lora_profile_begin(int(max_calls)))
+def moe_lora_profile_begin(max_calls: int, stages=None) -> None:
+    """Record HIP events around the named stages (all when None) of the next
+    max_calls align+forward calls."""
+    mask = 0xFFFFFFFF
+    if stages is not None:
+        names = [moe_lora_stage_name(i) for i in range(moe_lora_stage_count())]
+        mask = 0
+        for s in stages:
+            mask |= 1 << names.index(s)
+    _check("moe_lora_profile_begin", load_library().moe_lora_profile_begin(int(max_calls), mask))
 
 
 def moe_lora_profile_end() -> tuple[dict, int]:

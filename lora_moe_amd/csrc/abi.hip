@@ -97,6 +97,7 @@ struct Profiler {
   bool on = false;
   int max_calls = 0;
   int call = 0;
+  uint32_t mask = 0;
   std::vector<hipEvent_t> ev;  // [call][stage][start, stop]
   std::vector<uint32_t> recorded;
 };
@@ -112,12 +113,12 @@ void prof_release() {
 }  // namespace
 
 void prof_stage_begin(int stage, hipStream_t st) {
-  if (!g_prof.on || g_prof.call >= g_prof.max_calls) return;
+  if (!g_prof.on || g_prof.call >= g_prof.max_calls || !(g_prof.mask & (1u << stage))) return;
   hipEventRecord(g_prof.ev[((size_t)g_prof.call * ST_COUNT + stage) * 2], st);
 }
 
 void prof_stage_end(int stage, hipStream_t st) {
-  if (!g_prof.on || g_prof.call >= g_prof.max_calls) return;
+  if (!g_prof.on || g_prof.call >= g_prof.max_calls || !(g_prof.mask & (1u << stage))) return;
   hipEventRecord(g_prof.ev[((size_t)g_prof.call * ST_COUNT + stage) * 2 + 1], st);
   g_prof.recorded[g_prof.call] |= 1u << stage;
 }
@@ -264,7 +265,7 @@ const char* moe_lora_stage_name(int stage) {
   return (stage >= 0 && stage < ST_COUNT) ? names[stage] : "unknown";
 }
 
-int moe_lora_profile_begin(int max_calls) {
+int moe_lora_profile_begin(int max_calls, uint32_t stage_mask) {
   if (max_calls <= 0) return MOE_LORA_EINVAL;
   prof_release();
   g_prof.ev.resize((size_t)max_calls * ST_COUNT * 2);
@@ -279,6 +280,7 @@ int moe_lora_profile_begin(int max_calls) {
   g_prof.recorded.assign(max_calls, 0u);
   g_prof.max_calls = max_calls;
   g_prof.call = 0;
+  g_prof.mask = stage_mask;
   g_prof.on = true;
   return MOE_LORA_OK;
 }

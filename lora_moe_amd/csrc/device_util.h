@@ -45,6 +45,12 @@ __device__ __forceinline__ f32x16_t mfma_32x32x16(u32x4_t a, u32x4_t b, f32x16_t
 
 __device__ __forceinline__ u32x4_t ld16(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }
 
+// 16-byte load of data read once (a weight stream): marked non-temporal so it
+// streams through the caches without displacing lines that are reused
+__device__ __forceinline__ u32x4_t ld16_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+}
+
 __device__ __forceinline__ u32x4_t zero4() {
   u32x4_t z = {0u, 0u, 0u, 0u};
   return z;

@@ -125,7 +125,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmParams p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const bool ok = !masked || piece * 8 < krem;
-      rw[i] = ok ? ld16(Wexp + (woff[i] + (uint32_t)(k0 + piece * 8))) : zero4();
+      rw[i] = ok ? ld16_stream(Wexp + (woff[i] + (uint32_t)(k0 + piece * 8))) : zero4();
     }
 #pragma unroll
     for (int s = 0; s < 4; ++s) {

@@ -7,35 +7,83 @@
 // sized for MFMA throughput rather than for a weight stream:
 //
 //   * a 256 x 256 tile halves the L2 -> LDS traffic per flop of a 128 x 128
-//     tile (64 KB per 64-deep K step for 8.4 MFLOP);
+//     tile;
 //   * 8 wavefronts in a 2 x 4 grid, each owning 128 x 64 outputs = 4 x 2 bf16
 //     MFMA 32x32x16 tiles, so each 16-byte LDS fragment read feeds two or
-//     four MFMAs; the fragments of K sub-step kk+1 are read while kk
-//     multiplies;
-//   * A (x rows gathered by token, or h rows) and W tiles go global ->
-//     registers -> LDS, double-buffered (2 x 64 KB): the loads of K step q+1
-//     are in flight while step q multiplies; 16-byte chunks of each 128-byte
-//     LDS row are XOR-swizzled (chunk ^ ((row >> 1) & 7)) so that fragment
-//     reads and tile stores are free of bank conflicts;
+//     four MFMAs; the fragments of the next 16-deep K slice are read while the
+//     current one multiplies;
+//   * A (x rows gathered by token, or h rows) and W tiles are copied global ->
+//     LDS by the load unit itself (global_load_lds_dwordx4, 16 bytes per
+//     lane), into a ring of PNS stages of PBK-deep K slices: PNS - 1 stages are
+//     in flight while one multiplies, which hides HBM latency without holding
+//     the tiles in registers.  A stage is released by a single workgroup
+//     barrier per K step, placed after the last fragment read of the stage
+//     and before the last MFMAs that use it;
+//   * 16-byte chunks of each LDS row are XOR-swizzled so that fragment reads
+//     are free of bank conflicts; since the load unit writes 16 consecutive
+//     bytes per lane, the swizzle is applied on the global side (each lane
+//     fetches the chunk that belongs at its LDS slot);
+//   * the MFMAs take the W tile as their first operand, so the accumulator
+//     holds the tile transposed: each lane ends with runs of 4 adjacent
+//     output columns of one row, written with one 8-byte (h, bf16) or
+//     16-byte (d, fp32) store;
 //   * epilogue as in the 128 x 128 family: the expand as masked MFMAs per
 //     (expert, adapter) segment with z split into bf16 hi + lo, then the SiLU
 //     gate (mode 0, gate and up columns in the same lane) or the top-k weight
-//     (mode 1).
-// A wavefront whose 128 rows are all padding skips its MFMAs and stores.
+//     (mode 1); the rows' validity and weights were staged in LDS at the
+//     start.
+// A wavefront whose 128 rows are all padding skips its MFMAs and stores but
+// still copies its share of every stage.
 #include "device_util.h"
 #include "internal.h"
+
+#ifndef MOELORA_PREFILL_BK
+#define MOELORA_PREFILL_BK 64
+#endif
+#ifndef MOELORA_PREFILL_NS
+#define MOELORA_PREFILL_NS 2
+#endif
 
 namespace moelora {
 
 namespace {
 
-constexpr int PBM = 256, PBN = 256, PBK = 64;
-constexpr int PROW = PBK * 2;          // bytes per tile row in LDS
-constexpr int PTILE = PBM * PROW;      // 32 KB (A and W tiles alike)
-constexpr int PLDS = 4 * PTILE;        // two buffers of (A, W)
+constexpr int PBM = 256, PBN = 256;
+constexpr int PBK = MOELORA_PREFILL_BK;  // K depth of one stage
+constexpr int PNS = MOELORA_PREFILL_NS;  // stages in the LDS ring
+constexpr int CPR = PBK / 8;             // 16-byte chunks per tile row
+constexpr int PROW = PBK * 2;            // bytes per tile row in LDS
+constexpr int PTILE = PBM * PROW;        // A and W tiles alike
+constexpr int PSTAGE = 2 * PTILE;
+constexpr int PRING = PNS * PSTAGE;
+constexpr int PLDS = PRING + 2 * PBM * 4;  // ring + per-row validity and top-k weight
+constexpr int NI = PBK / 16;             // 1 KB copies per wavefront per operand per stage
+constexpr int ROWS_PER_COPY = 1024 / PROW;
+static_assert(PBK == 32 || PBK == 64, "stage depth");
+static_assert(PLDS <= 160 * 1024, "LDS ring exceeds 160 KB");
+static_assert(PNS >= 2, "ring needs two stages");
 
+typedef __attribute__((address_space(3))) char lds_char;
+
+// chunk slot of logical chunk `chunk` in tile row `row`: consecutive 16-lane
+// phases of a fragment read cover 16 rows and all 64 banks
 __device__ __forceinline__ int pswz(int row, int chunk) {
-  return row * PROW + ((chunk ^ ((row >> 1) & 7)) << 4);
+  return chunk ^ ((row / (16 / CPR)) & (CPR - 1));
+}
+__device__ __forceinline__ int poff(int row, int chunk) { return row * PROW + (pswz(row, chunk) << 4); }
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
+// 6:4, lgkmcnt 11:8); the fields not named are left at their maximum
+constexpr int wait_vm(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | (7 << 4) | (15 << 8); }
+constexpr int kWaitLgkm0 = 15 | (3 << 14) | (7 << 4);
+
+// Workgroup barrier without the release/acquire fence of __syncthreads (that
+// fence waits for every outstanding vector load, the copies of later stages
+// included).  Callers wait for their own copies and LDS writes first.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 template <int MODE>
@@ -48,6 +96,16 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_prefill_kernel(GemmParams
   const int mtile = blockIdx.x / p.ncol, ntc = blockIdx.x - mtile * p.ncol;
   const int row0 = mtile * PBM;
   if (row0 >= p.hdr[HDR_NUM_PADDED]) return;
+  int* row_ok = reinterpret_cast<int*>(smem + PRING);
+  float* row_w = reinterpret_cast<float*>(smem + PRING + PBM * 4);
+  // validity and top-k weight of the tile's rows, for the epilogue
+  int my_ok = 0;
+  float my_w = 0.f;
+  if (tid < PBM) {
+    const int pr = p.sorted[row0 + tid];
+    my_ok = pr < p.P;
+    if (MODE == 1 && my_ok) my_w = p.topk_w[pr];
+  }
   const int e = p.bexp[row0 / p.bm];
 
   // Output column of tile column c (0..255).  mode 0: columns [64w, 64w+64)
@@ -61,47 +119,55 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_prefill_kernel(GemmParams
     return min(ntc * PBN + c, p.N - 1);
   };
 
-  // global -> LDS: chunk c = tid + 512*i (i < 4) is tile row c/8, K offset
-  // 8*(c%8) (the same for every i)
-  const int kc = tid & 7;
-  const uint16_t* a_src[4];
-  const uint16_t* b_src[4];
+  // Copies: wavefront w fills tile rows [32w, 32w+32) of A and of W, NI
+  // copies of ROWS_PER_COPY rows each; lane l lands at row R0 + l / CPR,
+  // slot l % CPR, which holds logical chunk `lchunk`.
+  const int lrow = lane / CPR, lslot = lane % CPR;
+  const uint16_t* a_src[NI];
+  const uint16_t* b_src[NI];
+  int lchunk[NI];
   const uint16_t* Wexp = p.W + (size_t)e * p.N * p.K;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = (tid + 512 * i) >> 3;
+  for (int i = 0; i < NI; ++i) {
+    const int r = wave * 32 + i * ROWS_PER_COPY + lrow;
+    lchunk[i] = pswz(r, lslot);  // the swizzle is an involution
     const int grow = row0 + r;
     if (MODE == 0) {
       const int pr = p.sorted[grow];
       const int t = pr < p.P ? pr / p.topk : 0;  // padding rows read token 0; output dropped
-      a_src[i] = p.in + (size_t)t * p.K + kc * 8;
+      a_src[i] = p.in + (size_t)t * p.K + lchunk[i] * 8;
     } else {
-      a_src[i] = p.in + (size_t)grow * p.K + kc * 8;
+      a_src[i] = p.in + (size_t)grow * p.K + lchunk[i] * 8;
     }
-    b_src[i] = Wexp + (size_t)tile_col(r) * p.K + kc * 8;
+    b_src[i] = Wexp + (size_t)tile_col(r) * p.K + lchunk[i] * 8;
   }
 
-  const int ntile = (p.K + PBK - 1) / PBK;  // the last one may be partial (masked)
-  u32x4_t ra[4], rb[4];
-  auto load = [&](int q) {
-    const int k = q * PBK + kc * 8;
-    const bool ok = k < p.K;
-    const int koff = (ok ? k : p.K - 8) - kc * 8;  // clamped: always a valid address
+  const int ntile = (p.K + PBK - 1) / PBK;  // the last stage may be partial
+  const bool partial = (p.K % PBK) != 0;
+  auto issue = [&](int s) {
+    char* A = smem + (s % PNS) * PSTAGE;
+    char* B = A + PTILE;
+    const int k0 = s * PBK;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const u32x4_t va = ld16(a_src[i] + koff), vb = ld16(b_src[i] + koff);
-      ra[i] = ok ? va : zero4();
-      rb[i] = ok ? vb : zero4();
+    for (int i = 0; i < NI; ++i) {
+      const int k = k0 + lchunk[i] * 8;
+      const int koff = k < p.K ? k0 : p.K - 8 - lchunk[i] * 8;  // clamped: a valid address
+      const int roff = (wave * 32 + i * ROWS_PER_COPY) * PROW;
+      __builtin_amdgcn_global_load_lds((const void*)(a_src[i] + koff), (lds_char*)(A + roff), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(b_src[i] + koff), (lds_char*)(B + roff), 16, 0, 0);
     }
   };
-  auto store = [&](int buf) {
-    char* A = smem + buf * 2 * PTILE;
+  // zero this lane's chunks of stage s that lie beyond K (after they landed)
+  auto zero_tail = [&](int s) {
+    char* A = smem + (s % PNS) * PSTAGE;
     char* B = A + PTILE;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = (tid + 512 * i) >> 3;
-      *reinterpret_cast<u32x4_t*>(A + pswz(r, kc)) = ra[i];
-      *reinterpret_cast<u32x4_t*>(B + pswz(r, kc)) = rb[i];
+    for (int i = 0; i < NI; ++i) {
+      if (s * PBK + lchunk[i] * 8 >= p.K) {
+        const int off = (wave * 32 + i * ROWS_PER_COPY + lrow) * PROW + lslot * 16;
+        *reinterpret_cast<u32x4_t*>(A + off) = zero4();
+        *reinterpret_cast<u32x4_t*>(B + off) = zero4();
+      }
     }
   };
 
@@ -114,41 +180,61 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_prefill_kernel(GemmParams
       for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.f;
 
   const bool live = p.sorted[row0 + wm * 128] < p.P;  // any real row in this wavefront's 128
-  auto mma = [&](int buf) {
-    if (!live) return;
-    const char* A = smem + buf * 2 * PTILE;
+  u32x4_t af[2][4], bf[2][2];
+  auto frag = [&](int s, int kk, int set) {
+    const char* A = smem + (s % PNS) * PSTAGE;
     const char* B = A + PTILE;
-    u32x4_t af[2][4], bf[2][2];
-    auto frag = [&](int kk, int s) {
-      const int ch = 2 * kk + khalf;
+    const int ch = 2 * kk + khalf;
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-        af[s][mi] = *reinterpret_cast<const u32x4_t*>(A + pswz(wm * 128 + mi * 32 + l32, ch));
+    for (int mi = 0; mi < 4; ++mi)
+      af[set][mi] = *reinterpret_cast<const u32x4_t*>(A + poff(wm * 128 + mi * 32 + l32, ch));
 #pragma unroll
-      for (int ni = 0; ni < 2; ++ni)
-        bf[s][ni] = *reinterpret_cast<const u32x4_t*>(B + pswz(wn * 64 + ni * 32 + l32, ch));
-    };
-    frag(0, 0);
+    for (int ni = 0; ni < 2; ++ni)
+      bf[set][ni] = *reinterpret_cast<const u32x4_t*>(B + poff(wn * 64 + ni * 32 + l32, ch));
+  };
+  auto mma = [&](int set) {
 #pragma unroll
-    for (int kk = 0; kk < PBK / 16; ++kk) {
-      if (kk + 1 < PBK / 16) frag(kk + 1, (kk + 1) & 1);
+    for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 2; ++ni)
-          acc[mi][ni] = mfma_32x32x16(af[kk & 1][mi], bf[kk & 1][ni], acc[mi][ni]);
-    }
+      for (int ni = 0; ni < 2; ++ni) acc[mi][ni] = mfma_32x32x16(bf[set][ni], af[set][mi], acc[mi][ni]);
   };
 
-  load(0);
-  store(0);
-  __syncthreads();
+  // prologue: every ring slot gets a stage; wait for stage 0
+#pragma unroll
+  for (int s = 0; s < PNS; ++s)
+    if (s < ntile) issue(s);
+  __builtin_amdgcn_s_waitcnt(wait_vm(0));
+  if (tid < PBM) {
+    row_ok[tid] = my_ok;
+    row_w[tid] = my_w;
+  }
+  if (partial && ntile == 1) zero_tail(0);
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  stage_barrier();
+  if (live) frag(0, 0, 0);
+
+  constexpr int KK = PBK / 16;  // MFMA K slices per stage (even)
   for (int q = 0; q < ntile; ++q) {
-    const bool more = q + 1 < ntile;
-    if (more) load(q + 1);
-    mma(q & 1);
-    if (more) store((q + 1) & 1);
-    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk + 1 < KK; ++kk) {
+      if (live) {
+        frag(q, kk + 1, (kk + 1) & 1);
+        mma(kk & 1);
+      }
+    }
+    if (q + 1 < ntile) {
+      // own copies of stage q + 1 have landed (later stages may still fly)
+      if (q + PNS - 1 < ntile)
+        __builtin_amdgcn_s_waitcnt(wait_vm(2 * NI * (PNS - 2)));
+      else
+        __builtin_amdgcn_s_waitcnt(wait_vm(0));
+      if (partial && q + 1 == ntile - 1) zero_tail(q + 1);
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // fragment reads of stage q and zero writes done
+      stage_barrier();
+      if (q + PNS < ntile) issue(q + PNS);  // into the slot stage q just released
+      if (live) frag(q + 1, 0, 0);
+    }
+    if (live) mma((KK - 1) & 1);
   }
   if (!live) return;
 
@@ -187,35 +273,57 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_prefill_kernel(GemmParams
         }
 #pragma unroll
         for (int ni = 0; ni < 2; ++ni) {
-          acc[mi][ni] = mfma_32x32x16(zh, bfr[ni], acc[mi][ni]);
-          acc[mi][ni] = mfma_32x32x16(zl, bfr[ni], acc[mi][ni]);
+          acc[mi][ni] = mfma_32x32x16(bfr[ni], zh, acc[mi][ni]);
+          acc[mi][ni] = mfma_32x32x16(bfr[ni], zl, acc[mi][ni]);
         }
       }
     }
   }
 
-  // epilogue: element v of acc[mi][ni] is row 8*(v/4) + 4*khalf + v%4 of the
-  // 32-row block, column l32 of the 32-column block
+  // epilogue: the products were formed as W x A^T, so element v of
+  // acc[mi][ni] is row l32 of the 32-row block and column
+  // 8*(v/4) + 4*khalf + v%4 of the 32-column block: each group of 4
+  // consecutive elements is 4 adjacent outputs of one row, stored at once
+  // (N, I and H are multiples of 8, so a group is in range when its first
+  // column is)
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
+  for (int mi = 0; mi < 4; ++mi) {
+    const int lrow = wm * 128 + mi * 32 + l32;
+    if (!row_ok[lrow]) continue;  // padding row
+    const int row = row0 + lrow;
+    if (MODE == 0) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int row = wrow0 + mi * 32 + 8 * (v >> 2) + 4 * khalf + (v & 3);
-      const int pr = p.sorted[row];
-      if (pr >= p.P) continue;  // padding row
-      if (MODE == 0) {
-        const int j = ntc * 128 + wn * 32 + l32;
-        if (j < p.I)
-          p.h_out[(size_t)row * p.I + j] = f32_to_bf16(silu_f32(acc[mi][0][v]) * acc[mi][1][v]);
-      } else {
-        const float w = p.topk_w[pr];
+      for (int g = 0; g < 4; ++g) {
+        const int j = ntc * 128 + wn * 32 + 8 * g + 4 * khalf;
+        if (j < p.I) {
+          uint32_t hv[4];
 #pragma unroll
-        for (int ni = 0; ni < 2; ++ni) {
-          const int n = ntc * PBN + wn * 64 + ni * 32 + l32;
-          if (n < p.N) p.d_out[(size_t)row * p.H + n] = acc[mi][ni][v] * w;
+          for (int i = 0; i < 4; ++i)
+            hv[i] = f32_to_bf16(silu_f32(acc[mi][0][4 * g + i]) * acc[mi][1][4 * g + i]);
+          uint2 pk;
+          pk.x = hv[0] | (hv[1] << 16);
+          pk.y = hv[2] | (hv[3] << 16);
+          *reinterpret_cast<uint2*>(p.h_out + (size_t)row * p.I + j) = pk;
         }
       }
+    } else {
+      const float w = row_w[lrow];
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int n = ntc * PBN + wn * 64 + ni * 32 + 8 * g + 4 * khalf;
+          if (n < p.N) {
+            float4 o;
+            o.x = acc[mi][ni][4 * g] * w;
+            o.y = acc[mi][ni][4 * g + 1] * w;
+            o.z = acc[mi][ni][4 * g + 2] * w;
+            o.w = acc[mi][ni][4 * g + 3] * w;
+            *reinterpret_cast<float4*>(p.d_out + (size_t)row * p.H + n) = o;
+          }
+        }
     }
+  }
 }
 
 }  // namespace

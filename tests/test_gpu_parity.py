@@ -117,7 +117,7 @@ def test_tiny_scale_and_seed():
 
 @pytest.mark.parametrize("bm", [0, 64, 128, 256])
 @pytest.mark.parametrize("H,I,r", [(104, 104, 8), (104, 1000, 24), (1000, 104, 16), (2880, 2880, 64),
-                                   (256, 512, 128), (64, 40, 8)])
+                                   (256, 512, 128), (64, 40, 8), (24, 16, 8)])
 def test_ragged_tails(H, I, r, bm):
     """K and N tails (the pages' K = 100 vs BLOCK_SIZE_K = 64 example, here
     104 = 64 + 40) and every rank family, on both GEMM families (block_m 128
