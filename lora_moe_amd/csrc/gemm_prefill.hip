@@ -27,14 +27,16 @@
 //     holds the tile transposed: each lane ends with runs of 4 adjacent
 //     output columns of one row, written with one 8-byte (h, bf16) or
 //     16-byte (d, fp32) store;
-//   * epilogue as in the 128 x 128 family: the expand as masked MFMAs per
-//     (expert, adapter) segment with z split into bf16 hi + lo, then the SiLU
+//   * epilogue as in the 128 x 128 family: the expand (lora_expand) as
+//     masked MFMAs per (expert, adapter) segment with z split into bf16
+//     hi + lo, the B rows of several segments loaded together, then the SiLU
 //     gate (mode 0, gate and up columns in the same lane) or the top-k weight
 //     (mode 1); the rows' validity and weights were staged in LDS at the
 //     start.
 // A wavefront whose 128 rows are all padding skips its MFMAs and stores but
 // still copies its share of every stage.
 #include "device_util.h"
+#include "gemm_expand.h"
 #include "internal.h"
 
 #ifndef MOELORA_PREFILL_BK
@@ -239,46 +241,10 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_prefill_kernel(GemmParams
   if (!live) return;
 
   // LoRA expand: acc += s * z[rows of segment] * B[l][e][cols]^T per segment
-  const int S = p.L + 1;
-  const int wrow0 = row0 + wm * 128;
   int ncol[2];
 #pragma unroll
   for (int ni = 0; ni < 2; ++ni) ncol[ni] = tile_col(wn * 64 + ni * 32 + l32);
-  for (int l = 0; l < p.L; ++l) {
-    const int cnt = p.segcnt[e * S + l];
-    if (cnt == 0) continue;
-    const int st = p.segstart[e * S + l];
-    const int lo = max(st, wrow0), hi = min(st + cnt, wrow0 + 128);
-    if (lo >= hi) continue;
-    const uint16_t* Bl = p.B + ((size_t)l * p.E + e) * p.N * p.r;
-    for (int q0 = 0; q0 < p.r; q0 += 16) {
-      const int qa = q0 + 8 * khalf;
-      const bool qok = qa < p.r;
-      u32x4_t bfr[2];
-#pragma unroll
-      for (int ni = 0; ni < 2; ++ni) bfr[ni] = qok ? ld16(Bl + (size_t)ncol[ni] * p.r + qa) : zero4();
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi) {
-        const int sub0 = wrow0 + mi * 32;
-        if (sub0 >= hi || sub0 + 32 <= lo) continue;  // this 32-row block misses the segment
-        const int grow = sub0 + l32;
-        u32x4_t zh = zero4(), zl = zero4();
-        if (qok && grow >= lo && grow < hi) {
-          float zv[8];
-          const float4* zp = reinterpret_cast<const float4*>(p.z + (size_t)grow * p.r + qa);
-          const float4 z0 = zp[0], z1 = zp[1];
-          zv[0] = p.s * z0.x; zv[1] = p.s * z0.y; zv[2] = p.s * z0.z; zv[3] = p.s * z0.w;
-          zv[4] = p.s * z1.x; zv[5] = p.s * z1.y; zv[6] = p.s * z1.z; zv[7] = p.s * z1.w;
-          split8(zv, zh, zl);
-        }
-#pragma unroll
-        for (int ni = 0; ni < 2; ++ni) {
-          acc[mi][ni] = mfma_32x32x16(bfr[ni], zh, acc[mi][ni]);
-          acc[mi][ni] = mfma_32x32x16(bfr[ni], zl, acc[mi][ni]);
-        }
-      }
-    }
-  }
+  lora_expand<4, 2, true, 4>(acc, p, e, row0 + wm * 128, ncol);
 
   // epilogue: the products were formed as W x A^T, so element v of
   // acc[mi][ni] is row l32 of the 32-row block and column

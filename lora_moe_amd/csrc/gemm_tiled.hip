@@ -13,22 +13,27 @@
 //   * A (gathered x rows or h rows) and W tiles go global -> registers ->
 //     LDS: tile q multiplies from one LDS buffer while tile q+1 waits in
 //     registers and tile q+2 is in flight; each 128-byte LDS row stores its
-//     eight 16-byte chunks XOR-swizzled (chunk ^ (row & 7)) so that both the
-//     row-wise stores and the column-wise fragment reads avoid bank
+//     eight 16-byte chunks XOR-swizzled (chunk ^ ((row >> 1) & 7)) so that
+//     both the row-wise stores and the column-wise fragment reads avoid bank
 //     conflicts; the K remainder is one masked tile;
+//   * the MFMAs take the W tile as their first operand, so the accumulators
+//     hold the tile transposed and each lane ends with runs of 4 adjacent
+//     output columns of one row (one 8- or 16-byte store each);
 //   * the expand runs as extra MFMAs over the rank dimension after the main
-//     loop: for each (expert, adapter) segment that meets the wavefront's rows,
-//     the A operand is z of those rows (zero elsewhere) and the B operand the
-//     adapter's B rows for the tile's columns.  z is fp32; it enters the MFMA
-//     as a bf16 pair hi + lo (hi = rne(z), lo = rne(z - hi)), which keeps ~16
+//     loop (lora_expand): for each (expert, adapter) segment that meets the
+//     wavefront's rows, z of those rows (zero elsewhere) times the adapter's B
+//     rows for the tile's columns.  z is fp32; it enters the MFMA as a bf16
+//     pair hi + lo (hi = rne(z), lo = rne(z - hi)), which keeps ~16
 //     significant bits of z;
 //   * mode 0 pairs gate column j and up column I + j in the same lane (the
 //     wavefront's 64 columns are 32 gate + 32 up), so h = silu(gate) * up is
 //     formed in registers and stored bf16; mode 1 scales by the top-k weight
-//     and stores fp32 d.
+//     and stores fp32 d.  The rows' validity and top-k weights are staged in
+//     LDS at the start.
 // A wavefront whose 64 rows are all padding skips its MFMAs and stores
 // (expert runs put real rows first, padding last).
 #include "device_util.h"
+#include "gemm_expand.h"
 #include "internal.h"
 
 namespace moelora {
@@ -90,6 +95,8 @@ __device__ __forceinline__ void tile_of(int ncol, int nrow, int* mt, int* nt) {
 template <int MODE>
 __global__ __launch_bounds__(256, 2) void grouped_gemm_tiled_kernel(GemmParams p) {
   __shared__ __attribute__((aligned(16))) char lds[2][2][TILE_BYTES];  // [buffer][A, W]
+  __shared__ int row_ok[TBM];    // the tile's rows: real (1) or padding (0)
+  __shared__ float row_w[TBM];   // and their top-k weight (mode 1)
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 1, wn = wave & 1;
   const int l32 = lane & 31, khalf = lane >> 5;
@@ -98,6 +105,13 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_tiled_kernel(GemmParams p
   const int row0 = mtile * TBM;
   if (row0 >= p.hdr[HDR_NUM_PADDED]) return;
   const int e = p.bexp[row0 / p.bm];
+  int my_ok = 0;
+  float my_w = 0.f;
+  if (tid < TBM) {
+    const int pr = p.sorted[row0 + tid];
+    my_ok = pr < p.P;
+    if (MODE == 1 && my_ok) my_w = p.topk_w[pr];
+  }
 
   // Output column of tile column c (0..127).  mode 0: columns [64*wn, 64*wn+64)
   // are gate j0+32*wn+[0,32) followed by up I+j0+32*wn+[0,32).
@@ -187,7 +201,7 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_tiled_kernel(GemmParams p
 #pragma unroll
       for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < 2; ++ni) acc[mi][ni] = mfma_32x32x16(af[mi], bf[ni], acc[mi][ni]);
+        for (int ni = 0; ni < 2; ++ni) acc[mi][ni] = mfma_32x32x16(bf[ni], af[mi], acc[mi][ni]);
     }
   };
 
@@ -196,6 +210,10 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_tiled_kernel(GemmParams p
   load(0, 0);
   if (ntile > 1) load(1, 1);
   store(0, 0);
+  if (tid < TBM) {
+    row_ok[tid] = my_ok;
+    row_w[tid] = my_w;
+  }
   __syncthreads();
   int q = 0;
   for (; q + 3 < ntile; q += 2) {  // steady state, two tiles per trip (static register sets)
@@ -229,69 +247,54 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_tiled_kernel(GemmParams p
   if (!live) return;
 
   // LoRA expand: acc += s * z[rows of segment] * B[l][e][cols]^T per segment
-  const int S = p.L + 1;
   const int wrow0 = row0 + wm * 64;
   int ncol[2];
 #pragma unroll
   for (int ni = 0; ni < 2; ++ni) ncol[ni] = tile_col(wn * 64 + ni * 32 + l32);
-  for (int l = 0; l < p.L; ++l) {
-    const int cnt = p.segcnt[e * S + l];
-    if (cnt == 0) continue;
-    const int st = p.segstart[e * S + l];
-    const int lo = max(st, wrow0), hi = min(st + cnt, wrow0 + 64);
-    if (lo >= hi) continue;
-    const uint16_t* Bl = p.B + ((size_t)l * p.E + e) * p.N * p.r;
-    for (int q0 = 0; q0 < p.r; q0 += 16) {
-      const int qa = q0 + 8 * khalf;
-      const bool qok = qa < p.r;
-      u32x4_t bfr[2];
+  lora_expand<2, 2, true>(acc, p, e, wrow0, ncol);
+
+  // epilogue: element v of acc[mi][ni] is row l32 of the 32-row block and
+  // column 8*(v/4) + 4*khalf + v%4 of the 32-column block; each group of 4
+  // elements is 4 adjacent outputs of one row, stored at once (N, I and H
+  // are multiples of 8, so a group is in range when its first column is)
 #pragma unroll
-      for (int ni = 0; ni < 2; ++ni) bfr[ni] = qok ? ld16(Bl + (size_t)ncol[ni] * p.r + qa) : zero4();
+  for (int mi = 0; mi < 2; ++mi) {
+    const int lrow = wm * 64 + mi * 32 + l32;
+    if (!row_ok[lrow]) continue;  // padding row
+    const int row = row0 + lrow;
+    if (MODE == 0) {
 #pragma unroll
-      for (int mi = 0; mi < 2; ++mi) {
-        const int sub0 = wrow0 + mi * 32;
-        if (sub0 >= hi || sub0 + 32 <= lo) continue;  // this 32-row block misses the segment
-        const int grow = sub0 + l32;
-        u32x4_t zh = zero4(), zl = zero4();
-        if (qok && grow >= lo && grow < hi) {
-          float zv[8];
-          const float4* zp = reinterpret_cast<const float4*>(p.z + (size_t)grow * p.r + qa);
-          const float4 z0 = zp[0], z1 = zp[1];
-          zv[0] = p.s * z0.x; zv[1] = p.s * z0.y; zv[2] = p.s * z0.z; zv[3] = p.s * z0.w;
-          zv[4] = p.s * z1.x; zv[5] = p.s * z1.y; zv[6] = p.s * z1.z; zv[7] = p.s * z1.w;
-          split8(zv, zh, zl);
-        }
+      for (int g = 0; g < 4; ++g) {
+        const int j = ntile_col * 64 + wn * 32 + 8 * g + 4 * khalf;
+        if (j < p.I) {
+          uint32_t hv[4];
 #pragma unroll
-        for (int ni = 0; ni < 2; ++ni) {
-          acc[mi][ni] = mfma_32x32x16(zh, bfr[ni], acc[mi][ni]);
-          acc[mi][ni] = mfma_32x32x16(zl, bfr[ni], acc[mi][ni]);
+          for (int i = 0; i < 4; ++i)
+            hv[i] = f32_to_bf16(silu_f32(acc[mi][0][4 * g + i]) * acc[mi][1][4 * g + i]);
+          uint2 pk;
+          pk.x = hv[0] | (hv[1] << 16);
+          pk.y = hv[2] | (hv[3] << 16);
+          *reinterpret_cast<uint2*>(p.h_out + (size_t)row * p.I + j) = pk;
         }
       }
+    } else {
+      const float w = row_w[lrow];
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int n = ntile_col * TBN + wn * 64 + ni * 32 + 8 * g + 4 * khalf;
+          if (n < p.N) {
+            float4 o;
+            o.x = acc[mi][ni][4 * g] * w;
+            o.y = acc[mi][ni][4 * g + 1] * w;
+            o.z = acc[mi][ni][4 * g + 2] * w;
+            o.w = acc[mi][ni][4 * g + 3] * w;
+            *reinterpret_cast<float4*>(p.d_out + (size_t)row * p.H + n) = o;
+          }
+        }
     }
   }
-
-  // epilogue: element v of acc[mi][ni] is row 8*(v/4) + 4*khalf + v%4 of the
-  // 32-row block, column l32 of the 32-column block
-#pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int row = wrow0 + mi * 32 + 8 * (v >> 2) + 4 * khalf + (v & 3);
-      const int pr = p.sorted[row];
-      if (pr >= p.P) continue;  // padding row
-      if (MODE == 0) {
-        const int j = ntile_col * 64 + wn * 32 + l32;
-        if (j < p.I)
-          p.h_out[(size_t)row * p.I + j] = f32_to_bf16(silu_f32(acc[mi][0][v]) * acc[mi][1][v]);
-      } else {
-        const float w = p.topk_w[pr];
-#pragma unroll
-        for (int ni = 0; ni < 2; ++ni) {
-          const int n = ntile_col * TBN + wn * 64 + ni * 32 + l32;
-          if (n < p.N) p.d_out[(size_t)row * p.H + n] = acc[mi][ni][v] * w;
-        }
-      }
-    }
 }
 
 }  // namespace
