@@ -37,6 +37,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the reference baseline sample")
+    ap.add_argument("--cold-iters", type=int, default=-1,
+                    help="extra per-call timings with L2 and MALL flushed before each call "
+                         "(default 20, 10 for workload 5; 0 disables)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="only run a plain device copy of this many MB (counter calibration)")
     return ap.parse_args()
@@ -111,6 +114,26 @@ def copy_probe(mb):
     torch.cuda.synchronize()
     print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4,
                       "launches": 5}), flush=True)
+
+
+def cold_timing(step, iters, flush_mb=512):
+    """Per-call times of align+forward with the caches flushed first: a
+    flush_mb-MB fill before every call evicts L2 and the 256 MB MALL; the fill
+    is outside the events.  Median and minimum in ms."""
+    import torch
+    scratch = torch.empty(flush_mb << 20, dtype=torch.uint8, device="cuda")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(iters)]
+    for a, b in ev:
+        scratch.fill_(1)
+        a.record()
+        step()
+        b.record()
+    torch.cuda.synchronize()
+    ts = sorted(a.elapsed_time(b) for a, b in ev)
+    del scratch
+    return {"iters": iters, "median_ms": ts[len(ts) // 2], "min_ms": ts[0],
+            "flush_bytes_before_each": flush_mb << 20}
 
 
 def cpu_baseline(inp, target_s):
@@ -237,6 +260,9 @@ def main():
         "stages_ms": per_stage,
         "stages_ms_note": f"average of {calls} untimed calls with events around every stage",
     }
+    cold_iters = args.cold_iters if args.cold_iters >= 0 else (10 if args.workload == 5 else 20)
+    if cold_iters > 0:
+        out["cold"] = cold_timing(step, cold_iters)
     if not args.no_cpu_baseline:
         print("bench: timing the CPU reference", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
