@@ -9,7 +9,10 @@
 // one contiguous segment, so the base GEMM tiles by expert and the LoRA ops
 // tile by (expert, adapter) segment over the same rows.
 //
-// Four short kernels, all deterministic (no atomic placement):
+// Four short kernels, all deterministic (no atomic placement).  No thread
+// reads back global data written by another thread of its workgroup, so the
+// workgroup barriers order LDS only and the global stores drain in the
+// background:
 //   1. count: per chunk of 512 pairs, an LDS histogram over the E*(L+1) keys
 //      and each pair's rank among earlier same-key pairs of its chunk;
 //   2. bucket scan: per key, exclusive prefix of the chunk counts (one
@@ -45,29 +48,89 @@ __device__ __forceinline__ int pair_key(const int32_t* __restrict__ topk_ids,
   return e * (L + 1) + (l >= 0 ? l : L);
 }
 
+// Lanes of a wavefront with the same key >= 0 form a group: *rin = number of
+// lower lanes in the group, *gsize = group size, *leader = lowest lane.  The
+// wavefront's keys go through its 64 slots of wkeys (LDS, 16-byte aligned)
+// and every lane compares against all of them: a fixed cost, independent of
+// how many distinct keys the wavefront holds.
+__device__ __forceinline__ void wave_key_groups(int key, int* wkeys, int* rin, int* gsize,
+                                                bool* leader) {
+  const int lane = threadIdx.x & 63;
+  wkeys[lane] = key;  // LDS operations of one wavefront complete in order
+  int before = 0, total = 0;
+#pragma unroll
+  for (int j = 0; j < 64; j += 4) {
+    const int4 k4 = *reinterpret_cast<const int4*>(wkeys + j);
+    const int m0 = k4.x == key, m1 = k4.y == key, m2 = k4.z == key, m3 = k4.w == key;
+    total += m0 + m1 + m2 + m3;
+    before += (m0 & (j < lane)) + (m1 & (j + 1 < lane)) + (m2 & (j + 2 < lane)) + (m3 & (j + 3 < lane));
+  }
+  *rin = before;
+  *gsize = total;
+  *leader = key >= 0 && before == 0;
+}
+
+// Stable rank of each pair among the earlier pairs of the workgroup with the
+// same key: the wavefronts take turns (in order) reading and advancing the
+// per-key running count run[key] (LDS, zero on entry), so the result is
+// deterministic; run[] ends holding the workgroup's count per key.  All
+// threads must call it; nw = wavefronts that hold pairs; wkeys = blockDim.x
+// ints of LDS scratch.
+__device__ __forceinline__ int ordered_rank(int key, int* run, int nw, int* wkeys) {
+  const int wave = threadIdx.x >> 6;
+  int rin, gsize;
+  bool leader;
+  wave_key_groups(key, wkeys + wave * 64, &rin, &gsize, &leader);
+  int rnk = 0;
+  for (int w = 0; w < nw; ++w) {
+    if (wave == w && key >= 0) {
+      const int base = run[key];  // every lane reads before the leaders write (in-order LDS)
+      rnk = base + rin;
+      if (leader) run[key] = base + gsize;
+    }
+    lds_barrier();
+  }
+  return rnk;
+}
+
+// Sentinels for the padding rows of every expert run and for the rows past
+// the last run, and the row-block -> expert map: eoff[E+1] run starts and
+// n[E] real rows per expert (LDS).  One wavefront per expert in turn, its
+// lanes over the expert's rows and blocks.
+__device__ __forceinline__ void write_pads_and_blocks(int32_t* __restrict__ sorted,
+                                                      int32_t* __restrict__ bexp, const int* eoff,
+                                                      const int* n, int E, int P, int bm,
+                                                      int64_t cap_rows, int64_t cap_blocks) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  for (int e = wave; e < E; e += nw) {
+    const int a = eoff[e], b = eoff[e + 1];
+    for (int row = a + n[e] + lane; row < b; row += 64) sorted[row] = P;
+    for (int blk = a / bm + lane; blk < b / bm; blk += 64) bexp[blk] = e;
+  }
+  const int num_padded = eoff[E];
+  for (int64_t row = num_padded + threadIdx.x; row < cap_rows; row += blockDim.x) sorted[row] = P;
+  for (int64_t blk = num_padded / bm + threadIdx.x; blk < cap_blocks; blk += blockDim.x) bexp[blk] = -1;
+}
+
 __global__ __launch_bounds__(kAlignChunk) void align_count_kernel(
     const int32_t* __restrict__ topk_ids, const int32_t* __restrict__ lora_ids, int P, int k, int E,
     int L, int NB, int C, int32_t* __restrict__ chunk_cnt, int32_t* __restrict__ chunk_err,
     int32_t* __restrict__ rank) {
-  extern __shared__ int lds[];
-  int* hist = lds;                 // [NB]
-  int* keys = lds + NB;            // [kAlignChunk]
-  int* errs = keys + kAlignChunk;  // [1]
+  extern __shared__ __attribute__((aligned(16))) int lds[];
+  int* wkeys = lds;                // [kAlignChunk]
+  int* errs = wkeys + kAlignChunk; // [1]
+  int* hist = errs + 1;            // [NB]
   const int tid = threadIdx.x, c = blockIdx.x;
   for (int b = tid; b < NB; b += blockDim.x) hist[b] = 0;
   if (tid == 0) errs[0] = 0;
   const int p = c * kAlignChunk + tid;
   int key = -1, err = 0, l;
   if (p < P) key = pair_key(topk_ids, lora_ids, p, k, E, L, &l, &err);
-  keys[tid] = key;
-  __syncthreads();
-  if (key >= 0) atomicAdd(&hist[key], 1);  // counts are order-independent
+  lds_barrier();  // hist and errs cleared
   if (err) atomicAdd(&errs[0], err);
-  // rank among earlier pairs of this chunk with the same key (stable order)
-  int rnk = 0;
-  const int wend = ((tid >> 6) + 1) << 6;  // uniform per wavefront
-  for (int j = 0; j < wend; ++j) rnk += (j < tid) & (keys[j] == key);
-  __syncthreads();
+  // rank among earlier pairs of this chunk with the same key (stable order);
+  // hist ends as the chunk's count per key
+  const int rnk = ordered_rank(key, hist, (min(P - c * kAlignChunk, kAlignChunk) + 63) >> 6, wkeys);
   for (int b = tid; b < NB; b += blockDim.x) chunk_cnt[(size_t)b * C + c] = hist[b];
   if (p < P) rank[p] = rnk;
   if (tid == 0) chunk_err[c] = errs[0];
@@ -103,9 +166,15 @@ __global__ __launch_bounds__(1024) void align_offsets_kernel(
     int32_t* __restrict__ hdr, int32_t* __restrict__ sorted, int32_t* __restrict__ eoff,
     int32_t* __restrict__ segstart, int32_t* __restrict__ bexp, LoraTile* __restrict__ tiles) {
   extern __shared__ int lds[];
-  int* scan = lds;          // [16]
-  int* s_eoff = lds + 16;   // [E+1]
-  const int tid = threadIdx.x, nt = blockDim.x, S = L + 1;
+  const int tid = threadIdx.x, nt = blockDim.x, S = L + 1, NB = E * S;
+  int* scan = lds;              // [16]
+  int* s_eoff = scan + 16;      // [E+1] run starts
+  int* s_n = s_eoff + E + 1;    // [E] real rows per expert
+  int* s_cnt = s_n + E;         // [NB] rows per (expert, slot)
+  for (int b = tid; b < NB; b += nt) s_cnt[b] = segcnt[b];
+  int errs = 0;
+  for (int c = tid; c < C; c += nt) errs += chunk_err[c];
+  lds_barrier();
 
   // padded expert sizes, scanned over experts (each thread owns a range)
   const int per = (E + nt - 1) / nt;
@@ -113,55 +182,50 @@ __global__ __launch_bounds__(1024) void align_offsets_kernel(
   int local = 0;
   for (int e = e0; e < e1; ++e) {
     int n = 0;
-    for (int s = 0; s < S; ++s) n += segcnt[e * S + s];
+    for (int sl = 0; sl < S; ++sl) n += s_cnt[e * S + sl];
+    s_n[e] = n;
     local += (n + bm - 1) / bm * bm;
   }
   int total;
-  int at = block_exclusive_scan(local, scan, &total);
+  int at = block_exclusive_scan<true>(local, scan, &total);
   for (int e = e0; e < e1; ++e) {
     s_eoff[e] = at;
     eoff[e] = at;
     int n = 0;
-    for (int s = 0; s < S; ++s) {
-      segstart[e * S + s] = at + n;
-      n += segcnt[e * S + s];
+    for (int sl = 0; sl < S; ++sl) {
+      segstart[e * S + sl] = at + n;
+      n += s_cnt[e * S + sl];
     }
-    for (int row = at + n; row < at + (n + bm - 1) / bm * bm; ++row) sorted[row] = P;  // pads
     at += (n + bm - 1) / bm * bm;
   }
   if (tid == 0) {
     s_eoff[E] = total;
     eoff[E] = total;
   }
-  __syncthreads();
+  int nerr;
+  block_exclusive_scan<true>(errs, scan, &nerr);  // also orders the s_eoff writes before the reads below
   const int num_padded = total;
-  for (int64_t row = num_padded + tid; row < cap_rows; row += nt) sorted[row] = P;
-  for (int64_t b = tid; b < cap_blocks; b += nt) {
-    const int64_t row = b * bm;
-    int e = -1;
-    if (row < num_padded) {  // the last expert whose run starts at or before row
-      int lo = 0, hi = E - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (s_eoff[mid] <= row) lo = mid; else hi = mid - 1;
-      }
-      e = lo;
-    }
-    bexp[b] = e;
-  }
+  write_pads_and_blocks(sorted, bexp, s_eoff, s_n, E, P, bm, cap_rows, cap_blocks);
 
-  // shrink tiles: segments (e, l < L) cut into pieces of <= TS rows
+  // shrink tiles: segments (e, l < L) cut into pieces of <= TS rows; a
+  // thread owns consecutive segments, so their starts follow from the run
+  // start and the counts
   const int NS = E * L;
   const int perS = (NS + nt - 1) / nt;
   const int s0 = min(NS, tid * perS), s1 = min(NS, s0 + perS);
   int lt = 0;
-  for (int i = s0; i < s1; ++i) lt += (segcnt[(i / L) * S + i % L] + TS - 1) / TS;
+  for (int i = s0; i < s1; ++i) lt += (s_cnt[(i / L) * S + i % L] + TS - 1) / TS;
   int ntiles;
-  int tb = block_exclusive_scan(lt, scan, &ntiles);
-  __syncthreads();  // segstart written above by other threads
+  int tb = block_exclusive_scan<true>(lt, scan, &ntiles);
+  int st = 0, cur_e = -1;
   for (int i = s0; i < s1; ++i) {
     const int e = i / L, l = i % L;
-    const int cnt = segcnt[e * S + l], st = segstart[e * S + l];
+    if (e != cur_e) {  // first segment of this expert in the range
+      cur_e = e;
+      st = s_eoff[e];
+      for (int l2 = 0; l2 < l; ++l2) st += s_cnt[e * S + l2];
+    }
+    const int cnt = s_cnt[e * S + l];
     for (int o = 0; o < cnt; o += TS) {
       LoraTile tl;
       tl.e = e;
@@ -170,12 +234,11 @@ __global__ __launch_bounds__(1024) void align_offsets_kernel(
       tl.n = min(TS, cnt - o);
       tiles[tb++] = tl;
     }
+    st += cnt;
   }
   if (tid == 0) {
-    int errs = 0;
-    for (int c = 0; c < C; ++c) errs += chunk_err[c];
     hdr[HDR_NUM_PADDED] = num_padded;
-    hdr[HDR_ERR] = errs;
+    hdr[HDR_ERR] = nerr;
     hdr[HDR_NTILES] = ntiles;
   }
 }
@@ -208,7 +271,7 @@ __global__ __launch_bounds__(256) void align_place_kernel(
 }
 
 constexpr int kSmallMaxPairs = 1024;
-constexpr int kSmallMaxBuckets = 6144;  // keeps the LDS use under 64 KB
+constexpr size_t kSmallMaxLds = 64 * 1024;  // the single-workgroup path keeps its tables in LDS
 
 // The whole align for P <= 1024 in one workgroup of 1024 threads (thread =
 // pair), same outputs as the four-kernel path.
@@ -219,50 +282,24 @@ __global__ __launch_bounds__(1024) void align_small_kernel(
     int32_t* __restrict__ segstart, int32_t* __restrict__ segcnt, int32_t* __restrict__ bexp,
     int32_t* __restrict__ pos, LoraTile* __restrict__ tiles, float* __restrict__ zgu,
     float* __restrict__ zd) {
-  extern __shared__ int lds[];
+  extern __shared__ __attribute__((aligned(16))) int lds[];
   const int S = L + 1, NB = E * S;
-  int* cnt = lds;                    // [NB]
+  int* wkeys = lds;                  // [kSmallMaxPairs]
+  int* cnt = wkeys + kSmallMaxPairs; // [NB]
   int* sst = cnt + NB;               // [NB] segment starts
   int* s_eoff = sst + NB;            // [E+1]
-  int* scan = s_eoff + E + 1;        // [16]
+  int* s_n = s_eoff + E + 1;         // [E] real rows per expert
+  int* scan = s_n + E;               // [16]
   int* errs = scan + 16;             // [1]
   const int tid = threadIdx.x, nt = blockDim.x;
   for (int b = tid; b < NB; b += nt) cnt[b] = 0;
   if (tid == 0) errs[0] = 0;
   int key = -1, err = 0, l = -1;
   if (tid < P) key = pair_key(topk_ids, lora_ids, tid, k, E, L, &l, &err);
-  // Stable rank = earlier pairs with the same key.  Inside a wavefront:
-  // group lanes by key with ballots (one round per distinct key); across
-  // wavefronts: the wavefronts take turns reading and advancing the per-key
-  // running count, in order, so the result is deterministic.
-  const int lane = tid & 63, wave = tid >> 6;
-  const unsigned long long below = (1ull << lane) - 1ull;
-  unsigned long long todo = __ballot(key >= 0);
-  int rin = 0, gsize = 0;
-  bool leader = false;
-  while (todo) {
-    const int src = __ffsll((long long)todo) - 1;
-    const int kk = __shfl(key, src, 64);
-    const unsigned long long grp = __ballot(key == kk) & todo;
-    if (key == kk && key >= 0) {
-      rin = __popcll(grp & below);
-      gsize = __popcll(grp);
-      leader = lane == src;
-    }
-    todo &= ~grp;
-  }
-  __syncthreads();  // cnt and errs cleared
+  lds_barrier();  // cnt and errs cleared
   if (err) atomicAdd(&errs[0], err);
-  int rnk = 0;
-  const int nw = (min(P, nt) + 63) >> 6;
-  for (int w = 0; w < nw; ++w) {
-    if (wave == w && key >= 0) {
-      const int base = cnt[key];  // every lane reads before the leaders write (in-order LDS)
-      rnk = base + rin;
-      if (leader) cnt[key] = base + gsize;
-    }
-    __syncthreads();
-  }
+  // stable rank = earlier pairs with the same key; cnt ends as the key counts
+  const int rnk = ordered_rank(key, cnt, (min(P, nt) + 63) >> 6, wkeys);
 
   // padded expert sizes, scanned over experts (each thread owns a range)
   const int per = (E + nt - 1) / nt;
@@ -271,10 +308,11 @@ __global__ __launch_bounds__(1024) void align_small_kernel(
   for (int e = e0; e < e1; ++e) {
     int n = 0;
     for (int s = 0; s < S; ++s) n += cnt[e * S + s];
+    s_n[e] = n;
     local += (n + bm - 1) / bm * bm;
   }
   int total;
-  int at = block_exclusive_scan(local, scan, &total);
+  int at = block_exclusive_scan<true>(local, scan, &total);
   for (int e = e0; e < e1; ++e) {
     s_eoff[e] = at;
     eoff[e] = at;
@@ -285,29 +323,15 @@ __global__ __launch_bounds__(1024) void align_small_kernel(
       segcnt[e * S + s] = cnt[e * S + s];
       n += cnt[e * S + s];
     }
-    for (int row = at + n; row < at + (n + bm - 1) / bm * bm; ++row) sorted[row] = P;  // pads
     at += (n + bm - 1) / bm * bm;
   }
   if (tid == 0) {
     s_eoff[E] = total;
     eoff[E] = total;
   }
-  __syncthreads();
+  lds_barrier();
   const int num_padded = total;
-  for (int64_t row = num_padded + tid; row < cap_rows; row += nt) sorted[row] = P;
-  for (int64_t b = tid; b < cap_blocks; b += nt) {
-    const int64_t row = b * bm;
-    int e = -1;
-    if (row < num_padded) {  // the last expert whose run starts at or before row
-      int lo = 0, hi = E - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (s_eoff[mid] <= row) lo = mid; else hi = mid - 1;
-      }
-      e = lo;
-    }
-    bexp[b] = e;
-  }
+  write_pads_and_blocks(sorted, bexp, s_eoff, s_n, E, P, bm, cap_rows, cap_blocks);
   if (tid < P) {
     if (key < 0) {
       pos[tid] = -1;
@@ -332,7 +356,7 @@ __global__ __launch_bounds__(1024) void align_small_kernel(
   int lt = 0;
   for (int i = s0; i < s1; ++i) lt += (cnt[(i / L) * S + i % L] + TS - 1) / TS;
   int ntiles;
-  int tb = block_exclusive_scan(lt, scan, &ntiles);
+  int tb = block_exclusive_scan<true>(lt, scan, &ntiles);
   for (int i = s0; i < s1; ++i) {
     const int e = i / L, ll = i % L;
     const int c = cnt[e * S + ll], st = sst[e * S + ll];
@@ -361,9 +385,10 @@ int launch_align(const Layout& L, const int32_t* topk_ids, const int32_t* lora_i
   if (P <= 0) return MOE_LORA_OK;  // no pairs: nothing to sort
   const int zero_gu = plan_shrink(L, L.H).splits > 1;
   const int zero_d = plan_shrink(L, L.I).splits > 1;
-  if (P <= kSmallMaxPairs && NB <= kSmallMaxBuckets) {
+  const size_t small_lds = sizeof(int) * (kSmallMaxPairs + 2 * (size_t)NB + 2 * L.E + 1 + 16 + 1);
+  if (P <= kSmallMaxPairs && small_lds <= kSmallMaxLds) {
     prof_stage_begin(ST_ALIGN_PLACE, st);
-    const size_t lds = sizeof(int) * (2 * NB + L.E + 1 + 16 + 1);
+    const size_t lds = small_lds;
     align_small_kernel<<<1, kSmallMaxPairs, lds, st>>>(
         topk_ids, lora_ids, P, L.k, L.E, L.L, L.bm, L.cap_rows, L.cap_blocks, (int)L.TS, L.r, zero_gu,
         zero_d, w.hdr, w.sorted, w.eoff, w.segstart, w.segcnt, w.bexp, w.pos, w.tiles, w.zgu, w.zd);
@@ -371,12 +396,22 @@ int launch_align(const Layout& L, const int32_t* topk_ids, const int32_t* lora_i
     return hipGetLastError() == hipSuccess ? MOE_LORA_OK : MOE_LORA_EHIP;
   }
   prof_stage_begin(ST_ALIGN_COUNT, st);
-  align_count_kernel<<<C, kAlignChunk, (NB + kAlignChunk + 1) * sizeof(int), st>>>(
+  align_count_kernel<<<C, kAlignChunk, (kAlignChunk + 1 + NB) * sizeof(int), st>>>(
       topk_ids, lora_ids, P, L.k, L.E, L.L, NB, C, w.chunk, w.chunkerr, w.rank);
   align_bucket_scan_kernel<<<(NB + 3) / 4, 256, 0, st>>>(NB, C, w.chunk, w.segcnt);
   prof_stage_end(ST_ALIGN_COUNT, st);
   prof_stage_begin(ST_ALIGN_PLACE, st);
-  align_offsets_kernel<<<1, 1024, (16 + L.E + 1) * sizeof(int), st>>>(
+  const size_t off_lds = sizeof(int) * (16 + 2 * (size_t)L.E + 1 + NB);
+  if (off_lds > 64 * 1024) {  // above the default dynamic LDS limit (at most 115 KB here)
+    static bool attr_set = false;
+    if (!attr_set) {
+      if (hipFuncSetAttribute(reinterpret_cast<const void*>(&align_offsets_kernel),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
+        return MOE_LORA_EHIP;
+      attr_set = true;
+    }
+  }
+  align_offsets_kernel<<<1, 1024, off_lds, st>>>(
       P, L.E, L.L, C, L.bm, L.cap_rows, L.cap_blocks, (int)L.TS, w.chunkerr, w.segcnt, w.hdr,
       w.sorted, w.eoff, w.segstart, w.bexp, w.tiles);
   align_place_kernel<<<(P + 255) / 256, 256, 0, st>>>(topk_ids, lora_ids, P, L.k, L.E, L.L, C, L.r,

@@ -70,9 +70,30 @@ __device__ __forceinline__ void split8(const float* v, u32x4_t& hi, u32x4_t& lo)
 
 __device__ __forceinline__ float silu_f32(float v) { return v / (1.0f + __expf(-v)); }
 
+// Workgroup barrier that orders LDS traffic only: each wavefront waits for
+// its own LDS operations, not for its outstanding global stores (for kernels
+// whose threads never read back global data written by other threads of the
+// workgroup; the stores still complete before the kernel ends).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (3 << 14));  // lgkmcnt(0); vmcnt, expcnt unrestricted
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <bool LDS_ONLY>
+__device__ __forceinline__ void wg_barrier() {
+  if (LDS_ONLY)
+    lds_barrier();
+  else
+    __syncthreads();
+}
+
 // Exclusive scan of one int per thread across a workgroup of `nthreads`
 // (multiple of 64, <= 1024).  `lds` needs 16 ints.  Returns the exclusive
 // prefix; *total receives the workgroup sum.  All threads must call it.
+// LDS_ONLY: its barriers order LDS traffic only (see lds_barrier).
+template <bool LDS_ONLY = false>
 __device__ __forceinline__ int block_exclusive_scan(int v, int* lds, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   int x = v;
@@ -82,7 +103,7 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* lds, int* total)
     if (lane >= o) x += y;
   }
   if (lane == 63) lds[wave] = x;
-  __syncthreads();
+  wg_barrier<LDS_ONLY>();
   if (wave == 0) {
     int w = lane < nw ? lds[lane] : 0;
 #pragma unroll
@@ -92,10 +113,10 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* lds, int* total)
     }
     if (lane < nw) lds[lane] = w;  // inclusive wave sums
   }
-  __syncthreads();
+  wg_barrier<LDS_ONLY>();
   int before = wave ? lds[wave - 1] : 0;
   *total = lds[nw - 1];
-  __syncthreads();
+  wg_barrier<LDS_ONLY>();
   return before + x - v;
 }
 
