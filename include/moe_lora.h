@@ -48,7 +48,9 @@ extern "C" {
 #define MOE_LORA_EINVAL (-1)       /* null pointer, negative or zero size, topk > E, bad block_m */
 #define MOE_LORA_EALIGN (-2)       /* pointer not 16-byte aligned, H or I not a multiple of 8    */
 #define MOE_LORA_EWORKSPACE (-3)   /* workspace smaller than moe_lora_workspace_bytes()          */
-#define MOE_LORA_EUNSUPPORTED (-4) /* r not a multiple of 8 or r > 128; E*(L+1) > 14336          */
+#define MOE_LORA_EUNSUPPORTED (-4) /* r not a multiple of 8 or r > 128; E*(L+1) > 14336; x or the  */
+                                   /* intermediate h ((T*topk + E*255) x I bf16) of 2 GiB or more;  */
+                                   /* one expert's gate_up weights of 2^32 elements or more         */
 #define MOE_LORA_EHIP (-5)         /* a HIP runtime call or kernel launch failed                 */
 
 /* Layer sizes.  T may be 0 (every call is then a no-op). */

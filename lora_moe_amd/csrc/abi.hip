@@ -23,10 +23,11 @@ static int check_shape(const moe_lora_shape* s) {
   const int64_t P = (int64_t)s->T * s->topk;
   const int64_t cap = P + (int64_t)s->E * 255;
   if (P > (1LL << 30) || cap > (1LL << 30)) return MOE_LORA_EUNSUPPORTED;
-  // the streaming GEMM addresses one expert's weights, x and the intermediate
-  // rows with 32-bit element offsets
-  const int64_t lim = 1LL << 32;
-  if ((int64_t)2 * s->I * s->H >= lim || (int64_t)s->T * s->H >= lim || cap * s->I >= lim)
+  // the streaming GEMM addresses one expert's weights with 32-bit element
+  // offsets; the tiled GEMMs read x and the intermediate rows through buffer
+  // resources, which take byte offsets below 2^31
+  const int64_t lim = 1LL << 32, blim = 1LL << 31;
+  if ((int64_t)2 * s->I * s->H >= lim || (int64_t)s->T * s->H * 2 >= blim || cap * s->I * 2 >= blim)
     return MOE_LORA_EUNSUPPORTED;
   return MOE_LORA_OK;
 }

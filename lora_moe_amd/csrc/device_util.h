@@ -45,6 +45,19 @@ __device__ __forceinline__ f32x16_t mfma_32x32x16(u32x4_t a, u32x4_t b, f32x16_t
 
 __device__ __forceinline__ u32x4_t ld16(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }
 
+// Buffer resource over [base, base + bytes), bytes < 2^31, for 16-byte loads
+// whose offset may point past the end: such a load returns zeros (also when
+// it copies into LDS) and touches no memory, so padding rows of a tile cost no
+// traffic.  Word 3 is the gfx9 raw-buffer setting (32-bit data format).
+typedef __amdgpu_buffer_rsrc_t buf_rsrc_t;
+constexpr uint32_t kBufNone = 0x80000000u;  // an offset past the end of every such buffer
+__device__ __forceinline__ buf_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4_t ld16_buf(buf_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+
 // 16-byte load of data read once (a weight stream): marked non-temporal so it
 // streams through the caches without displacing lines that are reused
 __device__ __forceinline__ u32x4_t ld16_stream(const void* p) {

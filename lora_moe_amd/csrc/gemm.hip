@@ -225,6 +225,7 @@ int launch_gemm(const Layout& L, int mode, const uint16_t* in, const int32_t* lo
   WsPtrs w = ws_ptrs(ws, L);
   GemmParams gp;
   gp.in = mode == 0 ? in : w.h;
+  gp.in_bytes = (uint32_t)((mode == 0 ? L.T * (int64_t)L.H : L.cap_rows * (int64_t)L.I) * 2);
   gp.W = W;
   gp.B = B;
   gp.z = mode == 0 ? w.zgu : w.zd;

@@ -124,23 +124,22 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_prefill_kernel(GemmParams
   // Copies: wavefront w fills tile rows [32w, 32w+32) of A and of W, NI
   // copies of ROWS_PER_COPY rows each; lane l lands at row R0 + l / CPR,
   // slot l % CPR, which holds logical chunk `lchunk`.
+  // A rows come through a buffer resource: padding rows get an offset past
+  // the end and copy zeros without touching memory.
   const int lrow = lane / CPR, lslot = lane % CPR;
-  const uint16_t* a_src[NI];
+  uint32_t a_off[NI];  // byte offsets into the A buffer (x or h)
   const uint16_t* b_src[NI];
   int lchunk[NI];
   const uint16_t* Wexp = p.W + (size_t)e * p.N * p.K;
+  const buf_rsrc_t a_rs = make_rsrc(p.in, p.in_bytes);
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const int r = wave * 32 + i * ROWS_PER_COPY + lrow;
     lchunk[i] = pswz(r, lslot);  // the swizzle is an involution
     const int grow = row0 + r;
-    if (MODE == 0) {
-      const int pr = p.sorted[grow];
-      const int t = pr < p.P ? pr / p.topk : 0;  // padding rows read token 0; output dropped
-      a_src[i] = p.in + (size_t)t * p.K + lchunk[i] * 8;
-    } else {
-      a_src[i] = p.in + (size_t)grow * p.K + lchunk[i] * 8;
-    }
+    const int pr = p.sorted[grow];
+    const int arow = MODE == 0 ? pr / p.topk : grow;  // x row of the token, or the h row
+    a_off[i] = pr < p.P ? (uint32_t)(arow * p.K + lchunk[i] * 8) * 2u : kBufNone;
     b_src[i] = Wexp + (size_t)tile_col(r) * p.K + lchunk[i] * 8;
   }
 
@@ -155,7 +154,7 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_prefill_kernel(GemmParams
       const int k = k0 + lchunk[i] * 8;
       const int koff = k < p.K ? k0 : p.K - 8 - lchunk[i] * 8;  // clamped: a valid address
       const int roff = (wave * 32 + i * ROWS_PER_COPY) * PROW;
-      __builtin_amdgcn_global_load_lds((const void*)(a_src[i] + koff), (lds_char*)(A + roff), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rs, (lds_char*)(A + roff), 16, (int)(a_off[i] + (uint32_t)koff * 2u), 0, 0, 0);
       __builtin_amdgcn_global_load_lds((const void*)(b_src[i] + koff), (lds_char*)(B + roff), 16, 0, 0);
     }
   };

@@ -126,21 +126,20 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_tiled_kernel(GemmParams p
 
   // global -> LDS assignment: 16-byte chunk c = tid + 256*i (i < 4) is tile
   // row c/8, K offset 8*(c%8); the same K offset for every i
+  // A rows come through a buffer resource: padding rows get an offset past
+  // the end and load zeros without touching memory.
   const int kc = tid & 7;
-  const uint16_t* a_src[4];
+  uint32_t a_off[4];  // byte offsets into the A buffer (x or h)
   const uint16_t* b_src[4];
   const uint16_t* Wexp = p.W + (size_t)e * p.N * p.K;
+  const buf_rsrc_t a_rs = make_rsrc(p.in, p.in_bytes);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = (tid + 256 * i) >> 3;
     const int grow = row0 + r;
-    if (MODE == 0) {
-      const int pr = p.sorted[grow];
-      const int t = pr < p.P ? pr / p.topk : 0;  // padding rows read token 0; output dropped
-      a_src[i] = p.in + (size_t)t * p.K + kc * 8;
-    } else {
-      a_src[i] = p.in + (size_t)grow * p.K + kc * 8;
-    }
+    const int pr = p.sorted[grow];
+    const int arow = MODE == 0 ? pr / p.topk : grow;  // x row of the token, or the h row
+    a_off[i] = pr < p.P ? (uint32_t)(arow * p.K + kc * 8) * 2u : kBufNone;
     b_src[i] = Wexp + (size_t)tile_col(r) * p.K + kc * 8;
   }
 
@@ -163,7 +162,7 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_tiled_kernel(GemmParams p
     const int koff = (ok ? k : p.K - 8) - kc * 8;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      u32x4_t va = ld16(a_src[i] + koff), vb = ld16(b_src[i] + koff);
+      u32x4_t va = ld16_buf(a_rs, a_off[i] + (uint32_t)koff * 2u), vb = ld16(b_src[i] + koff);
       ra[set][i] = ok ? va : zero4();
       rb[set][i] = ok ? vb : zero4();
     }

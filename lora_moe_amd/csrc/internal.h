@@ -82,6 +82,7 @@ inline WsPtrs ws_ptrs(void* base, const Layout& L) {
 // Arguments of the grouped GEMM kernels (both families).
 struct GemmParams {
   const uint16_t* in;      // mode 0: x [T][K]; mode 1: h [cap_rows][K]
+  uint32_t in_bytes;       // size of that buffer (< 2^31, checked by the ABI)
   const uint16_t* W;       // [E][N][K]
   const uint16_t* B;       // [L][E][N][r]
   const float* z;          // [cap_rows][r]
