@@ -39,12 +39,14 @@ static int resolve_bm(const moe_lora_shape* s) {
   const int64_t touched = std::max<int64_t>(1, std::min<int64_t>(s->E, P));
   const int64_t rows = (P + touched - 1) / touched;
   // up to ~24 rows per expert the weight stream dominates (streaming GEMM
-  // family); beyond that a 128-row tile reads each expert's weights once
-  // (LDS-tiled family)
+  // family); up to a few dozen a 128-row tile reads each expert's weights
+  // once (LDS-tiled family); beyond that the 256 x 256 tiles, which read the
+  // gathered x rows half as often per column (padding rows cost no traffic)
+  // and each expert's weights once per 256 rows
   if (rows <= 16) return 16;
   if (rows <= 24) return 32;
-  if (rows < 192) return 128;
-  return 256;  // 256 x 256 tiles for prefill-sized batches
+  if (rows < 96) return 128;
+  return 256;
 }
 
 int make_layout(const moe_lora_shape* s, Layout* L) {
@@ -64,7 +66,13 @@ int make_layout(const moe_lora_shape* s, Layout* L) {
   L->cap_blocks = (L->cap_rows + L->bm - 1) / L->bm;
   L->NB = (int64_t)L->E * (L->L + 1);
   L->C = std::max<int64_t>(1, (L->P + kAlignChunk - 1) / kAlignChunk);
-  L->TS = L->r > 64 ? 16 : std::min(64, std::max(16, L->bm));
+  // shrink tile rows: 16 when (expert, adapter) segments would hold at most
+  // 16 rows under even routing and adapters, else 64, so that each adapter
+  // slab is read once per 64 rows (16 above rank 64: LDS budget)
+  {
+    const int64_t seg = (L->P + (int64_t)L->E * L->L - 1) / ((int64_t)L->E * L->L);
+    L->TS = (L->r > 64 || seg <= 16) ? 16 : 64;
+  }
   L->max_tiles = (L->P + L->TS - 1) / L->TS + std::min<int64_t>((int64_t)L->E * L->L, L->P);
   size_t o = 0;
   auto take = [&](size_t bytes) {

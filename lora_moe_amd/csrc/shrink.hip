@@ -12,11 +12,14 @@
 //
 // One work item = (tile of <= 16*RFS rows of one (expert, adapter) segment,
 // K split).  A workgroup of 4 wavefronts walks the split's 64-wide K steps
-// interleaved by wavefront; each wavefront accumulates the whole tile
+// interleaved by wavefront, issuing the loads of 2 or 4 of its steps before
+// their MFMAs; each wavefront accumulates the whole tile
 // [16*RFS x 16*NFR] with bf16 MFMA 16x16x32.  The four partial tiles are added
 // through LDS, then one wavefront stores (single split) or atomically adds
 // (several splits) into z.  mode 0 gathers the input rows of x by token
 // (gate_up shrink); mode 1 reads the SiLU-gate output h by row (down shrink).
+#include <algorithm>
+
 #include "device_util.h"
 #include "internal.h"
 
@@ -34,7 +37,13 @@ struct ShrinkParams {
   int K, E, r, topk, splits, steps_per_split, nsteps, use_atomic;
 };
 
-template <int MODE, int RFS, int NFR, bool EVEN>
+// U = K steps of one wavefront whose loads are issued together before their
+// MFMAs (registers: U * 2 * (RFS + NFR) 16-byte fragments); the host picks
+// it from the steps each wavefront has, up to this register bound
+template <int RFS, int NFR>
+constexpr int shrink_max_unroll() { return RFS + NFR <= 3 ? 4 : RFS + NFR <= 5 ? 2 : 1; }
+
+template <int MODE, int RFS, int NFR, bool EVEN, int U>
 __global__ __launch_bounds__(256) void lora_shrink_kernel(ShrinkParams p) {
   __shared__ float red[2][RFS * 16][NFR * 16 + 1];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -69,29 +78,42 @@ __global__ __launch_bounds__(256) void lora_shrink_kernel(ShrinkParams p) {
 #pragma unroll
       for (int nf = 0; nf < NFR; ++nf) acc[rf][nf] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+    // this wavefront's steps ks0 + wave + 4j, U at a time: all loads of a
+    // group are issued before its MFMAs (addresses of steps past the split or
+    // pieces past K are clamped to valid ones and their values zeroed, so no
+    // load sits under a branch)
     const int ks0 = sp * p.steps_per_split;
     const int ks1 = min(p.nsteps, ks0 + p.steps_per_split);
-    for (int ks = ks0 + wave; ks < ks1; ks += 4) {
-      const int kb = ks * 64 + kq * 16;
-      const bool v0 = EVEN || kb < p.K, v1 = EVEN || kb + 8 < p.K;
-      u32x4_t a0[RFS], a1[RFS], b0[NFR], b1[NFR];
+    for (int ks = ks0 + wave; ks < ks1; ks += 4 * U) {
+      u32x4_t a0[U][RFS], a1[U][RFS], b0[U][NFR], b1[U][NFR];
 #pragma unroll
-      for (int rf = 0; rf < RFS; ++rf) {
-        a0[rf] = v0 ? ld16(arow[rf] + kb) : zero4();
-        a1[rf] = v1 ? ld16(arow[rf] + kb + 8) : zero4();
-      }
+      for (int u = 0; u < U; ++u) {
+        const bool sv = ks + 4 * u < ks1;
+        const int kb = (sv ? ks + 4 * u : ks) * 64 + kq * 16;
+        const bool v0 = sv && (EVEN || kb < p.K), v1 = sv && (EVEN || kb + 8 < p.K);
+        const int k0 = EVEN || kb < p.K ? kb : 0, k1 = EVEN || kb + 8 < p.K ? kb + 8 : 0;
 #pragma unroll
-      for (int nf = 0; nf < NFR; ++nf) {
-        b0[nf] = v0 ? ld16(brow[nf] + kb) : zero4();
-        b1[nf] = v1 ? ld16(brow[nf] + kb + 8) : zero4();
-      }
-#pragma unroll
-      for (int rf = 0; rf < RFS; ++rf)
+        for (int rf = 0; rf < RFS; ++rf) {
+          const u32x4_t x0 = ld16(arow[rf] + k0), x1 = ld16(arow[rf] + k1);
+          a0[u][rf] = v0 ? x0 : zero4();
+          a1[u][rf] = v1 ? x1 : zero4();
+        }
 #pragma unroll
         for (int nf = 0; nf < NFR; ++nf) {
-          acc[rf][nf] = mfma_16x16x32(a0[rf], b0[nf], acc[rf][nf]);
-          acc[rf][nf] = mfma_16x16x32(a1[rf], b1[nf], acc[rf][nf]);
+          const u32x4_t y0 = ld16(brow[nf] + k0), y1 = ld16(brow[nf] + k1);
+          b0[u][nf] = v0 ? y0 : zero4();
+          b1[u][nf] = v1 ? y1 : zero4();
         }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int rf = 0; rf < RFS; ++rf)
+#pragma unroll
+          for (int nf = 0; nf < NFR; ++nf) {
+            acc[rf][nf] = mfma_16x16x32(a0[u][rf], b0[u][nf], acc[rf][nf]);
+            acc[rf][nf] = mfma_16x16x32(a1[u][rf], b1[u][nf], acc[rf][nf]);
+          }
     }
 
     // add the four wavefronts' partial tiles: (2,3) -> (0,1) -> 0
@@ -144,12 +166,23 @@ __global__ __launch_bounds__(256) void lora_shrink_kernel(ShrinkParams p) {
   }
 }
 
+template <int MODE, int RFS, int NFR, int U>
+void launch_u(const ShrinkParams& sp, bool even, int grid, hipStream_t st) {
+  if (even)
+    lora_shrink_kernel<MODE, RFS, NFR, true, U><<<grid, 256, 0, st>>>(sp);
+  else
+    lora_shrink_kernel<MODE, RFS, NFR, false, U><<<grid, 256, 0, st>>>(sp);
+}
+
 template <int MODE, int RFS, int NFR>
 void launch_t(const ShrinkParams& sp, bool even, int grid, hipStream_t st) {
-  if (even)
-    lora_shrink_kernel<MODE, RFS, NFR, true><<<grid, 256, 0, st>>>(sp);
-  else
-    lora_shrink_kernel<MODE, RFS, NFR, false><<<grid, 256, 0, st>>>(sp);
+  // steps per wavefront in one split
+  const int spw = (sp.steps_per_split + 3) / 4;
+  const int u = std::min(shrink_max_unroll<RFS, NFR>(), spw >= 4 ? 4 : spw >= 2 ? 2 : 1);
+  constexpr int mu = shrink_max_unroll<RFS, NFR>();
+  if (u >= 4) launch_u<MODE, RFS, NFR, mu>(sp, even, grid, st);
+  else if (u == 2) launch_u<MODE, RFS, NFR, (mu >= 2 ? 2 : 1)>(sp, even, grid, st);
+  else launch_u<MODE, RFS, NFR, 1>(sp, even, grid, st);
 }
 
 template <int MODE, int RFS>
