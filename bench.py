@@ -64,7 +64,7 @@ def stage_bytes_flops(wl, work):
 def kernel_sources(stage: str, block_m: int) -> list:
     """Source files the kernel of `stage` is built from at this block_m."""
     if stage.startswith("gemm"):
-        fam = "gemm.hip" if block_m <= 64 else "gemm_tiled.hip" if block_m == 128 else "gemm_prefill.hip"
+        fam = "gemm.hip" if block_m <= 64 else "gemm_dma.hip"
     elif stage.startswith("shrink"):
         fam = "shrink.hip"
     elif stage.startswith("align"):

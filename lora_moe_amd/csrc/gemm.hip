@@ -256,7 +256,8 @@ int launch_gemm(const Layout& L, int mode, const uint16_t* in, const int32_t* lo
     return hipGetLastError() == hipSuccess ? MOE_LORA_OK : MOE_LORA_EHIP;
   }
   if (L.bm >= 128) {
-    launch_gemm_tiled(gp, mode, L.cap_rows, st);
+    const int rc = launch_gemm_dma128(gp, mode, L.cap_rows, st);
+    if (rc) return rc;
     return hipGetLastError() == hipSuccess ? MOE_LORA_OK : MOE_LORA_EHIP;
   }
   // 16- or 32-row tiles (a 64-row block is two tiles of one expert)

@@ -1,0 +1,331 @@
+// Grouped GEMM with LDS-DMA staging for batches with many rows per expert:
+// square tiles of 128 x 128 (block_m = 128) or 256 x 256 (block_m = 256).
+//
+// Same contract as the register-streaming family in gemm.hip (one GEMM per
+// expert over its sorted rows; the LoRA expand z * B added to the base output
+// in the same kernel -- vLLM blog "Multi-LoRA for MoE models", sections
+// "Implementing multi-LoRA inference for MoE models in vLLM" and "Kernel
+// optimizations"), organised for reuse of the weight tile across a tile's rows:
+//
+//   * BN/64 x 2 wavefronts, each owning (BM/2) x 64 outputs = (BM/64) x 2 bf16
+//     MFMA 32x32x16 tiles, so each 16-byte LDS fragment read feeds two or
+//     more MFMAs; the fragments of the next 16-deep K slice are read while the
+//     current one multiplies;
+//   * A (x rows gathered by token, or h rows) and W tiles are copied global ->
+//     LDS by the load unit itself (16 bytes per lane), into a ring of NS
+//     stages of BK-deep K slices: NS - 1 stages are in flight while one
+//     multiplies, without holding tiles in registers.  A stage is released by
+//     a single workgroup barrier per K step, placed after the last fragment
+//     read of the stage and before the last MFMAs that use it;
+//   * A rows come through a buffer resource: padding rows (past an expert's
+//     real pairs) get an offset past the end and copy zeros without touching
+//     memory;
+//   * 16-byte chunks of each LDS row are XOR-swizzled so that fragment reads
+//     are free of bank conflicts; since the load unit writes 16 consecutive
+//     bytes per lane, the swizzle is applied on the global side (each lane
+//     fetches the chunk that belongs at its LDS slot);
+//   * the MFMAs take the W tile as their first operand, so the accumulator
+//     holds the tile transposed: each lane ends with runs of 4 adjacent output
+//     columns of one row, written with one 8-byte (h, bf16) or 16-byte (d,
+//     fp32) store;
+//   * epilogue: the expand (lora_expand) as masked MFMAs per (expert, adapter)
+//     segment with z split into bf16 hi + lo, then the SiLU gate (mode 0, gate
+//     and up columns in the same lane) or the top-k weight (mode 1); the rows'
+//     validity and weights are staged in LDS at the start.
+// A wavefront whose rows are all padding skips its MFMAs and stores but still
+// copies its share of every stage.
+#include "device_util.h"
+#include "gemm_expand.h"
+#include "internal.h"
+
+namespace moelora {
+
+namespace {
+
+typedef __attribute__((address_space(3))) char lds_char;
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
+// 6:4, lgkmcnt 11:8); the fields not named are left at their maximum
+constexpr int wait_vm(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | (7 << 4) | (15 << 8); }
+constexpr int kWaitLgkm0 = 15 | (3 << 14) | (7 << 4);
+
+// Workgroup barrier without the release/acquire fence of __syncthreads (that
+// fence waits for every outstanding vector load, the copies of later stages
+// included).  Callers wait for their own copies and LDS writes first.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int BM_, int BK_, int NS_>
+struct DmaCfg {
+  static constexpr int BM = BM_, BN = BM_;    // square tiles
+  static constexpr int BK = BK_;              // K depth of one stage
+  static constexpr int NS = NS_;              // stages in the LDS ring
+  static constexpr int WN = BN / 64, NW = 2 * WN, NT = 64 * NW;  // wavefronts: 2 x WN
+  static constexpr int MI = BM / 64, NI = 2;  // 32x32 blocks per wavefront
+  static constexpr int CPR = BK / 8;          // 16-byte chunks per tile row
+  static constexpr int PROW = BK * 2;         // bytes per tile row in LDS
+  static constexpr int TILE = BM * PROW;      // A and W tiles alike
+  static constexpr int STAGE = 2 * TILE;
+  static constexpr int RING = NS * STAGE;
+  static constexpr int LDS = RING + 2 * BM * 4;  // ring + per-row validity and top-k weight
+  static constexpr int WROWS = BM / NW;           // tile rows each wavefront copies (32)
+  static constexpr int ROWS_PER_COPY = 1024 / PROW;
+  static constexpr int NC = WROWS / ROWS_PER_COPY;  // 1 KB copies per wavefront per operand per stage
+  static_assert(BK == 32 || BK == 64, "stage depth");
+  static_assert(WROWS == 32, "copy layout");
+  static_assert(LDS <= 160 * 1024, "LDS ring exceeds 160 KB");
+  static_assert(NS >= 2, "ring needs two stages");
+
+  // chunk slot of logical chunk `chunk` in tile row `row`: consecutive 16-lane
+  // phases of a fragment read cover 16 rows and all 64 banks
+  static __device__ __forceinline__ int swz(int row, int chunk) {
+    return chunk ^ ((row / (16 / CPR)) & (CPR - 1));
+  }
+  static __device__ __forceinline__ int off(int row, int chunk) { return row * PROW + (swz(row, chunk) << 4); }
+};
+
+template <int MODE, class C, int WAVES_PER_SIMD>
+__global__ __launch_bounds__(C::NT, WAVES_PER_SIMD) void grouped_gemm_dma_kernel(GemmParams p) {
+  constexpr int BM = C::BM, BN = C::BN, BK = C::BK, NS = C::NS, MI = C::MI, NI = C::NI, NC = C::NC;
+  constexpr int WROWS = C::WROWS, RPC = C::ROWS_PER_COPY, CPR = C::CPR, PROW = C::PROW;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / C::WN, wn = wave % C::WN;
+  const int l32 = lane & 31, khalf = lane >> 5;
+  const int mtile = blockIdx.x / p.ncol, ntc = blockIdx.x - mtile * p.ncol;
+  const int row0 = mtile * BM;
+  if (row0 >= p.hdr[HDR_NUM_PADDED]) return;
+  int* row_ok = reinterpret_cast<int*>(smem + C::RING);
+  float* row_w = reinterpret_cast<float*>(smem + C::RING + BM * 4);
+  // validity and top-k weight of the tile's rows, for the epilogue
+  int my_ok = 0;
+  float my_w = 0.f;
+  if (tid < BM) {
+    const int pr = p.sorted[row0 + tid];
+    my_ok = pr < p.P;
+    if (MODE == 1 && my_ok) my_w = p.topk_w[pr];
+  }
+  const int e = p.bexp[row0 / p.bm];
+
+  // Output column of tile column c (0..BN-1).  mode 0: columns [64w, 64w+64)
+  // are gate j0+32w+[0,32) followed by up I+j0+32w+[0,32), j0 = (BN/2)*ntc.
+  auto tile_col = [&](int c) -> int {
+    if (MODE == 0) {
+      const int w = c >> 6, ni = (c >> 5) & 1;
+      const int j = min(ntc * (BN / 2) + w * 32 + (c & 31), p.I - 1);
+      return ni ? p.I + j : j;
+    }
+    return min(ntc * BN + c, p.N - 1);
+  };
+
+  // Copies: wavefront w fills tile rows [32w, 32w+32) of A and of W, NC
+  // copies of RPC rows each; lane l lands at row R0 + l / CPR, slot l % CPR,
+  // which holds logical chunk lchunk.
+  const int lrow = lane / CPR, lslot = lane % CPR;
+  uint32_t a_off[NC];  // byte offsets into the A buffer (x or h)
+  const uint16_t* b_src[NC];
+  int lchunk[NC];
+  const uint16_t* Wexp = p.W + (size_t)e * p.N * p.K;
+  const buf_rsrc_t a_rs = make_rsrc(p.in, p.in_bytes);
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const int r = wave * WROWS + i * RPC + lrow;
+    lchunk[i] = C::swz(r, lslot);  // the swizzle is an involution
+    const int grow = row0 + r;
+    const int pr = p.sorted[grow];
+    const int arow = MODE == 0 ? pr / p.topk : grow;  // x row of the token, or the h row
+    a_off[i] = pr < p.P ? (uint32_t)(arow * p.K + lchunk[i] * 8) * 2u : kBufNone;
+    b_src[i] = Wexp + (size_t)tile_col(r) * p.K + lchunk[i] * 8;
+  }
+
+  const int ntile = (p.K + BK - 1) / BK;  // the last stage may be partial
+  const bool partial = (p.K % BK) != 0;
+  auto issue = [&](int s) {
+    char* A = smem + (s % NS) * C::STAGE;
+    char* B = A + C::TILE;
+    const int k0 = s * BK;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const int k = k0 + lchunk[i] * 8;
+      const int koff = k < p.K ? k0 : p.K - 8 - lchunk[i] * 8;  // clamped: a valid address
+      const int roff = (wave * WROWS + i * RPC) * PROW;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rs, (lds_char*)(A + roff), 16, (int)(a_off[i] + (uint32_t)koff * 2u), 0, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(b_src[i] + koff), (lds_char*)(B + roff), 16, 0, 0);
+    }
+  };
+  // zero this lane's chunks of stage s that lie beyond K (after they landed)
+  auto zero_tail = [&](int s) {
+    char* A = smem + (s % NS) * C::STAGE;
+    char* B = A + C::TILE;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      if (s * BK + lchunk[i] * 8 >= p.K) {
+        const int o = (wave * WROWS + i * RPC + lrow) * PROW + lslot * 16;
+        *reinterpret_cast<u32x4_t*>(A + o) = zero4();
+        *reinterpret_cast<u32x4_t*>(B + o) = zero4();
+      }
+    }
+  };
+
+  f32x16_t acc[MI][NI];
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.f;
+
+  const int wrow = wm * (BM / 2);                    // first tile row of this wavefront
+  const bool live = p.sorted[row0 + wrow] < p.P;     // any real row in this wavefront's rows
+  u32x4_t af[2][MI], bf[2][NI];
+  auto frag = [&](int s, int kk, int set) {
+    const char* A = smem + (s % NS) * C::STAGE;
+    const char* B = A + C::TILE;
+    const int ch = 2 * kk + khalf;
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+      af[set][mi] = *reinterpret_cast<const u32x4_t*>(A + C::off(wrow + mi * 32 + l32, ch));
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni)
+      bf[set][ni] = *reinterpret_cast<const u32x4_t*>(B + C::off(wn * 64 + ni * 32 + l32, ch));
+  };
+  auto mma = [&](int set) {
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = mfma_32x32x16(bf[set][ni], af[set][mi], acc[mi][ni]);
+  };
+
+  // prologue: every ring slot gets a stage; wait for stage 0
+#pragma unroll
+  for (int s = 0; s < NS; ++s)
+    if (s < ntile) issue(s);
+  __builtin_amdgcn_s_waitcnt(wait_vm(0));
+  if (tid < BM) {
+    row_ok[tid] = my_ok;
+    row_w[tid] = my_w;
+  }
+  if (partial && ntile == 1) zero_tail(0);
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  stage_barrier();
+  if (live) frag(0, 0, 0);
+
+  constexpr int KK = BK / 16;  // MFMA K slices per stage (even)
+  constexpr int VM_AHEAD = 2 * NC * (NS - 2) < 63 ? 2 * NC * (NS - 2) : 63;
+  for (int q = 0; q < ntile; ++q) {
+#pragma unroll
+    for (int kk = 0; kk + 1 < KK; ++kk) {
+      if (live) {
+        frag(q, kk + 1, (kk + 1) & 1);
+        mma(kk & 1);
+      }
+    }
+    if (q + 1 < ntile) {
+      // own copies of stage q + 1 have landed (later stages may still fly)
+      if (q + NS - 1 < ntile)
+        __builtin_amdgcn_s_waitcnt(wait_vm(VM_AHEAD));
+      else
+        __builtin_amdgcn_s_waitcnt(wait_vm(0));
+      if (partial && q + 1 == ntile - 1) zero_tail(q + 1);
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // fragment reads of stage q and zero writes done
+      stage_barrier();
+      if (q + NS < ntile) issue(q + NS);  // into the slot stage q just released
+      if (live) frag(q + 1, 0, 0);
+    }
+    if (live) mma((KK - 1) & 1);
+  }
+  if (!live) return;
+
+  // LoRA expand: acc += s * z[rows of segment] * B[l][e][cols]^T per segment
+  int ncol[NI];
+#pragma unroll
+  for (int ni = 0; ni < NI; ++ni) ncol[ni] = tile_col(wn * 64 + ni * 32 + l32);
+  lora_expand<MI, NI, true, 4>(acc, p, e, row0 + wrow, ncol);
+
+  // epilogue: the products were formed as W x A^T, so element v of
+  // acc[mi][ni] is row l32 of the 32-row block and column
+  // 8*(v/4) + 4*khalf + v%4 of the 32-column block: each group of 4
+  // consecutive elements is 4 adjacent outputs of one row, stored at once
+  // (N, I and H are multiples of 8, so a group is in range when its first
+  // column is)
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi) {
+    const int lr = wrow + mi * 32 + l32;
+    if (!row_ok[lr]) continue;  // padding row
+    const int row = row0 + lr;
+    if (MODE == 0) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int j = ntc * (BN / 2) + wn * 32 + 8 * g + 4 * khalf;
+        if (j < p.I) {
+          uint32_t hv[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            hv[i] = f32_to_bf16(silu_f32(acc[mi][0][4 * g + i]) * acc[mi][1][4 * g + i]);
+          uint2 pk;
+          pk.x = hv[0] | (hv[1] << 16);
+          pk.y = hv[2] | (hv[3] << 16);
+          *reinterpret_cast<uint2*>(p.h_out + (size_t)row * p.I + j) = pk;
+        }
+      }
+    } else {
+      const float w = row_w[lr];
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int n = ntc * BN + wn * 64 + ni * 32 + 8 * g + 4 * khalf;
+          if (n < p.N) {
+            float4 o;
+            o.x = acc[mi][ni][4 * g] * w;
+            o.y = acc[mi][ni][4 * g + 1] * w;
+            o.z = acc[mi][ni][4 * g + 2] * w;
+            o.w = acc[mi][ni][4 * g + 3] * w;
+            *reinterpret_cast<float4*>(p.d_out + (size_t)row * p.H + n) = o;
+          }
+        }
+    }
+  }
+}
+
+template <class C, int WAVES_PER_SIMD>
+int launch_dma(const GemmParams& gp_in, int mode, int64_t cap_rows, hipStream_t st) {
+  static bool attr_set[2] = {false, false};
+  GemmParams gp = gp_in;
+  gp.ncol = mode == 0 ? (gp.I + C::BN / 2 - 1) / (C::BN / 2) : (gp.N + C::BN - 1) / C::BN;
+  gp.nrowt = (int)((cap_rows + C::BM - 1) / C::BM);
+  const unsigned grid = (unsigned)gp.ncol * (unsigned)gp.nrowt;
+  const void* fn = mode == 0 ? reinterpret_cast<const void*>(&grouped_gemm_dma_kernel<0, C, WAVES_PER_SIMD>)
+                             : reinterpret_cast<const void*>(&grouped_gemm_dma_kernel<1, C, WAVES_PER_SIMD>);
+  if (C::LDS > 64 * 1024 && !attr_set[mode]) {  // more than the default 64 KB of dynamic LDS
+    if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS) != hipSuccess)
+      return MOE_LORA_EHIP;
+    attr_set[mode] = true;
+  }
+  if (mode == 0)
+    grouped_gemm_dma_kernel<0, C, WAVES_PER_SIMD><<<grid, C::NT, C::LDS, st>>>(gp);
+  else
+    grouped_gemm_dma_kernel<1, C, WAVES_PER_SIMD><<<grid, C::NT, C::LDS, st>>>(gp);
+  return MOE_LORA_OK;
+}
+
+}  // namespace
+
+// 256 x 256 tiles, 8 wavefronts, two 64-deep stages (128 KB of LDS)
+int launch_gemm_prefill(const GemmParams& gp, int mode, int64_t cap_rows, hipStream_t st) {
+  return launch_dma<DmaCfg<256, 64, 2>, 2>(gp, mode, cap_rows, st);
+}
+
+// 128 x 128 tiles, 4 wavefronts, two 64-deep stages (64 KB of LDS, two
+// workgroups per CU).  Measured against 32-deep stages in a 3-stage ring with
+// three workgroups per CU and a 4-stage ring with two: the 64-deep stages win
+// (16-byte chunks of 128-byte row pieces instead of 64-byte ones).
+int launch_gemm_dma128(const GemmParams& gp, int mode, int64_t cap_rows, hipStream_t st) {
+  return launch_dma<DmaCfg<128, 64, 2>, 2>(gp, mode, cap_rows, st);
+}
+
+}  // namespace moelora

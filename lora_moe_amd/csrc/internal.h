@@ -138,10 +138,10 @@ int launch_gemm(const Layout& L, int mode, const uint16_t* x, const int32_t* lor
                 const float* topk_weights, const uint16_t* W, const uint16_t* B, void* ws,
                 hipStream_t st);
 
-// The LDS-tiled family, used when block_m == 128 (defined in gemm_tiled.hip).
-void launch_gemm_tiled(const GemmParams& gp, int mode, int64_t cap_rows, hipStream_t st);
-// The 256 x 256 prefill family, used when block_m == 256 (gemm_prefill.hip).
+// The LDS-DMA family (gemm_dma.hip): 256 x 256 tiles when block_m == 256,
+// 128 x 128 tiles when block_m == 128.
 int launch_gemm_prefill(const GemmParams& gp, int mode, int64_t cap_rows, hipStream_t st);
+int launch_gemm_dma128(const GemmParams& gp, int mode, int64_t cap_rows, hipStream_t st);
 
 int launch_combine(const Layout& L, void* ws, uint16_t* y, hipStream_t st);
 
