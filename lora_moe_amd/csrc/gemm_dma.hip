@@ -20,6 +20,8 @@
 //   * A rows come through a buffer resource: padding rows (past an expert's
 //     real pairs) get an offset past the end and copy zeros without touching
 //     memory;
+//   * a row tile that is its expert's only one reads the weight tile
+//     non-temporally (it is not reused by another row tile);
 //   * 16-byte chunks of each LDS row are XOR-swizzled so that fragment reads
 //     are free of bank conflicts; since the load unit writes 16 consecutive
 //     bytes per lane, the swizzle is applied on the global side (each lane
@@ -110,6 +112,10 @@ __global__ __launch_bounds__(C::NT, WAVES_PER_SIMD) void grouped_gemm_dma_kernel
     if (MODE == 1 && my_ok) my_w = p.topk_w[pr];
   }
   const int e = p.bexp[row0 / p.bm];
+  // the expert's weights are read by this row tile only (no neighbouring
+  // tile of the same expert): stream them non-temporally
+  const int blk = row0 / p.bm;
+  const bool w_once = !(blk > 0 && p.bexp[blk - 1] == e) && !(blk + 1 < p.nrowt && p.bexp[blk + 1] == e);
 
   // Output column of tile column c (0..BN-1).  mode 0: columns [64w, 64w+64)
   // are gate j0+32w+[0,32) followed by up I+j0+32w+[0,32), j0 = (BN/2)*ntc.
@@ -154,7 +160,10 @@ __global__ __launch_bounds__(C::NT, WAVES_PER_SIMD) void grouped_gemm_dma_kernel
       const int koff = k < p.K ? k0 : p.K - 8 - lchunk[i] * 8;  // clamped: a valid address
       const int roff = (wave * WROWS + i * RPC) * PROW;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rs, (lds_char*)(A + roff), 16, (int)(a_off[i] + (uint32_t)koff * 2u), 0, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(b_src[i] + koff), (lds_char*)(B + roff), 16, 0, 0);
+      if (w_once)  // cache policy operand 2: non-temporal
+        __builtin_amdgcn_global_load_lds((const void*)(b_src[i] + koff), (lds_char*)(B + roff), 16, 0, 2);
+      else
+        __builtin_amdgcn_global_load_lds((const void*)(b_src[i] + koff), (lds_char*)(B + roff), 16, 0, 0);
     }
   };
   // zero this lane's chunks of stage s that lie beyond K (after they landed)
