@@ -23,6 +23,8 @@
 //   4. place: row of pair p = segment start + chunk prefix + rank.
 // Small batches (at most 1024 pairs, decode) run all of it in one
 // single-workgroup kernel instead, with the counts and offsets in LDS.
+#include <algorithm>
+
 #include "device_util.h"
 #include "internal.h"
 
@@ -273,7 +275,7 @@ __global__ __launch_bounds__(256) void align_place_kernel(
 constexpr int kSmallMaxPairs = 1024;
 constexpr size_t kSmallMaxLds = 64 * 1024;  // the single-workgroup path keeps its tables in LDS
 
-// The whole align for P <= 1024 in one workgroup of 1024 threads (thread =
+// The whole align for P <= 1024 in one workgroup of ceil(P/64) wavefronts (thread =
 // pair), same outputs as the four-kernel path.
 __global__ __launch_bounds__(1024) void align_small_kernel(
     const int32_t* __restrict__ topk_ids, const int32_t* __restrict__ lora_ids, int P, int k, int E,
@@ -389,7 +391,9 @@ int launch_align(const Layout& L, const int32_t* topk_ids, const int32_t* lora_i
   if (P <= kSmallMaxPairs && small_lds <= kSmallMaxLds) {
     prof_stage_begin(ST_ALIGN_PLACE, st);
     const size_t lds = small_lds;
-    align_small_kernel<<<1, kSmallMaxPairs, lds, st>>>(
+    // one thread per pair (whole wavefronts): fewer wavefronts, cheaper barriers
+    const int nthreads = std::min(kSmallMaxPairs, (P + 63) / 64 * 64);
+    align_small_kernel<<<1, nthreads, lds, st>>>(
         topk_ids, lora_ids, P, L.k, L.E, L.L, L.bm, L.cap_rows, L.cap_blocks, (int)L.TS, L.r, zero_gu,
         zero_d, w.hdr, w.sorted, w.eoff, w.segstart, w.segcnt, w.bexp, w.pos, w.tiles, w.zgu, w.zd);
     prof_stage_end(ST_ALIGN_PLACE, st);
