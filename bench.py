@@ -32,7 +32,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", type=int, default=2, help="synthetic workload number 1..5")
+    ap.add_argument("--workload", type=int, default=2, help="synthetic workload number 1..6")
     ap.add_argument("--block-m", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,

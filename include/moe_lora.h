@@ -80,10 +80,13 @@ typedef struct moe_lora_views {
   float* z_gu;           /* [cap_rows][r] gate_up shrink result per row (adapter rows only)  */
   float* z_down;         /* [cap_rows][r] down shrink result per row (adapter rows only)     */
   uint16_t* h;           /* [cap_rows][I] bf16 SiLU-gate output per row                      */
-  float* d;              /* [cap_rows][H] down output per row, already times w[t][j]         */
+  float* d;              /* [d_splits][cap_rows][H] down output per row, already times       */
+                         /* w[t][j]; with several K splits the row's output is the sum of  */
+                         /* its slabs (the combine adds them in slab order)                */
   int64_t cap_rows;      /* T*topk + E*(block_m-1)                                           */
   int64_t cap_blocks;    /* ceil(cap_rows / block_m)                                         */
   int32_t block_m;       /* block size in effect (resolved when the shape says 0)           */
+  int32_t d_splits;      /* K splits of the down GEMM (1 unless few experts, wide weights)  */
 } moe_lora_views;
 
 /* block_m used for this shape (the shape's own value when non-zero), or a

@@ -44,7 +44,8 @@ class moe_lora_views(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "sorted_ids", "expert_off", "seg_start", "seg_cnt", "block_expert", "pos_of_pair",
         "num_padded", "err_count", "z_gu", "z_down", "h", "d")] + [
-        ("cap_rows", ctypes.c_int64), ("cap_blocks", ctypes.c_int64), ("block_m", ctypes.c_int32)]
+        ("cap_rows", ctypes.c_int64), ("cap_blocks", ctypes.c_int64), ("block_m", ctypes.c_int32),
+        ("d_splits", ctypes.c_int32)]
 
 
 def make_shape(T, H, I, E, topk, L, r, block_m=0, lora_scale=1.0) -> moe_lora_shape:
@@ -184,8 +185,8 @@ def workspace_tensors(shape, workspace) -> dict:
         z_gu=region(v.z_gu, cap * shape.r, torch.float32).view(cap, shape.r),
         z_down=region(v.z_down, cap * shape.r, torch.float32).view(cap, shape.r),
         h=region(v.h, cap * shape.I, torch.bfloat16).view(cap, shape.I),
-        d=region(v.d, cap * shape.H, torch.float32).view(cap, shape.H),
-        cap_rows=cap, cap_blocks=capb, block_m=v.block_m)
+        d=region(v.d, v.d_splits * cap * shape.H, torch.float32).view(v.d_splits, cap, shape.H),
+        cap_rows=cap, cap_blocks=capb, block_m=v.block_m, d_splits=v.d_splits)
 
 
 def moe_lora_device_errors(shape, workspace, stream=None) -> int:

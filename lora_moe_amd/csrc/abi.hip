@@ -45,6 +45,10 @@ static int resolve_bm(const moe_lora_shape* s) {
   // and each expert's weights once per 256 rows
   if (rows <= 16) return 16;
   if (rows <= 24) return 32;
+  // few experts with wide weights (dense layers): the tiled grids would be
+  // too small to fill the GPU (the down projection has one 128-column tile
+  // per expert and 128 output columns), so stream instead
+  if (touched * ((s->H + 127) / 128) < 512) return 32;
   if (rows < 96) return 128;
   return 256;
 }
@@ -74,6 +78,15 @@ int make_layout(const moe_lora_shape* s, Layout* L) {
     L->TS = (L->r > 64 || seg <= 16) ? 16 : 64;
   }
   L->max_tiles = (L->P + L->TS - 1) / L->TS + std::min<int64_t>((int64_t)L->E * L->L, L->P);
+  // The streaming down GEMM splits K when its (row tile x 64-column) grid is
+  // small (few experts with wide weights, e.g. dense layers): each split
+  // writes its own partial slab of d and the combine adds the slabs in order.
+  L->dsplit = 1;
+  if (L->bm <= 64) {
+    const int64_t tiles = ((L->H + 63) / 64) * ((L->cap_rows + 15) / 16);
+    const int64_t chunks = std::max<int64_t>(1, L->I / 128);
+    L->dsplit = (int)std::min<int64_t>(std::min<int64_t>(8, chunks), std::max<int64_t>(1, (1024 + tiles - 1) / tiles));
+  }
   size_t o = 0;
   auto take = [&](size_t bytes) {
     size_t at = o;
@@ -94,7 +107,7 @@ int make_layout(const moe_lora_shape* s, Layout* L) {
   L->off_zgu = take(sizeof(float) * L->cap_rows * L->r);
   L->off_zd = take(sizeof(float) * L->cap_rows * L->r);
   L->off_h = take(sizeof(uint16_t) * L->cap_rows * L->I);
-  L->off_d = take(sizeof(float) * L->cap_rows * L->H);
+  L->off_d = take(sizeof(float) * L->dsplit * L->cap_rows * L->H);
   L->total = o;
   return MOE_LORA_OK;
 }
@@ -173,6 +186,7 @@ int moe_lora_workspace_view(const moe_lora_shape* shape, void* workspace, moe_lo
   out->z_down = w.zd;
   out->h = w.h;
   out->d = w.d;
+  out->d_splits = L.dsplit;
   out->cap_rows = L.cap_rows;
   out->cap_blocks = L.cap_blocks;
   out->block_m = L.bm;

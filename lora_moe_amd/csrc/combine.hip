@@ -13,7 +13,8 @@ namespace {
 
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ d,
                                                       const int32_t* __restrict__ pos, int T,
-                                                      int H, int k, uint16_t* __restrict__ y) {
+                                                      int H, int k, int nslab, int64_t slab,
+                                                      uint16_t* __restrict__ y) {
   const int per_row = H / 8;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (int64_t)T * per_row) return;
@@ -22,10 +23,15 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   for (int j = 0; j < k; ++j) {
     const int row = pos[(size_t)t * k + j];
     if (row < 0) continue;  // dropped pair (invalid expert id)
-    const float4* src = reinterpret_cast<const float4*>(d + (size_t)row * H + c);
-    const float4 v0 = src[0], v1 = src[1];
-    acc[0] += v0.x; acc[1] += v0.y; acc[2] += v0.z; acc[3] += v0.w;
-    acc[4] += v1.x; acc[5] += v1.y; acc[6] += v1.z; acc[7] += v1.w;
+    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};  // the pair's output: its K-split slabs in order
+    for (int sl = 0; sl < nslab; ++sl) {
+      const float4* src = reinterpret_cast<const float4*>(d + sl * slab + (size_t)row * H + c);
+      const float4 v0 = src[0], v1 = src[1];
+      v[0] += v0.x; v[1] += v0.y; v[2] += v0.z; v[3] += v0.w;
+      v[4] += v1.x; v[5] += v1.y; v[6] += v1.z; v[7] += v1.w;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] += v[i];
   }
   u32x4_t out;
 #pragma unroll
@@ -40,7 +46,7 @@ int launch_combine(const Layout& L, void* ws, uint16_t* y, hipStream_t st) {
   WsPtrs w = ws_ptrs(ws, L);
   const int64_t n = (int64_t)L.T * (L.H / 8);
   const int grid = (int)((n + 255) / 256);
-  combine_kernel<<<grid, 256, 0, st>>>(w.d, w.pos, L.T, L.H, L.k, y);
+  combine_kernel<<<grid, 256, 0, st>>>(w.d, w.pos, L.T, L.H, L.k, L.dsplit, L.cap_rows * (int64_t)L.H, y);
   return hipGetLastError() == hipSuccess ? MOE_LORA_OK : MOE_LORA_EHIP;
 }
 

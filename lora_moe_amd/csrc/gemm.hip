@@ -116,8 +116,16 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmParams p) {
   }
 
   // full 128-wide chunks run unmasked in rotated order; a K remainder (a
-  // multiple of 8 below 128) is one masked chunk at the end
-  const int nfull = p.K / KC, krem = p.K - nfull * KC;
+  // multiple of 8 below 128) is one masked chunk at the end.  With K splits
+  // (mode 1, blockIdx.z) this workgroup takes chunks [kc0, kc0 + nfull) and
+  // the last split also the remainder.
+  const int split = MODE == 1 ? (int)blockIdx.z : 0;
+  const int all_full = p.K / KC;
+  const int cps = (all_full + p.ksplit - 1) / p.ksplit;
+  const int kc0 = MODE == 1 ? min(all_full, split * cps) : 0;
+  const int nfull = MODE == 1 ? min(all_full, kc0 + cps) - kc0 : all_full;
+  const int krem = (MODE == 0 || split == p.ksplit - 1) ? p.K - all_full * KC : 0;
+  const int kbase = kc0 * KC;  // first K element of this split
   const int rot = (MOELORA_STREAM_ROTATE && nfull) ? (int)((blockIdx.x * 4u + wave) * 7u % (unsigned)nfull) : 0;
 
   u32x4_t rw[4], rx[RF][4];
@@ -125,7 +133,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmParams p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const bool ok = !masked || piece * 8 < krem;
-      rw[i] = ok ? ld16_stream(Wexp + (woff[i] + (uint32_t)(k0 + piece * 8))) : zero4();
+      rw[i] = ok ? ld16_stream(Wexp + (woff[i] + (uint32_t)(kbase + k0 + piece * 8))) : zero4();
     }
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -133,7 +141,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmParams p) {
       const bool ok = !masked || kk < krem;
 #pragma unroll
       for (int rf = 0; rf < RF; ++rf)
-        rx[rf][s] = ok ? ld16(p.in + (aoff[rf] + (uint32_t)(k0 + kk))) : zero4();
+        rx[rf][s] = ok ? ld16(p.in + (aoff[rf] + (uint32_t)(kbase + k0 + kk))) : zero4();
     }
   };
   uint16_t* slice = wl[wave];
@@ -195,7 +203,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmParams p) {
         if (!(l >= 0 && l < p.L)) l = -1;
       }
       float v = acc[rf][i];
-      if (l >= 0)
+      if (l >= 0 && split == 0)  // the expand joins the first K split only
         v += p.s * expand_dot(p.z + (size_t)row * p.r,
                               p.B + (((size_t)l * p.E + e) * p.N + wr) * p.r, p.r);
       if (MODE == 0) {
@@ -205,7 +213,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmParams p) {
           p.h_out[(size_t)row * p.I + j] = f32_to_bf16(real ? silu_f32(v) * up : 0.f);
       } else {
         const int n = blockIdx.x * 64 + wave * 16 + m;
-        if (real && n < p.N) p.d_out[(size_t)row * p.H + n] = v * p.topk_w[pr];
+        if (real && n < p.N) p.d_out[split * p.d_slab + (size_t)row * p.H + n] = v * p.topk_w[pr];
       }
     }
 }
@@ -213,7 +221,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmParams p) {
 template <int MODE, int RF>
 void launch_rf(const GemmParams& gp, int64_t cap_rows, hipStream_t st) {
   const int ncol = MODE == 0 ? (gp.I + 31) / 32 : (gp.H + 63) / 64;
-  dim3 grid(ncol, (unsigned)((cap_rows + RF * 16 - 1) / (RF * 16)));
+  dim3 grid(ncol, (unsigned)((cap_rows + RF * 16 - 1) / (RF * 16)), MODE == 1 ? gp.ksplit : 1);
   grouped_gemm_kernel<MODE, RF><<<grid, 256, 0, st>>>(gp);
 }
 
@@ -249,6 +257,8 @@ int launch_gemm(const Layout& L, int mode, const uint16_t* in, const int32_t* lo
   gp.P = (int)L.P;
   gp.bm = L.bm;
   gp.nsteps = (gp.K + 63) / 64;
+  gp.ksplit = mode == 1 ? L.dsplit : 1;
+  gp.d_slab = L.cap_rows * (int64_t)L.H;
   gp.s = L.s;
   if (L.bm >= 256) {
     const int rc = launch_gemm_prefill(gp, mode, L.cap_rows, st);

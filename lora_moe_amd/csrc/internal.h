@@ -26,6 +26,7 @@ struct Layout {
   int T, H, I, E, k, L, r, bm;
   float s;
   int64_t P, cap_rows, cap_blocks, NB, C, TS, max_tiles;
+  int dsplit;  // K splits of the down GEMM (d holds one partial slab per split)
   size_t off_hdr, off_sorted, off_eoff, off_segstart, off_segcnt, off_bexp, off_pos;
   size_t off_chunk, off_chunkerr, off_rank, off_tiles, off_zgu, off_zd, off_h, off_d, total;
 };
@@ -97,6 +98,8 @@ struct GemmParams {
   float* d_out;            // mode 1: [cap_rows][H]
   int K, N, I, H, E, L, r, topk, P, bm, nsteps;
   int ncol, nrowt;  // tiled family: column tiles and row tiles of the launch
+  int ksplit;       // streaming family, mode 1: K splits (d_out slab per split)
+  int64_t d_slab;   // elements between the d_out slabs of consecutive splits
   float s;
 };
 

@@ -114,7 +114,7 @@ class Workload:
         return self.T * self.topk
 
 
-# The five layer workloads.  Shapes, adapter-id distributions and routing skew
+# The layer workloads.  Shapes, adapter-id distributions and routing skew
 # follow the synthetic layer shapes this library is measured on; the
 # "illustrative" one is the 4096/11008/r=32 expert of the pages' Figure 1.
 WORKLOADS = {
@@ -124,6 +124,9 @@ WORKLOADS = {
     4: Workload("qwen3moe-like", T=2048, H=2048, I=768, E=128, topk=8, L=32, r=16,
                 lora_mode="none_fraction", none_fraction=0.2),
     5: Workload("deepseek-like", T=8192, H=7168, I=2048, E=256, topk=8, L=8, r=64, bias_std=2.0),
+    # dense multi-LoRA decode (one expert, every token routed to it with
+    # weight 1): a Qwen3-32B-sized MLP with 8 adapters of rank 16
+    6: Workload("dense-qwen3-32b-like", T=32, H=5120, I=25600, E=1, topk=1, L=8, r=16),
 }
 
 

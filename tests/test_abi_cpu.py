@@ -44,7 +44,7 @@ def shape_of(wl, bm=0):
     return lm.make_shape(wl.T, wl.H, wl.I, wl.E, wl.topk, wl.L, wl.r, bm, wl.scale)
 
 
-@pytest.mark.parametrize("n", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 6])
 def test_workspace_and_block_m(lib, n):
     wl = synth.WORKLOADS[n]
     s = shape_of(wl)
