@@ -42,6 +42,8 @@ def _bind(lib):
     lib.orc_pair.argtypes = [i, i, i, i, i, i, i, d] + [vp] * 9 + [i, i] + [vp] * 5
     lib.orc_align.restype = i
     lib.orc_align.argtypes = [i, i, i, i, i, vp, vp, i, i] + [vp] * 8
+    lib.orc_route.restype = i
+    lib.orc_route.argtypes = [i, i, i, vp, vp, vp]
     return lib
 
 
@@ -154,6 +156,20 @@ class Oracle:
         out["num_padded"] = int(out["num_padded"][0])
         out["err_count"] = int(out["err_count"][0])
         return out
+
+
+    def route(self, logits, k):
+        """Reference router: (ids [T][k] int32, weights [T][k] float64)."""
+        lg, lg_p = _c(logits, np.float32)
+        T, E = lg.shape
+        ids = np.zeros((T, k), np.int32)
+        w = np.zeros((T, k), np.float64)
+        if T == 0:
+            return ids, w
+        rc = self.lib.orc_route(T, E, k, lg_p, ids.ctypes.data, w.ctypes.data)
+        if rc != 0:
+            raise ValueError("k outside [1, E]")
+        return ids, w
 
 
 def layer_from_inputs(inp, tokens=None, oracle: Oracle | None = None, nthreads=None, scale=None):

@@ -265,3 +265,39 @@ int orc_align(int T, int k, int E, int L, int block_m, const int32_t* topk_ids,
   free(cur);
   return 0;
 }
+
+/* Router: each token goes to the k experts with the largest logits, and the
+ * layer sums their outputs with weights (vLLM blog, section on implementing
+ * multi-LoRA for MoE: the router picks top-k experts per token and the
+ * outputs are aggregated).  The pages fix neither the order of equal logits
+ * nor the weight formula; the plain reading used here:
+ *   - experts in descending logit order, equal logits by ascending index
+ *     (slot j holds the j-th choice);
+ *   - weights = softmax over the k chosen logits, which equals the full
+ *     softmax's top-k probabilities renormalised to sum to one.
+ * logits [T][E] float (finite), ids [T][k] int32, w [T][k] double.
+ * Returns 0, or -1 for k outside [1, E]. */
+int orc_route(int T, int E, int k, const float* logits, int32_t* ids, double* w) {
+  if (k < 1 || k > E) return -1;
+  unsigned char* taken = (unsigned char*)malloc((size_t)E);
+  if (!taken) return -1;
+  for (int t = 0; t < T; ++t) {
+    const float* lg = logits + (size_t)t * E;
+    memset(taken, 0, (size_t)E);
+    for (int j = 0; j < k; ++j) {
+      int best = -1;
+      for (int e = 0; e < E; ++e) {
+        if (taken[e]) continue;
+        if (best < 0 || (double)lg[e] > (double)lg[best]) best = e;  /* strict: ties keep the lower index */
+      }
+      taken[best] = 1;
+      ids[(size_t)t * k + j] = best;
+    }
+    const double m = (double)lg[ids[(size_t)t * k]];  /* the largest chosen logit */
+    double sum = 0.0;
+    for (int j = 0; j < k; ++j) sum += exp((double)lg[ids[(size_t)t * k + j]] - m);
+    for (int j = 0; j < k; ++j) w[(size_t)t * k + j] = exp((double)lg[ids[(size_t)t * k + j]] - m) / sum;
+  }
+  free(taken);
+  return 0;
+}

@@ -12,7 +12,9 @@ What pins what:
     y = xW + xAB), and the same per (token, expert) pair in the general case;
   * invariances: token permutation, top-k slot order, adapter relabelling,
     expert relabelling, x = 0, B = 0, A = 0, no-adapter id, weight linearity;
-  * the align against a comparison sort of the keys and hand-worked examples.
+  * the align against a comparison sort of the keys and hand-worked examples;
+  * the router against a sort on (-logit, expert), scipy's softmax, hand-worked
+    examples in ``golden/router_examples.json`` and its invariances.
 """
 from __future__ import annotations
 
@@ -374,4 +376,80 @@ def pin_align_invariants(orc):
 
 
 ALIGN_PINS = [pin_align_examples, pin_align_comparison_sort, pin_align_invariants]
-ALL_PINS = LAYER_PINS + ALIGN_PINS
+
+
+# ------------------------------------------------------------------ router
+
+def route_by_sorting(logits, k):
+    """Top-k by sorting (expert, logit) pairs on (-logit, expert) -- an
+    independent statement of "largest first, ties to the lower index" -- and
+    the weights from scipy's softmax over the chosen logits."""
+    from scipy.special import softmax
+    T, E = logits.shape
+    ids = np.zeros((T, k), np.int32)
+    w = np.zeros((T, k))
+    for t in range(T):
+        order = sorted(range(E), key=lambda e: (-float(logits[t, e]), e))[:k]
+        ids[t] = order
+        w[t] = softmax(logits[t, order].astype(np.float64))
+    return ids, w
+
+
+def router_cases():
+    rng = np.random.default_rng(7)
+    cases = []
+    for T, E, k in [(5, 8, 2), (4, 16, 4), (3, 6, 6), (6, 32, 8), (2, 5, 1)]:
+        lg = rng.standard_normal((T, E)).astype(np.float32)
+        cases.append((f"normal T={T} E={E} k={k}", lg, k))
+    # ties: logits on a coarse grid
+    lg = rng.integers(-2, 3, size=(8, 10)).astype(np.float32)
+    cases.append(("grid ties", lg, 3))
+    return cases
+
+
+def pin_router_examples(orc):
+    data = json.load(open(os.path.join(GOLDEN, "router_examples.json")))
+    for ex in data["examples"]:
+        ids, w = orc.route(np.array(ex["logits"], np.float32), ex["k"])
+        assert ids.tolist() == ex["ids"], f"{ex['name']}: ids {ids.tolist()}"
+        close(w, np.array(ex["weights"]), rtol=ex.get("weights_rtol", 1e-14), what=ex["name"])
+
+
+def pin_router_sorting(orc):
+    for name, lg, k in router_cases():
+        ids, w = orc.route(lg, k)
+        ids2, w2 = route_by_sorting(lg, k)
+        assert np.array_equal(ids, ids2), f"{name}: ids differ from the sorted order"
+        close(w, w2, rtol=1e-13, what=name)
+
+
+def pin_router_invariants(orc):
+    rng = np.random.default_rng(11)
+    lg = rng.standard_normal((6, 12)).astype(np.float32)
+    k = 4
+    ids, w = orc.route(lg, k)
+    # weights sum to one; full softmax renormalised over the chosen experts
+    assert np.allclose(w.sum(axis=1), 1.0, rtol=0, atol=1e-14)
+    full = np.exp(lg.astype(np.float64) - lg.max(axis=1, keepdims=True))
+    full /= full.sum(axis=1, keepdims=True)
+    sel = np.take_along_axis(full, ids.astype(np.int64), axis=1)
+    close(w, sel / sel.sum(axis=1, keepdims=True), rtol=1e-13, what="renormalised softmax")
+    # weights are non-increasing along the slots
+    assert np.all(np.diff(w, axis=1) <= 1e-15)
+    # a shift of a token's logits by a power of two changes nothing
+    ids_s, w_s = orc.route(lg + np.float32(4.0), k)
+    assert np.array_equal(ids, ids_s)
+    close(w, w_s, rtol=1e-6, what="shift")
+    # relabelling experts relabels the choice (distinct logits here)
+    perm = rng.permutation(12)
+    ids_p, w_p = orc.route(lg[:, perm], k)
+    assert np.array_equal(perm[ids_p], ids), "expert relabelling"
+    close(w, w_p, rtol=1e-14, what="relabel")
+    # k = E: every expert once, weights = the full softmax in that order
+    ids_a, w_a = orc.route(lg, 12)
+    assert all(sorted(r) == list(range(12)) for r in ids_a.tolist())
+    close(w_a, np.take_along_axis(full, ids_a.astype(np.int64), axis=1), rtol=1e-13, what="k=E")
+
+
+ROUTER_PINS = [pin_router_examples, pin_router_sorting, pin_router_invariants]
+ALL_PINS = LAYER_PINS + ALIGN_PINS + ROUTER_PINS

@@ -49,6 +49,15 @@ MUTANTS = [
      "for (int i = 0; i < cap_rows; ++i) sorted_ids[i] = -1;"),
     ("align_no_lora_errors", "if (!(l >= -1 && l < L)) errs++;", "if (0) errs++;"),
     ("align_block_expert_unset", "block_expert[b] = -1;\n", "block_expert[b] = 0;\n"),
+    # router
+    ("router_ties_to_higher", "if (best < 0 || (double)lg[e] > (double)lg[best]) best = e;",
+     "if (best < 0 || (double)lg[e] >= (double)lg[best]) best = e;"),
+    ("router_smallest_first", "if (best < 0 || (double)lg[e] > (double)lg[best]) best = e;",
+     "if (best < 0 || (double)lg[e] < (double)lg[best]) best = e;"),
+    ("router_full_softmax", "for (int j = 0; j < k; ++j) sum += exp((double)lg[ids[(size_t)t * k + j]] - m);",
+     "for (int j = 0; j < E; ++j) sum += exp((double)lg[j] - m);"),
+    ("router_unnormalised", "w[(size_t)t * k + j] = exp((double)lg[ids[(size_t)t * k + j]] - m) / sum;",
+     "w[(size_t)t * k + j] = exp((double)lg[ids[(size_t)t * k + j]] - m);"),
 ]
 
 
