@@ -118,6 +118,32 @@ size_t moe_lora_workspace_bytes(const moe_lora_shape* shape);
 int moe_lora_align(const moe_lora_shape* shape, const int32_t* topk_ids, const int32_t* lora_ids,
                    void* workspace, size_t ws_bytes, void* stream);
 
+/* Router: each token's top-k experts and their weights from fp32 logits.
+ * The router sends each token to its top-k experts and the layer aggregates
+ * their outputs (vLLM blog, section "Implementing multi-LoRA inference for MoE
+ * models in vLLM"); the pages fix neither tie order nor weight formula.  This
+ * library: experts by descending logit, equal logits by ascending expert index
+ * (slot j = j-th choice, bit-exact); weights = softmax over the k chosen
+ * logits (fp32), i.e. the full softmax's top-k probabilities renormalised.
+ *
+ *   logits        device [T][E] fp32 (finite; a non-finite logit is never
+ *                 chosen, and a slot left without an eligible expert gets -1)
+ *   topk_ids      device [T][topk] int32, written
+ *   topk_weights  device [T][topk] fp32, written
+ * shape->topk must be at most 64 (MOE_LORA_EUNSUPPORTED otherwise).  Async on
+ * stream; the outputs feed moe_lora_align / moe_lora_forward. */
+int moe_lora_route(const moe_lora_shape* shape, const float* logits, int32_t* topk_ids,
+                   float* topk_weights, void* stream);
+
+/* moe_lora_route followed by moe_lora_align on the routed ids, fused into a
+ * single kernel when T*topk <= 1024 (the decode case) and the align's tables
+ * fit in LDS; otherwise the router kernel runs first.  Arguments as in the two
+ * calls; topk_ids and topk_weights are written and the workspace receives the
+ * align outputs. */
+int moe_lora_route_align(const moe_lora_shape* shape, const float* logits, const int32_t* lora_ids,
+                         int32_t* topk_ids, float* topk_weights, void* workspace, size_t ws_bytes,
+                         void* stream);
+
 /* Typed device pointers into `workspace` for this shape (host only, no GPU
  * work).  For tests and tools that inspect the align or intermediates. */
 int moe_lora_workspace_view(const moe_lora_shape* shape, void* workspace, moe_lora_views* out);

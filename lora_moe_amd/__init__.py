@@ -70,6 +70,10 @@ def load_library(path: str = LIB_PATH):
     lib.moe_lora_workspace_bytes.restype = ctypes.c_size_t
     lib.moe_lora_align.argtypes = [sp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.moe_lora_align.restype = i32
+    lib.moe_lora_route.argtypes = [sp, vp, vp, vp, vp]
+    lib.moe_lora_route.restype = i32
+    lib.moe_lora_route_align.argtypes = [sp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.moe_lora_route_align.restype = i32
     lib.moe_lora_workspace_view.argtypes = [sp, vp, ctypes.POINTER(moe_lora_views)]
     lib.moe_lora_workspace_view.restype = i32
     lib.moe_lora_forward.argtypes = [sp] + [vp] * 11 + [ctypes.c_size_t, vp, vp]
@@ -132,6 +136,25 @@ def alloc_workspace(shape: moe_lora_shape, device="cuda"):
     if n == 0:
         raise MoeLoraError("moe_lora_workspace_bytes", MOE_LORA_EINVAL)
     return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def moe_lora_route(shape, logits, topk_ids, topk_weights, stream=None) -> None:
+    """Top-k experts and weights of each token from fp32 logits [T, E] into
+    topk_ids [T, k] (int32) and topk_weights [T, k] (fp32)."""
+    _check("moe_lora_route", load_library().moe_lora_route(
+        ctypes.byref(shape), _ptr(logits, "logits"), _ptr(topk_ids, "topk_ids"),
+        _ptr(topk_weights, "topk_weights"), _stream(stream)))
+
+
+def moe_lora_route_align(shape, logits, lora_ids, topk_ids, topk_weights, workspace,
+                         stream=None) -> None:
+    """moe_lora_route then moe_lora_align on the routed ids (one kernel for
+    small batches)."""
+    _check("moe_lora_route_align", load_library().moe_lora_route_align(
+        ctypes.byref(shape), _ptr(logits, "logits"), _ptr(lora_ids, "lora_ids"),
+        _ptr(topk_ids, "topk_ids"), _ptr(topk_weights, "topk_weights"),
+        _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
 
 
 def moe_lora_align(shape, topk_ids, lora_ids, workspace, stream=None) -> None:

@@ -205,6 +205,35 @@ int moe_lora_align(const moe_lora_shape* shape, const int32_t* topk_ids, const i
   return launch_align(L, topk_ids, lora_ids, workspace, (hipStream_t)stream);
 }
 
+int moe_lora_route(const moe_lora_shape* shape, const float* logits, int32_t* topk_ids,
+                   float* topk_weights, void* stream) {
+  Layout L;
+  int rc = make_layout(shape, &L);
+  if (rc) return rc;
+  if (L.T == 0) return MOE_LORA_OK;
+  if (!logits || !topk_ids || !topk_weights) return MOE_LORA_EINVAL;
+  if (L.k > 64) return MOE_LORA_EUNSUPPORTED;
+  prof_stage_begin(ST_ROUTE, (hipStream_t)stream);
+  rc = launch_router(L, logits, topk_ids, topk_weights, (hipStream_t)stream);
+  prof_stage_end(ST_ROUTE, (hipStream_t)stream);
+  return rc;
+}
+
+int moe_lora_route_align(const moe_lora_shape* shape, const float* logits, const int32_t* lora_ids,
+                         int32_t* topk_ids, float* topk_weights, void* workspace, size_t ws_bytes,
+                         void* stream) {
+  Layout L;
+  int rc = make_layout(shape, &L);
+  if (rc) return rc;
+  if (L.T == 0) return MOE_LORA_OK;
+  if (!logits || !lora_ids || !topk_ids || !topk_weights) return MOE_LORA_EINVAL;
+  if (L.k > 64) return MOE_LORA_EUNSUPPORTED;
+  if (!workspace || ws_bytes < L.total) return MOE_LORA_EWORKSPACE;
+  if (!aligned16(workspace)) return MOE_LORA_EALIGN;
+  return launch_align(L, topk_ids, lora_ids, workspace, (hipStream_t)stream, logits, topk_ids,
+                      topk_weights);
+}
+
 int moe_lora_forward(const moe_lora_shape* shape, const uint16_t* x, const int32_t* topk_ids,
                      const float* topk_weights, const int32_t* lora_ids, const uint16_t* W_gu,
                      const uint16_t* W_down, const uint16_t* A_gu, const uint16_t* B_gu,
@@ -284,7 +313,8 @@ int moe_lora_stage_count(void) { return ST_COUNT; }
 
 const char* moe_lora_stage_name(int stage) {
   static const char* names[ST_COUNT] = {"align_count", "align_place", "shrink_gate_up",
-                                        "gemm_gate_up", "shrink_down", "gemm_down", "combine"};
+                                        "gemm_gate_up", "shrink_down", "gemm_down", "combine",
+                                        "route"};
   return (stage >= 0 && stage < ST_COUNT) ? names[stage] : "unknown";
 }
 

@@ -27,6 +27,7 @@
 
 #include "device_util.h"
 #include "internal.h"
+#include "router_device.h"
 
 namespace moelora {
 
@@ -283,11 +284,13 @@ __global__ __launch_bounds__(1024) void align_small_kernel(
     int32_t* __restrict__ hdr, int32_t* __restrict__ sorted, int32_t* __restrict__ eoff,
     int32_t* __restrict__ segstart, int32_t* __restrict__ segcnt, int32_t* __restrict__ bexp,
     int32_t* __restrict__ pos, LoraTile* __restrict__ tiles, float* __restrict__ zgu,
-    float* __restrict__ zd) {
+    float* __restrict__ zd, const float* __restrict__ logits, int32_t* __restrict__ ids_out,
+    float* __restrict__ w_out) {
   extern __shared__ __attribute__((aligned(16))) int lds[];
   const int S = L + 1, NB = E * S;
   int* wkeys = lds;                  // [kSmallMaxPairs]
-  int* cnt = wkeys + kSmallMaxPairs; // [NB]
+  int* rids = wkeys + kSmallMaxPairs; // [kSmallMaxPairs] routed expert per pair (router fused)
+  int* cnt = rids + kSmallMaxPairs;  // [NB]
   int* sst = cnt + NB;               // [NB] segment starts
   int* s_eoff = sst + NB;            // [E+1]
   int* s_n = s_eoff + E + 1;         // [E] real rows per expert
@@ -296,8 +299,27 @@ __global__ __launch_bounds__(1024) void align_small_kernel(
   const int tid = threadIdx.x, nt = blockDim.x;
   for (int b = tid; b < NB; b += nt) cnt[b] = 0;
   if (tid == 0) errs[0] = 0;
+  const int32_t* ids_src = topk_ids;
+  if (logits) {  // router fused in: wavefront w routes tokens w, w + nw, ...
+    const int lane = tid & 63, nw = nt >> 6;
+    for (int t = tid >> 6; t < P / k; t += nw) {
+      int ce;
+      float cw;
+      if (E <= 512)
+        route_token<8>(logits + (size_t)t * E, E, k, &ce, &cw);
+      else
+        route_token<0>(logits + (size_t)t * E, E, k, &ce, &cw);
+      if (lane < k) {
+        rids[t * k + lane] = ce;
+        ids_out[(size_t)t * k + lane] = ce;
+        w_out[(size_t)t * k + lane] = cw;
+      }
+    }
+    lds_barrier();
+    ids_src = rids;
+  }
   int key = -1, err = 0, l = -1;
-  if (tid < P) key = pair_key(topk_ids, lora_ids, tid, k, E, L, &l, &err);
+  if (tid < P) key = pair_key(ids_src, lora_ids, tid, k, E, L, &l, &err);
   lds_barrier();  // cnt and errs cleared
   if (err) atomicAdd(&errs[0], err);
   // stable rank = earlier pairs with the same key; cnt ends as the key counts
@@ -381,23 +403,31 @@ __global__ __launch_bounds__(1024) void align_small_kernel(
 }  // namespace
 
 int launch_align(const Layout& L, const int32_t* topk_ids, const int32_t* lora_ids, void* ws,
-                 hipStream_t st) {
+                 hipStream_t st, const float* logits, int32_t* ids_out, float* w_out) {
   WsPtrs w = ws_ptrs(ws, L);
   const int P = (int)L.P, NB = (int)L.NB, C = (int)L.C;
   if (P <= 0) return MOE_LORA_OK;  // no pairs: nothing to sort
   const int zero_gu = plan_shrink(L, L.H).splits > 1;
   const int zero_d = plan_shrink(L, L.I).splits > 1;
-  const size_t small_lds = sizeof(int) * (kSmallMaxPairs + 2 * (size_t)NB + 2 * L.E + 1 + 16 + 1);
+  const size_t small_lds = sizeof(int) * (2 * kSmallMaxPairs + 2 * (size_t)NB + 2 * L.E + 1 + 16 + 1);
   if (P <= kSmallMaxPairs && small_lds <= kSmallMaxLds) {
     prof_stage_begin(ST_ALIGN_PLACE, st);
     const size_t lds = small_lds;
     // one thread per pair (whole wavefronts): fewer wavefronts, cheaper barriers
     const int nthreads = std::min(kSmallMaxPairs, (P + 63) / 64 * 64);
     align_small_kernel<<<1, nthreads, lds, st>>>(
-        topk_ids, lora_ids, P, L.k, L.E, L.L, L.bm, L.cap_rows, L.cap_blocks, (int)L.TS, L.r, zero_gu,
-        zero_d, w.hdr, w.sorted, w.eoff, w.segstart, w.segcnt, w.bexp, w.pos, w.tiles, w.zgu, w.zd);
+        logits ? nullptr : topk_ids, lora_ids, P, L.k, L.E, L.L, L.bm, L.cap_rows, L.cap_blocks, (int)L.TS, L.r, zero_gu,
+        zero_d, w.hdr, w.sorted, w.eoff, w.segstart, w.segcnt, w.bexp, w.pos, w.tiles, w.zgu, w.zd,
+        logits, ids_out, w_out);
     prof_stage_end(ST_ALIGN_PLACE, st);
     return hipGetLastError() == hipSuccess ? MOE_LORA_OK : MOE_LORA_EHIP;
+  }
+  if (logits) {  // router first, into the caller's id and weight buffers
+    prof_stage_begin(ST_ROUTE, st);
+    const int rc = launch_router(L, logits, ids_out, w_out, st);
+    prof_stage_end(ST_ROUTE, st);
+    if (rc) return rc;
+    topk_ids = ids_out;
   }
   prof_stage_begin(ST_ALIGN_COUNT, st);
   align_count_kernel<<<C, kAlignChunk, (kAlignChunk + 1 + NB) * sizeof(int), st>>>(

@@ -113,6 +113,7 @@ enum Stage {
   ST_SHRINK_DOWN,
   ST_GEMM_DOWN,
   ST_COMBINE,
+  ST_ROUTE,
   ST_COUNT
 };
 
@@ -123,8 +124,12 @@ void prof_call_done();
 
 // ------------------------------------------------------------------ launchers
 
+// logits != nullptr: route first (top-k and weights from logits [T][E]) into
+// ids_out / w_out, then align on those ids; topk_ids is then unused.
 int launch_align(const Layout& L, const int32_t* topk_ids, const int32_t* lora_ids, void* ws,
-                 hipStream_t st);
+                 hipStream_t st, const float* logits = nullptr, int32_t* ids_out = nullptr,
+                 float* w_out = nullptr);
+int launch_router(const Layout& L, const float* logits, int32_t* ids, float* w, hipStream_t st);
 
 struct ShrinkPlan {
   int splits;       // K split count (1 = plain stores)
