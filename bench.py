@@ -260,6 +260,32 @@ def main():
         "stages_ms": per_stage,
         "stages_ms_note": f"average of {calls} untimed calls with events around every stage",
     }
+    # the path from router logits: moe_lora_route_align (router fused into the
+    # align for small batches) + moe_lora_forward.  The logits are built so the
+    # router reproduces the workload's routing: log(w) at each chosen expert,
+    # -1e30 elsewhere (softmax of log w over the chosen experts is w itself).
+    logits = torch.full((wl.T, wl.E), -1e30, dtype=torch.float32, device="cuda")
+    logits.scatter_(1, dev["topk_ids"].long(), torch.log(dev["topk_weights"].clamp_min(1e-30)))
+    r_ids = torch.empty_like(dev["topk_ids"])
+    r_w = torch.empty_like(dev["topk_weights"])
+
+    def step_routed():
+        lm.moe_lora_route_align(shape, logits, dev["lora_ids"], r_ids, r_w, ws, stream)
+        lm.moe_lora_forward(shape, dev["x"], r_ids, r_w, dev["lora_ids"],
+                            dev["W_gu"], dev["W_down"], dev["A_gu"], dev["B_gu"], dev["A_down"],
+                            dev["B_down"], ws, y, stream)
+
+    for _ in range(args.warmup):
+        step_routed()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step_routed()
+    torch.cuda.synchronize()
+    routed_s = (time.perf_counter() - t0) / args.steps
+    out["from_logits"] = {"ms_per_step": routed_s * 1e3, "tokens_per_s": wl.T / routed_s,
+                          "note": "moe_lora_route_align + moe_lora_forward from logits that "
+                                  "reproduce the workload's routing"}
     cold_iters = args.cold_iters if args.cold_iters >= 0 else (10 if args.workload == 5 else 20)
     if cold_iters > 0:
         out["cold"] = cold_timing(step, cold_iters)

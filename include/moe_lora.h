@@ -136,7 +136,7 @@ int moe_lora_route(const moe_lora_shape* shape, const float* logits, int32_t* to
                    float* topk_weights, void* stream);
 
 /* moe_lora_route followed by moe_lora_align on the routed ids, fused into a
- * single kernel when T*topk <= 1024 (the decode case) and the align's tables
+ * single kernel when T*topk <= 256 (decode batches) and the align's tables
  * fit in LDS; otherwise the router kernel runs first.  Arguments as in the two
  * calls; topk_ids and topk_weights are written and the workspace receives the
  * align outputs. */

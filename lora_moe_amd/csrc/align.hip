@@ -275,8 +275,10 @@ __global__ __launch_bounds__(256) void align_place_kernel(
 
 constexpr int kSmallMaxPairs = 1024;
 constexpr size_t kSmallMaxLds = 64 * 1024;  // the single-workgroup path keeps its tables in LDS
+constexpr int kFusedRouteMaxPairs = 256;  // router fused into the single-workgroup align up to here
 
-// The whole align for P <= 1024 in one workgroup of ceil(P/64) wavefronts (thread =
+// The whole align (and, when given logits, the router: one thread per
+// token) for P <= 1024 in one workgroup of ceil(P/64) wavefronts (thread =
 // pair), same outputs as the four-kernel path.
 __global__ __launch_bounds__(1024) void align_small_kernel(
     const int32_t* __restrict__ topk_ids, const int32_t* __restrict__ lora_ids, int P, int k, int E,
@@ -300,20 +302,10 @@ __global__ __launch_bounds__(1024) void align_small_kernel(
   for (int b = tid; b < NB; b += nt) cnt[b] = 0;
   if (tid == 0) errs[0] = 0;
   const int32_t* ids_src = topk_ids;
-  if (logits) {  // router fused in: wavefront w routes tokens w, w + nw, ...
-    const int lane = tid & 63, nw = nt >> 6;
-    for (int t = tid >> 6; t < P / k; t += nw) {
-      int ce;
-      float cw;
-      if (E <= 512)
-        route_token<8>(logits + (size_t)t * E, E, k, &ce, &cw);
-      else
-        route_token<0>(logits + (size_t)t * E, E, k, &ce, &cw);
-      if (lane < k) {
-        rids[t * k + lane] = ce;
-        ids_out[(size_t)t * k + lane] = ce;
-        w_out[(size_t)t * k + lane] = cw;
-      }
+  if (logits) {  // router fused in: thread t routes token t
+    if (tid < P / k) {
+      route_token_thread(logits + (size_t)tid * E, E, k, rids + tid * k, w_out + (size_t)tid * k);
+      for (int j = 0; j < k; ++j) ids_out[(size_t)tid * k + j] = rids[tid * k + j];
     }
     lds_barrier();
     ids_src = rids;
@@ -410,7 +402,19 @@ int launch_align(const Layout& L, const int32_t* topk_ids, const int32_t* lora_i
   const int zero_gu = plan_shrink(L, L.H).splits > 1;
   const int zero_d = plan_shrink(L, L.I).splits > 1;
   const size_t small_lds = sizeof(int) * (2 * kSmallMaxPairs + 2 * (size_t)NB + 2 * L.E + 1 + 16 + 1);
-  if (P <= kSmallMaxPairs && small_lds <= kSmallMaxLds) {
+  const bool small = P <= kSmallMaxPairs && small_lds <= kSmallMaxLds;
+  // The router runs inside the single-workgroup align (one thread per token)
+  // only for decode-sized batches; beyond that its own kernel (a wavefront per
+  // token, all tokens at once) runs first and the align reads its output.
+  if (logits && !(small && P <= kFusedRouteMaxPairs)) {
+    prof_stage_begin(ST_ROUTE, st);
+    const int rc = launch_router(L, logits, ids_out, w_out, st);
+    prof_stage_end(ST_ROUTE, st);
+    if (rc) return rc;
+    topk_ids = ids_out;
+    logits = nullptr;
+  }
+  if (small) {
     prof_stage_begin(ST_ALIGN_PLACE, st);
     const size_t lds = small_lds;
     // one thread per pair (whole wavefronts): fewer wavefronts, cheaper barriers
@@ -421,13 +425,6 @@ int launch_align(const Layout& L, const int32_t* topk_ids, const int32_t* lora_i
         logits, ids_out, w_out);
     prof_stage_end(ST_ALIGN_PLACE, st);
     return hipGetLastError() == hipSuccess ? MOE_LORA_OK : MOE_LORA_EHIP;
-  }
-  if (logits) {  // router first, into the caller's id and weight buffers
-    prof_stage_begin(ST_ROUTE, st);
-    const int rc = launch_router(L, logits, ids_out, w_out, st);
-    prof_stage_end(ST_ROUTE, st);
-    if (rc) return rc;
-    topk_ids = ids_out;
   }
   prof_stage_begin(ST_ALIGN_COUNT, st);
   align_count_kernel<<<C, kAlignChunk, (kAlignChunk + 1 + NB) * sizeof(int), st>>>(

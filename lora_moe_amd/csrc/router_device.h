@@ -95,4 +95,36 @@ __device__ __forceinline__ void route_token(const float* __restrict__ lg, int E,
   *my_w = ce >= 0 ? ex / sum : 0.f;
 }
 
+// The same choice and weights by one thread for one token (no lane
+// exchanges): k scans over the token's E logits.  For small batches, where a
+// thread per token keeps every token in flight at once.  Writes ids[0..k) and
+// w[0..k) (ids may be LDS: it is read back for the weights).
+__device__ __forceinline__ void route_token_thread(const float* __restrict__ lg, int E, int k,
+                                                   int32_t* ids, float* __restrict__ w) {
+  float pv = __builtin_inff();
+  int pe = -1;
+  float m = 0.f;
+  int nch = 0;
+  for (int j = 0; j < k; ++j) {
+    float bv = -__builtin_inff();
+    int be = -1;
+    for (int e = 0; e < E; ++e) {
+      const float x = lg[e];
+      if (before(pv, pe, x, e) && (be < 0 || before(x, e, bv, be))) {
+        bv = x;
+        be = e;
+      }
+    }
+    ids[j] = be;
+    if (be < 0) continue;  // nothing eligible is left (non-finite logits)
+    if (j == 0) m = bv;
+    ++nch;
+    pv = bv;
+    pe = be;
+  }
+  float sum = 0.f;
+  for (int j = 0; j < nch; ++j) sum += expf(lg[ids[j]] - m);
+  for (int j = 0; j < k; ++j) w[j] = j < nch ? expf(lg[ids[j]] - m) / sum : 0.f;
+}
+
 }  // namespace moelora
