@@ -190,11 +190,11 @@ def main():
     y = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda")
     stream = torch.cuda.current_stream()
 
-    def step():
-        lm.moe_lora_align(shape, dev["topk_ids"], dev["lora_ids"], ws, stream)
+    def step(st=stream):
+        lm.moe_lora_align(shape, dev["topk_ids"], dev["lora_ids"], ws, st)
         lm.moe_lora_forward(shape, dev["x"], dev["topk_ids"], dev["topk_weights"], dev["lora_ids"],
                             dev["W_gu"], dev["W_down"], dev["A_gu"], dev["B_gu"], dev["A_down"],
-                            dev["B_down"], ws, y, stream)
+                            dev["B_down"], ws, y, st)
 
     for _ in range(args.warmup):
         step()
@@ -286,6 +286,26 @@ def main():
     out["from_logits"] = {"ms_per_step": routed_s * 1e3, "tokens_per_s": wl.T / routed_s,
                           "note": "moe_lora_route_align + moe_lora_forward from logits that "
                                   "reproduce the workload's routing"}
+    # the same step captured once in a HIP graph and replayed (no per-launch
+    # host work, launches queued back to back)
+    g = torch.cuda.CUDAGraph()
+    gs = torch.cuda.Stream()
+    gs.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(gs):
+        with torch.cuda.graph(g, stream=gs):
+            step(gs)
+    torch.cuda.current_stream().wait_stream(gs)
+    for _ in range(args.warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        g.replay()
+    torch.cuda.synchronize()
+    graph_s = (time.perf_counter() - t0) / args.steps
+    out["graph"] = {"ms_per_step": graph_s * 1e3, "tokens_per_s": wl.T / graph_s,
+                    "note": "align + forward captured once in a HIP graph, replayed"}
+    del g
     cold_iters = args.cold_iters if args.cold_iters >= 0 else (10 if args.workload == 5 else 20)
     if cold_iters > 0:
         out["cold"] = cold_timing(step, cold_iters)
