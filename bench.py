@@ -64,14 +64,16 @@ def stage_bytes_flops(wl, work):
 def kernel_sources(stage: str, block_m: int) -> list:
     """Source files the kernel of `stage` is built from at this block_m."""
     if stage.startswith("gemm"):
-        fam = "gemm.hip" if block_m <= 64 else "gemm_dma.hip"
+        fam = ["gemm.hip"] if block_m <= 64 else ["gemm_dma.hip", "gemm_expand.h"]
     elif stage.startswith("shrink"):
-        fam = "shrink.hip"
+        fam = ["shrink.hip"]
     elif stage.startswith("align"):
-        fam = "align.hip"
+        fam = ["align.hip", "router_device.h"]
+    elif stage.startswith("route"):
+        fam = ["router.hip", "router_device.h"]
     else:
-        fam = "combine.hip"
-    return [fam, "device_util.h", "internal.h"]
+        fam = ["combine.hip"]
+    return fam + ["device_util.h", "internal.h"]
 
 
 def kernel_source_sha(stage: str, block_m: int) -> str:
