@@ -43,39 +43,46 @@ __device__ __forceinline__ float expand_dot(const float* __restrict__ z,
   return acc;
 }
 
-#ifndef MOELORA_STREAM_ROTATE
-#define MOELORA_STREAM_ROTATE 1  // stagger the K start per wavefront
-#endif
-
-// Tile: 16*RF rows x 64 weight rows per workgroup, 16 weight rows per
-// wavefront.  mode 0: wavefront w owns gate rows j0+8w..j0+8w+7 and the
-// matching up rows I+j0+8w.., so one MFMA column fragment holds 8 gate and 8
-// up columns; mode 1: wavefront w owns output columns n0+16w..n0+16w+15.
+// Tile: 16*RF rows x (16*NWV) weight rows per workgroup of NWV wavefronts,
+// 16 weight rows per wavefront.  mode 0: wavefront w owns gate rows
+// j0+8w..j0+8w+7 and the matching up rows I+j0+8w.., so one MFMA column
+// fragment holds 8 gate and 8 up columns; mode 1: wavefront w owns output
+// columns n0+16w..n0+16w+15.
 //
-// The kernel is a weight stream, and HBM only reaches its bandwidth with many
-// requests outstanding and spread over its channels:
+// The kernel is a weight stream.  What bounds it is the rate at which each
+// CU can have 128-byte lines fetched through its L1, so every byte a CU asks
+// for besides the weights (the row fragments) costs weight bandwidth:
 //  * each wavefront streams its 16 weight rows in chunks of KC = 128 K
 //    elements; a load instruction covers 4 rows x 256 contiguous bytes (whole
-//    128-byte lines); DEPTH chunks are in flight in registers; each chunk is
-//    written to a wavefront-private LDS slice with its 16-byte pieces
-//    XOR-swizzled (piece ^ row), so the MFMA fragment reads (16 rows, same K
-//    piece) spread over all banks.  The slice is private, so no workgroup
-//    barrier is needed: LDS operations of one wavefront complete in order.
-//    The next chunk's loads are issued before this chunk's MFMAs; deeper
-//    register prefetch measured slower (it costs occupancy);
-//  * each wavefront starts at its own K chunk and wraps around: weight rows
-//    lie K*2 bytes apart, so wavefronts walking K in lockstep would hit the
-//    same HBM channels at once (staggering measured +18% on this pattern);
-//  * row fragments (x gathered by token, or h) come from L2 with the weight
-//    chunk they meet; padding rows point at the tile's first row, so their
-//    loads coalesce with it (their outputs are dropped);
+//    128-byte lines), non-temporal (each weight byte is read once); each
+//    chunk is written to a wavefront-private LDS slice with its 16-byte
+//    pieces XOR-swizzled (piece ^ row), so the MFMA fragment reads (16 rows,
+//    same K piece) spread over all banks.  The next chunk's loads are issued
+//    before this chunk's MFMAs (a second chunk in flight measured no faster);
+//  * the row fragments of a chunk (16*RF rows x 128 K of x gathered by
+//    token, or of h) are fetched once per workgroup, one or two 16-byte
+//    pieces per thread, into a double-buffered LDS tile shared by all its
+//    wavefronts: fetched per wavefront they cost up to twice the weight
+//    traffic when every row is real (a dense layer's 32 tokens), and halved
+//    that case's speed.  So the wavefronts of a workgroup walk K together,
+//    one barrier per chunk;
+//  * each workgroup starts at its own K chunk and wraps around: weight rows
+//    lie K*2 bytes apart, so workgroups walking K in lockstep would hit the
+//    same HBM channels at once;
+//  * padding rows point at the tile's first row (their outputs are dropped);
 //  * steady-state loads are unconditional (full chunks; the K remainder is
 //    one masked chunk at the end): a load under a branch makes the compiler
 //    drain all outstanding loads before it.
-template <int MODE, int RF>
-__global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmParams p) {
+// NWV = 8 for gate_up with 32-row tiles halves the row-fragment traffic per
+// weight byte again; the down GEMM keeps NWV = 4 (its grid is small: H
+// columns only, K-split instead).
+template <int MODE, int RF, int NWV>
+__global__ __launch_bounds__(64 * NWV) void grouped_gemm_kernel(GemmParams p) {
   constexpr int KC = 128;
-  __shared__ __attribute__((aligned(16))) uint16_t wl[4][16 * KC];
+  constexpr int XPT = RF * 4 / NWV;  // row-fragment pieces staged per thread per chunk
+  static_assert(XPT >= 1 && XPT * NWV == RF * 4, "row tile pieces must divide over the threads");
+  __shared__ __attribute__((aligned(16))) uint16_t wl[NWV][16 * KC];
+  __shared__ __attribute__((aligned(16))) uint16_t xl[2][RF * 16 * KC];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps chunk math scalar
   const int m = lane & 15, kq = lane >> 4;
@@ -86,10 +93,10 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmParams p) {
   // weight row held by fragment column c (0..15) of this wavefront
   auto wrow_of = [&](int c) -> int {
     if (MODE == 0) {
-      const int j = min((int)blockIdx.x * 32 + wave * 8 + (c & 7), p.I - 1);
+      const int j = min((int)blockIdx.x * (NWV * 8) + wave * 8 + (c & 7), p.I - 1);
       return c < 8 ? j : p.I + j;
     }
-    return min((int)blockIdx.x * 64 + wave * 16 + c, p.N - 1);
+    return min((int)blockIdx.x * (NWV * 16) + wave * 16 + c, p.N - 1);
   };
   const uint16_t* __restrict__ Wexp = p.W + (size_t)e * p.N * p.K;
   // instruction i covers fragment rows 4i..4i+3 (16 lanes x 16 bytes per
@@ -99,20 +106,24 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmParams p) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) woff[i] = (uint32_t)wrow_of(4 * i + (lane >> 4)) * (uint32_t)p.K;
 
-  // row offsets (elements) from p.in; they fit 32 bits (checked on the host)
-  uint32_t aoff[RF];
+  // staged row-fragment pieces: thread tid stages piece (tid & 15) of tile
+  // rows xr[j] = (tid >> 4) + j * 4 * NWV; offsets (elements) from p.in fit
+  // 32 bits (checked on the host)
+  int xr[XPT];
+  uint32_t aoff[XPT];
 #pragma unroll
-  for (int rf = 0; rf < RF; ++rf) {
-    int row = row0 + rf * 16 + m;
+  for (int j = 0; j < XPT; ++j) {
+    xr[j] = (tid >> 4) + j * 4 * NWV;
+    int row = row0 + xr[j];
     int pr = p.sorted[row];
     if (pr >= p.P) {  // padding row: read the tile's first row instead
       row = row0;
       pr = p.sorted[row0];
     }
     if (MODE == 0)
-      aoff[rf] = (uint32_t)(pr < p.P ? pr / p.topk : 0) * (uint32_t)p.K;
+      aoff[j] = (uint32_t)(pr < p.P ? pr / p.topk : 0) * (uint32_t)p.K;
     else
-      aoff[rf] = (uint32_t)row * (uint32_t)p.K;
+      aoff[j] = (uint32_t)row * (uint32_t)p.K;
   }
 
   // full 128-wide chunks run unmasked in rotated order; a K remainder (a
@@ -126,51 +137,52 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmParams p) {
   const int nfull = MODE == 1 ? min(all_full, kc0 + cps) - kc0 : all_full;
   const int krem = (MODE == 0 || split == p.ksplit - 1) ? p.K - all_full * KC : 0;
   const int kbase = kc0 * KC;  // first K element of this split
-  const int rot = (MOELORA_STREAM_ROTATE && nfull) ? (int)((blockIdx.x * 4u + wave) * 7u % (unsigned)nfull) : 0;
+  const int rot = nfull ? (int)((blockIdx.x * 7u + blockIdx.y * 3u) % (unsigned)nfull) : 0;
 
-  u32x4_t rw[4], rx[RF][4];
+  u32x4_t rw[4], rx[XPT];
   auto load = [&](int k0, bool masked) {
+    const bool ok = !masked || piece * 8 < krem;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bool ok = !masked || piece * 8 < krem;
+    for (int i = 0; i < 4; ++i)
       rw[i] = ok ? ld16_stream(Wexp + (woff[i] + (uint32_t)(kbase + k0 + piece * 8))) : zero4();
-    }
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int kk = (4 * s + kq) * 8;
-      const bool ok = !masked || kk < krem;
-#pragma unroll
-      for (int rf = 0; rf < RF; ++rf)
-        rx[rf][s] = ok ? ld16(p.in + (aoff[rf] + (uint32_t)(kbase + k0 + kk))) : zero4();
-    }
+    for (int j = 0; j < XPT; ++j)
+      rx[j] = ok ? ld16(p.in + (aoff[j] + (uint32_t)(kbase + k0 + piece * 8))) : zero4();
   };
+  int buf = 0;
   uint16_t* slice = wl[wave];
 
   f32x4_t acc[RF];
 #pragma unroll
   for (int rf = 0; rf < RF; ++rf) acc[rf] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // the chunk in registers: weight pieces -> LDS slice (swizzled), row
-  // fragments kept aside, then the next chunk's loads are issued before the
-  // MFMAs of this one
+  // the chunk in registers -> LDS (weights to the wavefront's slice, row
+  // pieces to this chunk's shared buffer), then the next chunk's loads are
+  // issued, then one barrier and the MFMAs of this chunk.  The buffer written
+  // here was last read a chunk ago, before the previous barrier.
   auto consume = [&](int next_k0, int next_kind) {  // kind: 0 none, 1 full, 2 masked remainder
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int fr = 4 * i + (lane >> 4);
       *reinterpret_cast<u32x4_t*>(&slice[fr * KC + ((piece ^ fr) << 3)]) = rw[i];
     }
-    u32x4_t xa[RF][4];
+    uint16_t* xb = xl[buf];
 #pragma unroll
-    for (int rf = 0; rf < RF; ++rf)
-#pragma unroll
-      for (int s = 0; s < 4; ++s) xa[rf][s] = rx[rf][s];
+    for (int j = 0; j < XPT; ++j)
+      *reinterpret_cast<u32x4_t*>(&xb[xr[j] * KC + ((piece ^ (xr[j] & 15)) << 3)]) = rx[j];
+    buf ^= 1;
     if (next_kind) load(next_k0, next_kind == 2);
+    lds_barrier();
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const u32x4_t b =
           *reinterpret_cast<const u32x4_t*>(&slice[m * KC + (((4 * s + kq) ^ m) << 3)]);
 #pragma unroll
-      for (int rf = 0; rf < RF; ++rf) acc[rf] = mfma_16x16x32(xa[rf][s], b, acc[rf]);
+      for (int rf = 0; rf < RF; ++rf) {
+        const u32x4_t a =
+            *reinterpret_cast<const u32x4_t*>(&xb[(rf * 16 + m) * KC + (((4 * s + kq) ^ m) << 3)]);
+        acc[rf] = mfma_16x16x32(a, b, acc[rf]);
+      }
     }
   };
 
@@ -208,11 +220,11 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmParams p) {
                               p.B + (((size_t)l * p.E + e) * p.N + wr) * p.r, p.r);
       if (MODE == 0) {
         const float up = __shfl_xor(v, 8, 64);  // lane m < 8: gate; m + 8: its up
-        const int j = blockIdx.x * 32 + wave * 8 + m;
+        const int j = blockIdx.x * (NWV * 8) + wave * 8 + m;
         if (m < 8 && j < p.I)
           p.h_out[(size_t)row * p.I + j] = f32_to_bf16(real ? silu_f32(v) * up : 0.f);
       } else {
-        const int n = blockIdx.x * 64 + wave * 16 + m;
+        const int n = blockIdx.x * (NWV * 16) + wave * 16 + m;
         if (real && n < p.N) p.d_out[split * p.d_slab + (size_t)row * p.H + n] = v * p.topk_w[pr];
       }
     }
@@ -220,9 +232,10 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmParams p) {
 
 template <int MODE, int RF>
 void launch_rf(const GemmParams& gp, int64_t cap_rows, hipStream_t st) {
-  const int ncol = MODE == 0 ? (gp.I + 31) / 32 : (gp.H + 63) / 64;
+  constexpr int NWV = MODE == 0 ? 4 * RF : 4;
+  const int ncol = MODE == 0 ? (gp.I + NWV * 8 - 1) / (NWV * 8) : (gp.H + NWV * 16 - 1) / (NWV * 16);
   dim3 grid(ncol, (unsigned)((cap_rows + RF * 16 - 1) / (RF * 16)), MODE == 1 ? gp.ksplit : 1);
-  grouped_gemm_kernel<MODE, RF><<<grid, 256, 0, st>>>(gp);
+  grouped_gemm_kernel<MODE, RF, NWV><<<grid, NWV * 64, 0, st>>>(gp);
 }
 
 }  // namespace
