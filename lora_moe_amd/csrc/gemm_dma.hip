@@ -36,6 +36,8 @@
 //     validity and weights are staged in LDS at the start.
 // A wavefront whose rows are all padding skips its MFMAs and stores but still
 // copies its share of every stage.
+#include <type_traits>
+
 #include "device_util.h"
 #include "gemm_expand.h"
 #include "internal.h"
@@ -150,7 +152,8 @@ __global__ __launch_bounds__(C::NT, WAVES_PER_SIMD) void grouped_gemm_dma_kernel
 
   const int ntile = (p.K + BK - 1) / BK;  // the last stage may be partial
   const bool partial = (p.K % BK) != 0;
-  auto issue = [&](int s) {
+  auto issue = [&](int s, auto nt_c) {
+    constexpr bool NTL = decltype(nt_c)::value;
     char* A = smem + (s % NS) * C::STAGE;
     char* B = A + C::TILE;
     const int k0 = s * BK;
@@ -160,10 +163,8 @@ __global__ __launch_bounds__(C::NT, WAVES_PER_SIMD) void grouped_gemm_dma_kernel
       const int koff = k < p.K ? k0 : p.K - 8 - lchunk[i] * 8;  // clamped: a valid address
       const int roff = (wave * WROWS + i * RPC) * PROW;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rs, (lds_char*)(A + roff), 16, (int)(a_off[i] + (uint32_t)koff * 2u), 0, 0, 0);
-      if (w_once)  // cache policy operand 2: non-temporal
-        __builtin_amdgcn_global_load_lds((const void*)(b_src[i] + koff), (lds_char*)(B + roff), 16, 0, 2);
-      else
-        __builtin_amdgcn_global_load_lds((const void*)(b_src[i] + koff), (lds_char*)(B + roff), 16, 0, 0);
+      // cache policy operand 2: non-temporal
+      __builtin_amdgcn_global_load_lds((const void*)(b_src[i] + koff), (lds_char*)(B + roff), 16, 0, NTL ? 2 : 0);
     }
   };
   // zero this lane's chunks of stage s that lie beyond K (after they landed)
@@ -202,39 +203,55 @@ __global__ __launch_bounds__(C::NT, WAVES_PER_SIMD) void grouped_gemm_dma_kernel
     for (int ni = 0; ni < NI; ++ni)
       bf[set][ni] = *reinterpret_cast<const u32x4_t*>(B + C::off(wn * 64 + ni * 32 + l32, ch));
   };
-  auto mma = [&](int set) {
+  // The MFMAs of fragment set `set`, with the reads of the next slice's
+  // fragments (stage qn, slice kkn, into the other set) issued after the
+  // first of them: at that first MFMA every older read is complete, so a
+  // conservative wait there costs nothing, and the reads overlap the rest.
+  // The scheduling barriers keep this order (the scheduler would otherwise
+  // sink the reads next to their use).
+  auto step = [&](int set, bool next, int qn, int kkn) {
+    acc[0][0] = mfma_32x32x16(bf[set][0], af[set][0], acc[0][0]);
+    __builtin_amdgcn_sched_barrier(0);
+    if (next) frag(qn, kkn, set ^ 1);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-      for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = mfma_32x32x16(bf[set][ni], af[set][mi], acc[mi][ni]);
+      for (int ni = 0; ni < NI; ++ni)
+        if (mi | ni) acc[mi][ni] = mfma_32x32x16(bf[set][ni], af[set][mi], acc[mi][ni]);
   };
 
-  // prologue: every ring slot gets a stage; wait for stage 0
-#pragma unroll
-  for (int s = 0; s < NS; ++s)
-    if (s < ntile) issue(s);
-  __builtin_amdgcn_s_waitcnt(wait_vm(0));
-  if (tid < BM) {
-    row_ok[tid] = my_ok;
-    row_w[tid] = my_w;
-  }
-  if (partial && ntile == 1) zero_tail(0);
-  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-  stage_barrier();
-  if (live) frag(0, 0, 0);
-
+  // The K loop, specialised on whether this wavefront multiplies (live) and
+  // on the weight cache policy, so that it has no data-dependent branches
+  // around LDS reads: the compiler counts outstanding LDS reads in order, and
+  // a read issued on one path only makes it wait for all of them at the
+  // join.  In particular the MFMAs of a stage's last K slice, issued after
+  // the barrier together with the first fragment reads of the next stage,
+  // must not wait for those reads.
   constexpr int KK = BK / 16;  // MFMA K slices per stage (even)
   constexpr int VM_AHEAD = 2 * NC * (NS - 2) < 63 ? 2 * NC * (NS - 2) : 63;
-  for (int q = 0; q < ntile; ++q) {
+  auto kloop = [&](auto live_c, auto nt_c) {
+    constexpr bool LIVE = decltype(live_c)::value;
+    // prologue: every ring slot gets a stage; wait for stage 0
 #pragma unroll
-    for (int kk = 0; kk + 1 < KK; ++kk) {
-      if (live) {
-        frag(q, kk + 1, (kk + 1) & 1);
-        mma(kk & 1);
-      }
+    for (int s = 0; s < NS; ++s)
+      if (s < ntile) issue(s, nt_c);
+    __builtin_amdgcn_s_waitcnt(wait_vm(0));
+    if (tid < BM) {
+      row_ok[tid] = my_ok;
+      row_w[tid] = my_w;
     }
-    if (q + 1 < ntile) {
-      // own copies of stage q + 1 have landed (later stages may still fly)
+    if (partial && ntile == 1) zero_tail(0);
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    stage_barrier();
+    if (LIVE) frag(0, 0, 0);
+    for (int q = 0; q + 1 < ntile; ++q) {
+#pragma unroll
+      for (int kk = 0; kk + 1 < KK; ++kk)
+        if (LIVE) step(kk & 1, true, q, kk + 1);
+      // own copies of stage q + 1 have landed (later stages may still fly);
+      // the wait stays behind this stage's MFMAs
+      __builtin_amdgcn_sched_barrier(0);
       if (q + NS - 1 < ntile)
         __builtin_amdgcn_s_waitcnt(wait_vm(VM_AHEAD));
       else
@@ -242,10 +259,25 @@ __global__ __launch_bounds__(C::NT, WAVES_PER_SIMD) void grouped_gemm_dma_kernel
       if (partial && q + 1 == ntile - 1) zero_tail(q + 1);
       __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // fragment reads of stage q and zero writes done
       stage_barrier();
-      if (q + NS < ntile) issue(q + NS);  // into the slot stage q just released
-      if (live) frag(q + 1, 0, 0);
+      if (q + NS < ntile) issue(q + NS, nt_c);  // into the slot stage q just released
+      // last slice of stage q (its fragments are in registers), with the
+      // first reads of stage q + 1
+      if (LIVE) step((KK - 1) & 1, true, q + 1, 0);
     }
-    if (live) mma((KK - 1) & 1);
+    if (LIVE) {  // the last stage
+#pragma unroll
+      for (int kk = 0; kk + 1 < KK; ++kk) step(kk & 1, true, ntile - 1, kk + 1);
+      step((KK - 1) & 1, false, 0, 0);
+    }
+  };
+  typedef std::integral_constant<bool, true> yes;
+  typedef std::integral_constant<bool, false> no;
+  if (live) {
+    if (w_once) kloop(yes(), yes());
+    else kloop(yes(), no());
+  } else {
+    if (w_once) kloop(no(), yes());
+    else kloop(no(), no());
   }
   if (!live) return;
 
