@@ -93,6 +93,29 @@ typedef struct moe_lora_views {
  * negative status when the shape is invalid.  Host only, pure. */
 int moe_lora_resolve_block_m(const moe_lora_shape* shape);
 
+/* One entry of a tile-configuration table, the result of an offline sweep
+ * (the pages' tuned kernel configurations per shape: "Multi-LoRA for MoE
+ * models", section "Kernel optimizations").  Key: the shape class, with
+ * rows_per_expert = ceil(T*topk / min(E, T*topk)) of the swept shape; value:
+ * the block_m measured fastest for it. */
+typedef struct {
+  int32_t rows_per_expert, H, I, E, r, L; /* key */
+  int32_t block_m;                        /* value: 16, 32, 64, 128 or 256 */
+} moe_lora_tune_entry;
+
+/* block_m for `shape` chosen from a tuning table: the shape's own block_m
+ * when it is non-zero; otherwise the block_m of the nearest entry, where the
+ * distance is the sum over the key fields of |log2(shape value / entry
+ * value)|, rows_per_expert counted four times (ties: the earlier entry),
+ * provided that distance is at most max_dist (max_dist <= 0: no limit) and
+ * the shape's workspace layout is valid with that block_m; otherwise the
+ * built-in choice (moe_lora_resolve_block_m).  Entries with a block_m
+ * outside {16, 32, 64, 128, 256} or a non-positive key field are skipped.
+ * table may be NULL when n == 0.  Returns a negative status when the shape
+ * is invalid.  Host only, pure: the table is read, not kept. */
+int moe_lora_tune_block_m(const moe_lora_shape* shape, const moe_lora_tune_entry* table, int32_t n,
+                          float max_dist);
+
 /* Bytes of device workspace that moe_lora_align / moe_lora_forward need for
  * this shape, or 0 when the shape is invalid.  Host only, pure. */
 size_t moe_lora_workspace_bytes(const moe_lora_shape* shape);

@@ -12,6 +12,7 @@ import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libmoe_lora.so")
+TUNING_PATH = os.path.join(PKG, "tuning", "gfx950.json")
 
 MOE_LORA_OK = 0
 MOE_LORA_EINVAL = -1
@@ -48,9 +49,38 @@ class moe_lora_views(ctypes.Structure):
         ("d_splits", ctypes.c_int32)]
 
 
-def make_shape(T, H, I, E, topk, L, r, block_m=0, lora_scale=1.0) -> moe_lora_shape:
-    return moe_lora_shape(int(T), int(H), int(I), int(E), int(topk), int(L), int(r), int(block_m),
-                          float(lora_scale))
+class moe_lora_tune_entry(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("rows_per_expert", "H", "I", "E", "r", "L", "block_m")]
+
+
+def make_shape(T, H, I, E, topk, L, r, block_m=0, lora_scale=1.0, tuning=None) -> moe_lora_shape:
+    """The shape struct; with block_m == 0 and a tuning table (load_tuning),
+    block_m is taken from the table (moe_lora_tune_block_m)."""
+    s = moe_lora_shape(int(T), int(H), int(I), int(E), int(topk), int(L), int(r), int(block_m),
+                       float(lora_scale))
+    if tuning is not None and not block_m:
+        bm = moe_lora_tune_block_m(s, tuning)
+        if bm > 0:
+            s.block_m = bm
+    return s
+
+
+def load_tuning(path: str = TUNING_PATH):
+    """Entries of a tile-configuration table written by ``lora_moe_amd.tune``
+    (JSON), as the C array moe_lora_tune_block_m reads."""
+    import json
+    with open(path) as f:
+        doc = json.load(f)
+    rows = doc["entries"]
+    arr = (moe_lora_tune_entry * max(1, len(rows)))()
+    for i, e in enumerate(rows):
+        arr[i] = moe_lora_tune_entry(*(int(e[n]) for n, _ in moe_lora_tune_entry._fields_))
+    return arr, len(rows)
+
+
+def moe_lora_tune_block_m(shape: moe_lora_shape, tuning, max_dist: float = 0.0) -> int:
+    table, n = tuning
+    return load_library().moe_lora_tune_block_m(ctypes.byref(shape), table, int(n), float(max_dist))
 
 
 def load_library(path: str = LIB_PATH):
@@ -66,6 +96,9 @@ def load_library(path: str = LIB_PATH):
     i32 = ctypes.c_int
     lib.moe_lora_resolve_block_m.argtypes = [sp]
     lib.moe_lora_resolve_block_m.restype = i32
+    lib.moe_lora_tune_block_m.argtypes = [sp, ctypes.POINTER(moe_lora_tune_entry), ctypes.c_int32,
+                                          ctypes.c_float]
+    lib.moe_lora_tune_block_m.restype = i32
     lib.moe_lora_workspace_bytes.argtypes = [sp]
     lib.moe_lora_workspace_bytes.restype = ctypes.c_size_t
     lib.moe_lora_align.argtypes = [sp, vp, vp, vp, ctypes.c_size_t, vp]

@@ -1,6 +1,7 @@
 // C ABI of the MoE-LoRA library: argument checks, workspace layout, stage
 // dispatch and stage timing.  Declarations and contracts: include/moe_lora.h.
 #include <algorithm>
+#include <cmath>
 #include <vector>
 
 #include "internal.h"
@@ -161,6 +162,47 @@ extern "C" {
 int moe_lora_resolve_block_m(const moe_lora_shape* shape) {
   int rc = check_shape(shape);
   return rc ? rc : resolve_bm(shape);
+}
+
+int moe_lora_tune_block_m(const moe_lora_shape* shape, const moe_lora_tune_entry* table, int32_t n,
+                          float max_dist) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  if (shape->block_m) return shape->block_m;
+  const int64_t P = (int64_t)shape->T * shape->topk;
+  const int64_t touched = std::max<int64_t>(1, std::min<int64_t>(shape->E, P));
+  const double key[6] = {(double)((P + touched - 1) / touched), (double)shape->H, (double)shape->I,
+                         (double)shape->E, (double)shape->r, (double)shape->L};
+  const double weight[6] = {4.0, 1.0, 1.0, 1.0, 1.0, 1.0};
+  int best = -1;
+  double best_d = 0.0;
+  for (int32_t i = 0; table && i < n; ++i) {
+    const moe_lora_tune_entry& t = table[i];
+    const int bm = t.block_m;
+    if (bm != 16 && bm != 32 && bm != 64 && bm != 128 && bm != 256) continue;
+    const int32_t ek[6] = {t.rows_per_expert, t.H, t.I, t.E, t.r, t.L};
+    double d = 0.0;
+    bool ok = true;
+    for (int j = 0; j < 6; ++j) {
+      if (ek[j] <= 0) {
+        ok = false;
+        break;
+      }
+      d += weight[j] * std::fabs(std::log2(std::max(key[j], 1.0) / (double)ek[j]));
+    }
+    if (!ok || (max_dist > 0.f && d > (double)max_dist)) continue;
+    if (best < 0 || d < best_d) {
+      best = i;
+      best_d = d;
+    }
+  }
+  if (best >= 0) {
+    moe_lora_shape s2 = *shape;
+    s2.block_m = table[best].block_m;
+    Layout L;
+    if (make_layout(&s2, &L) == MOE_LORA_OK) return s2.block_m;
+  }
+  return resolve_bm(shape);
 }
 
 size_t moe_lora_workspace_bytes(const moe_lora_shape* shape) {

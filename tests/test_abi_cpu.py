@@ -112,3 +112,56 @@ def test_view_offsets_are_aligned_and_disjoint(lib):
     assert all(a % 256 == 0 for a in addrs)
     assert len(set(addrs)) == len(addrs)
     assert v.d - (1 << 20) + v.cap_rows * wl.H * 4 <= lm.moe_lora_workspace_bytes(s)
+
+
+# ------------------------------------------------------------------ tuning table
+
+def _entry(rows, H, I, E, r, L, bm):
+    return lm.moe_lora_tune_entry(rows, H, I, E, r, L, bm)
+
+
+def test_tune_pick_nearest_and_fallbacks(lib):
+    """moe_lora_tune_block_m: nearest entry by the weighted log2 distance,
+    the built-in choice when the table is empty, too far or invalid, and the
+    shape's own block_m when it is set."""
+    decode = lm.make_shape(16, 4096, 11008, 8, 2, 8, 32)       # 4 rows per expert
+    prefill = lm.make_shape(8192, 7168, 2048, 256, 8, 8, 64)   # 256 rows per expert
+    table = (lm.moe_lora_tune_entry * 3)(_entry(4, 4096, 11008, 8, 32, 8, 64),
+                                         _entry(256, 7168, 2048, 256, 64, 8, 128),
+                                         _entry(300, 7168, 2048, 256, 64, 8, 256))
+    t = (table, 3)
+    assert lm.moe_lora_tune_block_m(decode, t) == 64
+    assert lm.moe_lora_tune_block_m(prefill, t) == 128          # exact key beats the near one
+    builtin = lm.moe_lora_resolve_block_m(decode)
+    assert lm.moe_lora_tune_block_m(decode, (table, 0)) == builtin
+    # rows_per_expert counts four times: 4 -> 8 rows is distance 4
+    far = (lm.moe_lora_tune_entry * 1)(_entry(8, 4096, 11008, 8, 32, 8, 128))
+    assert lm.moe_lora_tune_block_m(decode, (far, 1), 3.5) == builtin
+    assert lm.moe_lora_tune_block_m(decode, (far, 1), 4.5) == 128
+    assert lm.moe_lora_tune_block_m(decode, (far, 1), 0.0) == 128
+    # invalid entries are skipped
+    bad = (lm.moe_lora_tune_entry * 2)(_entry(4, 4096, 11008, 8, 32, 8, 48),
+                                       _entry(0, 4096, 11008, 8, 32, 8, 32))
+    assert lm.moe_lora_tune_block_m(decode, (bad, 2)) == builtin
+    # a set block_m wins; an invalid shape returns its status
+    assert lm.moe_lora_tune_block_m(lm.make_shape(16, 4096, 11008, 8, 2, 8, 32, 128), t) == 128
+    assert lm.moe_lora_tune_block_m(lm.make_shape(16, 4096, 11008, 8, 2, 8, 7), t) == lm.MOE_LORA_EUNSUPPORTED
+    # make_shape consults the table only when block_m is 0
+    assert lm.make_shape(16, 4096, 11008, 8, 2, 8, 32, tuning=t).block_m == 64
+    assert lm.make_shape(16, 4096, 11008, 8, 2, 8, 32, 32, tuning=t).block_m == 32
+
+
+def test_committed_tuning_table_is_valid(lib):
+    """The shipped table loads, its entries are complete and valid, and each
+    entry picks its own block_m for the workload it was swept on."""
+    import json
+    doc = json.load(open(lm.TUNING_PATH))
+    assert doc["arch"] == "gfx950" and doc["entries"]
+    table = lm.load_tuning()
+    byname = {w.name: w for w in synth.WORKLOADS.values()}
+    for e in doc["entries"]:
+        assert e["block_m"] in (16, 32, 64, 128, 256)
+        assert str(e["block_m"]) in e["ms"] and min(e["ms"], key=e["ms"].get) == str(e["block_m"])
+        wl = byname[e["workload"]]
+        shape = lm.make_shape(wl.T, wl.H, wl.I, wl.E, wl.topk, wl.L, wl.r, 0, wl.scale, tuning=table)
+        assert shape.block_m == e["block_m"]

@@ -1,0 +1,18 @@
+"""The layer at the block_m the shipped tile-configuration table picks
+matches the fp64 reference, for a shape in the table's range but not in it."""
+import pytest
+
+import synth
+from test_gpu_parity import full_check
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("n", [1])
+def test_layer_at_tuned_block_m(n):
+    import lora_moe_amd as lm
+    table = lm.load_tuning()
+    wl = synth.WORKLOADS[n]
+    shape = lm.make_shape(wl.T, wl.H, wl.I, wl.E, wl.topk, wl.L, wl.r, 0, wl.scale, tuning=table)
+    assert shape.block_m in (16, 32, 64, 128, 256)
+    full_check(synth.make_inputs(wl), shape.block_m, f"workload {n} at tuned block_m {shape.block_m}")
