@@ -168,7 +168,7 @@ def cpu_baseline(inp, target_s):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+        print("bench.py runs on one GPU only: this library has no multi-GPU path "
               "(collectives and sharding are out of scope); rerun with --gpus 1.",
               file=sys.stderr, flush=True)
         sys.exit(2)
