@@ -434,13 +434,10 @@ int launch_align(const Layout& L, const int32_t* topk_ids, const int32_t* lora_i
   prof_stage_begin(ST_ALIGN_PLACE, st);
   const size_t off_lds = sizeof(int) * (16 + 2 * (size_t)L.E + 1 + NB);
   if (off_lds > 64 * 1024) {  // above the default dynamic LDS limit (at most 115 KB here)
-    static bool attr_set = false;
-    if (!attr_set) {
-      if (hipFuncSetAttribute(reinterpret_cast<const void*>(&align_offsets_kernel),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
-        return MOE_LORA_EHIP;
-      attr_set = true;
-    }
+    static std::atomic<uint64_t> attr_done{0};
+    const int rc = ensure_dynamic_lds(reinterpret_cast<const void*>(&align_offsets_kernel), 160 * 1024,
+                                      attr_done);
+    if (rc) return rc;
   }
   align_offsets_kernel<<<1, 1024, off_lds, st>>>(
       P, L.E, L.L, C, L.bm, L.cap_rows, L.cap_blocks, (int)L.TS, w.chunkerr, w.segcnt, w.hdr,

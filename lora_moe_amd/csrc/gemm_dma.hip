@@ -335,17 +335,16 @@ __global__ __launch_bounds__(C::NT, WAVES_PER_SIMD) void grouped_gemm_dma_kernel
 
 template <class C, int WAVES_PER_SIMD>
 int launch_dma(const GemmParams& gp_in, int mode, int64_t cap_rows, hipStream_t st) {
-  static bool attr_set[2] = {false, false};
+  static std::atomic<uint64_t> attr_done[2];
   GemmParams gp = gp_in;
   gp.ncol = mode == 0 ? (gp.I + C::BN / 2 - 1) / (C::BN / 2) : (gp.N + C::BN - 1) / C::BN;
   gp.nrowt = (int)((cap_rows + C::BM - 1) / C::BM);
   const unsigned grid = (unsigned)gp.ncol * (unsigned)gp.nrowt;
   const void* fn = mode == 0 ? reinterpret_cast<const void*>(&grouped_gemm_dma_kernel<0, C, WAVES_PER_SIMD>)
                              : reinterpret_cast<const void*>(&grouped_gemm_dma_kernel<1, C, WAVES_PER_SIMD>);
-  if (C::LDS > 64 * 1024 && !attr_set[mode]) {  // more than the default 64 KB of dynamic LDS
-    if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS) != hipSuccess)
-      return MOE_LORA_EHIP;
-    attr_set[mode] = true;
+  if (C::LDS > 64 * 1024) {  // more than the default 64 KB of dynamic LDS
+    const int rc = ensure_dynamic_lds(fn, C::LDS, attr_done[mode]);
+    if (rc) return rc;
   }
   if (mode == 0)
     grouped_gemm_dma_kernel<0, C, WAVES_PER_SIMD><<<grid, C::NT, C::LDS, st>>>(gp);

@@ -6,6 +6,7 @@
 #include <stddef.h>
 
 #include <algorithm>
+#include <atomic>
 #include <stdint.h>
 
 #include "moe_lora.h"
@@ -123,6 +124,22 @@ void prof_stage_end(int stage, hipStream_t st);
 void prof_call_done();
 
 // ------------------------------------------------------------------ launchers
+
+// Raises kernel fn's dynamic-LDS limit to `bytes` on the current device (the
+// attribute belongs to the device; above 64 KB it must be set before the
+// launch).  `done` remembers the devices (ids < 64) already set; safe to call
+// from several host threads.
+inline int ensure_dynamic_lds(const void* fn, int bytes, std::atomic<uint64_t>& done) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_LORA_EHIP;
+  const uint64_t bit = dev >= 0 && dev < 64 ? (uint64_t)1 << dev : 0;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return MOE_LORA_OK;
+  if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes) != hipSuccess)
+    return MOE_LORA_EHIP;
+  if (bit) done.fetch_or(bit, std::memory_order_acq_rel);
+  return MOE_LORA_OK;
+}
+
 
 // logits != nullptr: route first (top-k and weights from logits [T][E]) into
 // ids_out / w_out, then align on those ids; topk_ids is then unused.
