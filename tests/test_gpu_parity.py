@@ -168,6 +168,17 @@ def test_edge_cases():
     assert lm.moe_lora_device_errors(shape, ws) == 4
 
 
+@pytest.mark.parametrize("T,E,L", [(200, 4, 100), (600, 64, 200)])
+@pytest.mark.parametrize("bm", [0, 32, 128, 256])
+def test_more_than_64_adapters(T, E, L, bm):
+    """L > 64 adapters: the tiled expand scans adapter ids 64 at a time; the
+    align's (expert, slot) table has E x (L + 1) buckets (12864 at E = 64,
+    L = 200, with P = 1200 pairs: the multi-kernel align)."""
+    wl = synth.Workload("many-adapters", T=T, H=256, I=384, E=E, topk=2, L=L, r=16,
+                        lora_mode="uniform_with_none")
+    full_check(synth.make_inputs(wl), bm, f"T={T} E={E} L={L} bm={bm}")
+
+
 def test_shrink_stage_matches_reference():
     """z = x A for every adapter row, against the reference's shrink output."""
     import lora_moe_amd as lm
