@@ -115,6 +115,30 @@ __device__ __forceinline__ void write_pads_and_blocks(int32_t* __restrict__ sort
   for (int64_t blk = num_padded / bm + threadIdx.x; blk < cap_blocks; blk += blockDim.x) bexp[blk] = -1;
 }
 
+// Clears the split-K accumulators (z, r floats per row) of the rows in
+// `row` (one per lane, -1 = none) of a whole wavefront: the lanes take the
+// rows in turn, 64 / (r/4) rows per store instruction with consecutive
+// lanes on consecutive 16-byte pieces of a row, so each store writes whole
+// rows (a lane-per-row store writes 64 scattered pieces).  All lanes of the
+// wavefront must call it; r % 8 == 0 and r <= 128.
+__device__ __forceinline__ void clear_z_rows(int row, int r, int zero_gu, int zero_d,
+                                             float* __restrict__ zgu, float* __restrict__ zd) {
+  const int lane = threadIdx.x & 63;
+  const int cpr = r >> 2;        // 16-byte pieces per row (2..32)
+  const int rpi = 64 / cpr;      // rows per instruction
+  const int sub = lane / cpr, piece = lane - sub * cpr;
+  const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j0 = 0; j0 < 64; j0 += rpi) {
+    const int j = j0 + sub;
+    const int src = j < 64 ? j : 63;
+    const int rj = __shfl(row, src, 64);
+    if (sub < rpi && j < 64 && rj >= 0) {
+      if (zero_gu) *reinterpret_cast<float4*>(zgu + (size_t)rj * r + piece * 4) = z;
+      if (zero_d) *reinterpret_cast<float4*>(zd + (size_t)rj * r + piece * 4) = z;
+    }
+  }
+}
+
 __global__ __launch_bounds__(kAlignChunk) void align_count_kernel(
     const int32_t* __restrict__ topk_ids, const int32_t* __restrict__ lora_ids, int P, int k, int E,
     int L, int NB, int C, int32_t* __restrict__ chunk_cnt, int32_t* __restrict__ chunk_err,
@@ -253,24 +277,21 @@ __global__ __launch_bounds__(256) void align_place_kernel(
     int32_t* __restrict__ sorted, int32_t* __restrict__ pos, float* __restrict__ zgu,
     float* __restrict__ zd) {
   const int p = blockIdx.x * blockDim.x + threadIdx.x;
-  if (p >= P) return;
-  int l;
-  const int key = pair_key(topk_ids, lora_ids, p, k, E, L, &l, nullptr);
-  if (key < 0) {
-    pos[p] = -1;
-    return;
-  }
-  const int c = p / kAlignChunk;
-  const int row = segstart[key] + chunk_cnt[(size_t)key * C + c] + rank[p];
-  sorted[row] = p;
-  pos[p] = row;
-  if (l >= 0) {  // clear the split-K accumulators of adapter rows
-    for (int q = 0; q < r; q += 4) {
-      const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (zero_gu) *reinterpret_cast<float4*>(zgu + (size_t)row * r + q) = z;
-      if (zero_d) *reinterpret_cast<float4*>(zd + (size_t)row * r + q) = z;
+  int zrow = -1;  // adapter row whose split-K accumulators this lane's pair owns
+  if (p < P) {
+    int l;
+    const int key = pair_key(topk_ids, lora_ids, p, k, E, L, &l, nullptr);
+    if (key < 0) {
+      pos[p] = -1;
+    } else {
+      const int c = p / kAlignChunk;
+      const int row = segstart[key] + chunk_cnt[(size_t)key * C + c] + rank[p];
+      sorted[row] = p;
+      pos[p] = row;
+      if (l >= 0) zrow = row;
     }
   }
+  if (zero_gu || zero_d) clear_z_rows(zrow, r, zero_gu, zero_d, zgu, zd);  // whole wavefronts
 }
 
 constexpr int kSmallMaxPairs = 1024;
@@ -348,6 +369,7 @@ __global__ __launch_bounds__(1024) void align_small_kernel(
   lds_barrier();
   const int num_padded = total;
   write_pads_and_blocks(sorted, bexp, s_eoff, s_n, E, P, bm, cap_rows, cap_blocks);
+  int zrow = -1;  // adapter row whose split-K accumulators this pair owns
   if (tid < P) {
     if (key < 0) {
       pos[tid] = -1;
@@ -355,15 +377,10 @@ __global__ __launch_bounds__(1024) void align_small_kernel(
       const int row = sst[key] + rnk;
       sorted[row] = tid;
       pos[tid] = row;
-      if (l >= 0) {
-        for (int q = 0; q < r; q += 4) {
-          const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
-          if (zero_gu) *reinterpret_cast<float4*>(zgu + (size_t)row * r + q) = z;
-          if (zero_d) *reinterpret_cast<float4*>(zd + (size_t)row * r + q) = z;
-        }
-      }
+      if (l >= 0) zrow = row;
     }
   }
+  if (zero_gu || zero_d) clear_z_rows(zrow, r, zero_gu, zero_d, zgu, zd);  // whole wavefronts
 
   // shrink tiles: segments (e, l < L) cut into pieces of <= TS rows
   const int NS = E * L;
