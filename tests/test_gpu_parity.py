@@ -168,6 +168,20 @@ def test_edge_cases():
     assert lm.moe_lora_device_errors(shape, ws) == 4
 
 
+@pytest.mark.parametrize("bm", [0, 32, 128, 256])
+def test_routing_extremes(bm):
+    """Every token to every expert (topk = E), and every token to one expert
+    (several row tiles of one expert, the others untouched)."""
+    base = synth.Workload("extreme", T=300, H=256, I=128, E=4, topk=4, L=3, r=16,
+                          lora_mode="uniform_with_none")
+    full_check(synth.make_inputs(base), bm, f"topk = E bm={bm}")
+    one = replace(base, T=700, E=8, topk=1)
+    inp = synth.make_inputs(one)
+    inp.topk_ids[:] = 5
+    inp.topk_weights[:] = 1.0
+    full_check(inp, bm, f"one expert bm={bm}")
+
+
 @pytest.mark.parametrize("T,E,L", [(200, 4, 100), (600, 64, 200)])
 @pytest.mark.parametrize("bm", [0, 32, 128, 256])
 def test_more_than_64_adapters(T, E, L, bm):
