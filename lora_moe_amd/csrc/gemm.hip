@@ -8,12 +8,14 @@
 // same kernel rather than by a separate add (section "Kernel optimizations":
 // the add of the LoRA result to the base result is fused into the expand).
 //
-// mode 0 (gate_up): a workgroup owns 32 columns j0..j0+31 of the
-//   intermediate and computes both the gate rows j and the up rows I+j of
-//   W_gu, so the SiLU gate h = silu(gate) * up is formed in registers:
-//   the lane holding gate(row, j) also holds up(row, j).  h is stored bf16.
-// mode 1 (down): a workgroup owns 64 output columns; the epilogue adds the
-//   expand and multiplies by the pair's top-k weight; d is stored fp32.
+// mode 0 (gate_up): a workgroup owns 8 * NWV columns j0.. of the
+//   intermediate (32 or 64) and computes both the gate rows j and the up
+//   rows I+j of W_gu, so the SiLU gate h = silu(gate) * up is formed in
+//   registers: the lane holding gate(row, j) also holds up(row, j).  h is
+//   stored bf16.
+// mode 1 (down): a workgroup owns 64 output columns of one K split; the
+//   epilogue adds the expand (first split only) and multiplies by the pair's
+//   top-k weight; d is stored fp32, one slab per K split.
 //
 // This family serves small row counts per expert (block_m <= 64, decode):
 // every weight byte is used by one row tile only, so the kernel is a weight
