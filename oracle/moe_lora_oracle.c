@@ -16,7 +16,11 @@
  *     outputs (same section); the weighted top-k sum is the plain reading;
  *   - the activation between the projections is not named on the pages; the
  *     plain reading used here is SiLU-gating: h = silu(gate) * up with
- *     silu(v) = v / (1 + exp(-v)), gate = first half of the gate_up output.
+ *     silu(v) = v / (1 + exp(-v)), gate = first half of the gate_up output;
+ *   - the (expert, adapter) align: a stable counting sort of the pairs with
+ *     per-expert padding (orc_align), and the router that picks the top-k
+ *     experts and their weights from logits (orc_route); the readings are in
+ *     their comments.
  *
  * Parity status: every function here is pinned by the CPU tests (closed-form
  * worked examples, reductions to a dense SwiGLU MLP computed with library
