@@ -213,7 +213,10 @@ ShrinkPlan plan_shrink(const Layout& L, int K) {
   // expected number of shrink tiles: at most one per touched (expert, adapter)
   // segment plus one per TS adapter rows
   const int64_t est = std::max<int64_t>(1, std::min<int64_t>(L.max_tiles, std::min<int64_t>(L.P, (int64_t)L.E * L.L)));
-  int splits = (int)std::max<int64_t>(1, 2048 / est);
+  // K splits only while the tiles alone leave the chip short of work: with
+  // 384 or more tiles (1.5 per CU) a single split measured as fast or faster
+  // (no atomics, and the align then has no accumulators to clear)
+  int splits = est >= 384 ? 1 : (int)std::max<int64_t>(1, 2048 / est);
   splits = std::min(splits, std::max(1, nsteps / 4));  // >= 4 steps: one per wavefront
   sp.splits = splits;
   const int64_t items = L.max_tiles * splits;
