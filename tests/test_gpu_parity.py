@@ -86,13 +86,16 @@ def test_align_deterministic():
 
 # ------------------------------------------------------------------ layer, small shapes
 
-def full_check(inp, block_m=0, what="", scale=None):
+def full_check(inp, block_m=0, what="", scale=None, errors=0):
+    import lora_moe_amd as lm
     if scale is not None:
         inp = synth.Inputs(replace(inp.wl, scale=scale), **{k: v for k, v in inp.arrays().items()})
     wl = inp.wl
     log(f"layer {what}: T={wl.T} H={wl.H} I={wl.I} E={wl.E} k={wl.topk} L={wl.L} r={wl.r} bm={block_m}")
     dev = to_device(inp)
     y, shape, ws = run_gpu(dev, wl, block_m)
+    # invalid ids plus GEMM waits for in-launch shrink workgroups that gave up
+    assert lm.moe_lora_device_errors(shape, ws) == errors, what
     ref = oracle_tokens(inp, None)
     compare(y, ref, what)
     if (inp.lora_ids >= 0).any():
@@ -161,7 +164,7 @@ def test_edge_cases():
     inp.topk_ids[7, 0] = -2
     inp.lora_ids[5] = 17
     inp.lora_ids[9] = -4
-    y, ref = full_check(inp, 0, "invalid ids")
+    y, ref = full_check(inp, 0, "invalid ids", errors=4)
     import lora_moe_amd as lm
     dev = to_device(inp)
     _, shape, ws = run_gpu(dev, inp.wl)
@@ -231,6 +234,8 @@ def test_workload_full_size_sampled(n, ntok):
     toks = sample_tokens(wl.T, ntok)
     synth.host_slabs_for_tokens(inp, toks)
     y, shape, ws = run_gpu(dev, wl)
+    import lora_moe_amd as lm
+    assert lm.moe_lora_device_errors(shape, ws) == 0  # no shrink wait gave up
     ref = oracle_tokens(inp, toks)
     # workloads 2-5 take the stated tolerance; the dense one (not among the
     # stated workloads, I = 25600) the one scaled for its down-projection depth
