@@ -191,6 +191,13 @@ __global__ __launch_bounds__(C::NT, WAVES_PER_SIMD) void grouped_gemm_dma_kernel
 
   const int wrow = wm * (BM / 2);                    // first tile row of this wavefront
   const bool live = p.sorted[row0 + wrow] < p.P;     // any real row in this wavefront's rows
+  // 32-row blocks of this wavefront that hold a real row: padding rows close
+  // an expert's run, so a block holds one exactly when its first row is real
+  // (block 0 does whenever the wavefront is live); the others skip their MFMAs
+  bool blk_live[MI];
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+    blk_live[mi] = __builtin_amdgcn_readfirstlane(p.sorted[row0 + wrow + 32 * mi] < p.P);
   u32x4_t af[2][MI], bf[2][NI];
   auto frag = [&](int s, int kk, int set) {
     const char* A = smem + (s % NS) * C::STAGE;
@@ -218,7 +225,8 @@ __global__ __launch_bounds__(C::NT, WAVES_PER_SIMD) void grouped_gemm_dma_kernel
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni)
-        if (mi | ni) acc[mi][ni] = mfma_32x32x16(bf[set][ni], af[set][mi], acc[mi][ni]);
+        if ((mi | ni) && (mi == 0 || blk_live[mi]))
+          acc[mi][ni] = mfma_32x32x16(bf[set][ni], af[set][mi], acc[mi][ni]);
   };
 
   // The K loop, specialised on whether this wavefront multiplies (live) and
