@@ -222,6 +222,30 @@ def test_shrink_stage_matches_reference():
     assert checked > 20
 
 
+@pytest.mark.parametrize("bm", [0, 16, 32, 64, 128, 256])
+def test_exact_small_integer_layer(bm):
+    """Small-integer inputs make every intermediate exact (exact_inputs.py):
+    the layer output must equal the exact values the fp64 reference gives
+    (exact_inputs.exact) bit for bit, with and without adapters, in every GEMM family and through the
+    split-K shrinks' atomics."""
+    import lora_moe_amd as lm
+    import exact_inputs
+    inp = exact_inputs.make()
+    wl = inp.wl
+    log(f"exact integers bm={bm}: T={wl.T} H={wl.H} I={wl.I} E={wl.E} k={wl.topk} L={wl.L} r={wl.r}")
+    dev = to_device(inp)
+    y, shape, ws = run_gpu(dev, wl, bm)
+    assert lm.moe_lora_device_errors(shape, ws) == 0
+    want = exact_inputs.exact(oracle_tokens(inp, None))
+    bad = np.argwhere(y != want)
+    assert bad.size == 0, f"{len(bad)} outputs differ, first {bad[:3].tolist()}: {y[tuple(bad[0])]} vs {want[tuple(bad[0])]}"
+    none = torch.full_like(dev["lora_ids"], -1)
+    y0, _, _ = run_gpu(dev, wl, bm, lora_ids=none, workspace=ws)
+    want0 = exact_inputs.exact(oracle_tokens(inp, None, lora_ids=np.full_like(inp.lora_ids, -1)))
+    assert np.array_equal(y0, want0)
+    assert not np.array_equal(y, y0)
+
+
 # ------------------------------------------------------------------ full-size workloads
 
 @pytest.mark.parametrize("n,ntok", [(2, 16), (3, 24), (4, 24), (5, 8), (6, 16)])
