@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--cold-iters", type=int, default=-1,
                     help="extra per-call timings with L2 and MALL flushed before each call "
                          "(default 20, 10 for workload 5; 0 disables)")
+    ap.add_argument("--read-probe-mb", type=int, default=0,
+                    help="time a bf16 reduction and a device copy over this many MiB (attainable HBM rates)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="only run a plain device copy of this many MB (counter calibration)")
     return ap.parse_args()
@@ -118,6 +120,32 @@ def copy_probe(mb):
                       "launches": 5}), flush=True)
 
 
+def read_probe(mb, iters=10):
+    """Attainable HBM rates on this device as context for the nominal 8 TB/s:
+    a reduction over an mb-MiB bf16 buffer (torch.sum, fp32 accumulation;
+    reads the buffer once) and a device copy of it (reads and writes it),
+    each timed over `iters` launches after two warm-ups."""
+    import torch
+    n = mb * (1 << 20) // 2
+    a = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    b = torch.empty_like(a)
+    out = {"read_probe_bytes": n * 2}
+    for name, fn, moved in (("sum", lambda: a.sum(dtype=torch.float32), n * 2),
+                            ("copy", lambda: b.copy_(a), n * 4)):
+        for _ in range(2):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / iters
+        out[f"{name}_ms"] = ms
+        out[f"{name}_GBps"] = moved / (ms * 1e-3) / 1e9
+    print(json.dumps(out), flush=True)
+
+
 def cold_timing(step, iters, flush_mb=512):
     """Per-call times of align+forward with the caches flushed first: a
     flush_mb-MB fill before every call evicts L2 and the 256 MB MALL; the fill
@@ -176,6 +204,9 @@ def main():
 
     if args.copy_probe_mb:
         copy_probe(args.copy_probe_mb)
+        return
+    if args.read_probe_mb:
+        read_probe(args.read_probe_mb)
         return
     import lora_moe_amd as lm
     import synth
