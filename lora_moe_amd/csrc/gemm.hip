@@ -75,9 +75,10 @@ __device__ __forceinline__ float expand_dot(const float* __restrict__ z,
 //  * steady-state loads are unconditional (full chunks; the K remainder is
 //    one masked chunk at the end): a load under a branch makes the compiler
 //    drain all outstanding loads before it.
-// NWV = 8 for gate_up with 32-row tiles halves the row-fragment traffic per
-// weight byte again; the down GEMM keeps NWV = 4 (its grid is small: H
-// columns only, K-split instead).
+// NWV = 8 with 32-row tiles (gate_up and down) halves the row-fragment
+// traffic per weight byte again: with 4 wavefronts the dense layer's down GEMM
+// (32 real rows) fetched half a byte of h per weight byte and ran at 4 TB/s;
+// with 8 its time fell 64 -> 58 us.  16-row tiles keep NWV = 4.
 template <int MODE, int RF, int NWV>
 __global__ __launch_bounds__(64 * NWV) void grouped_gemm_kernel(GemmParams p) {
   constexpr int KC = 128;
@@ -234,7 +235,8 @@ __global__ __launch_bounds__(64 * NWV) void grouped_gemm_kernel(GemmParams p) {
 
 template <int MODE, int RF>
 void launch_rf(const GemmParams& gp, int64_t cap_rows, hipStream_t st) {
-  constexpr int NWV = MODE == 0 ? 4 * RF : 4;
+  // 8 wavefronts (128 weight rows) share each 32-row tile's staged fragments
+  constexpr int NWV = MODE == 0 ? 4 * RF : (RF == 2 ? 8 : 4);
   const int ncol = MODE == 0 ? (gp.I + NWV * 8 - 1) / (NWV * 8) : (gp.H + NWV * 16 - 1) / (NWV * 16);
   dim3 grid(ncol, (unsigned)((cap_rows + RF * 16 - 1) / (RF * 16)), MODE == 1 ? gp.ksplit : 1);
   grouped_gemm_kernel<MODE, RF, NWV><<<grid, NWV * 64, 0, st>>>(gp);
