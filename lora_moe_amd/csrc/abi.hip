@@ -85,7 +85,10 @@ int make_layout(const moe_lora_shape* s, Layout* L) {
   L->dsplit = 1;
   if (L->bm <= 64) {
     const int64_t tile_rows = L->bm >= 32 ? 32 : 16;
-    const int64_t tile_cols = L->bm >= 32 ? 128 : 64;  // 8 or 4 wavefronts of 16 columns
+    // the split count is sized for ~1024 workgroups of an estimated tile
+    // grid; at 16-row tiles it counts 64-column tiles (the measured best
+    // split at the decode shape), at 32-row tiles the kernel's 128 columns
+    const int64_t tile_cols = L->bm >= 32 ? 128 : 64;
     const int64_t tiles = ((L->H + tile_cols - 1) / tile_cols) * ((L->cap_rows + tile_rows - 1) / tile_rows);
     const int64_t chunks = std::max<int64_t>(1, L->I / 128);
     L->dsplit = (int)std::min<int64_t>(std::min<int64_t>(8, chunks), std::max<int64_t>(1, (1024 + tiles - 1) / tiles));

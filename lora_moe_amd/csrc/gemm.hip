@@ -75,15 +75,19 @@ __device__ __forceinline__ float expand_dot(const float* __restrict__ z,
 //  * steady-state loads are unconditional (full chunks; the K remainder is
 //    one masked chunk at the end): a load under a branch makes the compiler
 //    drain all outstanding loads before it.
-// NWV = 8 with 32-row tiles (gate_up and down) halves the row-fragment
-// traffic per weight byte again: with 4 wavefronts the dense layer's down GEMM
-// (32 real rows) fetched half a byte of h per weight byte and ran at 4 TB/s;
-// with 8 its time fell 64 -> 58 us.  16-row tiles keep NWV = 4.
+// NWV = 8 (gate_up with 32-row tiles, every down GEMM) halves the
+// row-fragment traffic per weight byte again: with 4 wavefronts the dense
+// layer's down GEMM (32 real rows) fetched half a byte of h per weight byte
+// and ran at 4 TB/s; with 8 its time fell 64 -> 58 us.  With 16-row tiles
+// and 8 wavefronts each thread stages 8 bytes instead of 16.
 template <int MODE, int RF, int NWV>
 __global__ __launch_bounds__(64 * NWV) void grouped_gemm_kernel(GemmParams p) {
   constexpr int KC = 128;
-  constexpr int XPT = RF * 4 / NWV;  // row-fragment pieces staged per thread per chunk
-  static_assert(XPT >= 1 && XPT * NWV == RF * 4, "row tile pieces must divide over the threads");
+  // row-fragment pieces staged per thread per chunk; with more threads than
+  // 16-byte pieces (16 rows, 8 wavefronts) each thread stages 8 bytes
+  constexpr bool HALF = RF * 4 < NWV;
+  constexpr int XPT = HALF ? 1 : RF * 4 / NWV;
+  static_assert(HALF ? RF * 8 == NWV : XPT * NWV == RF * 4, "row tile pieces must divide over the threads");
   __shared__ __attribute__((aligned(16))) uint16_t wl[NWV][16 * KC];
   __shared__ __attribute__((aligned(16))) uint16_t xl[2][RF * 16 * KC];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -114,9 +118,11 @@ __global__ __launch_bounds__(64 * NWV) void grouped_gemm_kernel(GemmParams p) {
   // 32 bits (checked on the host)
   int xr[XPT];
   uint32_t aoff[XPT];
+  const int xpiece = HALF ? (tid >> 1) & 15 : tid & 15;  // 16-byte piece of the chunk row
+  const int xhalf = HALF ? tid & 1 : 0;                  // its 8-byte half (HALF)
 #pragma unroll
   for (int j = 0; j < XPT; ++j) {
-    xr[j] = (tid >> 4) + j * 4 * NWV;
+    xr[j] = HALF ? tid >> 5 : (tid >> 4) + j * 4 * NWV;
     int row = row0 + xr[j];
     int pr = p.sorted[row];
     if (pr >= p.P) {  // padding row: read the tile's first row instead
@@ -143,6 +149,7 @@ __global__ __launch_bounds__(64 * NWV) void grouped_gemm_kernel(GemmParams p) {
   const int rot = nfull ? (int)((blockIdx.x * 7u + blockIdx.y * 3u) % (unsigned)nfull) : 0;
 
   u32x4_t rw[4], rx[XPT];
+  uint2 rxh;  // HALF: this thread's 8 bytes
   auto load = [&](int k0, bool masked) {
     const bool ok = !masked || piece * 8 < krem;
 #pragma unroll
@@ -150,7 +157,14 @@ __global__ __launch_bounds__(64 * NWV) void grouped_gemm_kernel(GemmParams p) {
       rw[i] = ok ? ld16_stream(Wexp + (woff[i] + (uint32_t)(kbase + k0 + piece * 8))) : zero4();
 #pragma unroll
     for (int j = 0; j < XPT; ++j)
-      rx[j] = ok ? ld16(p.in + (aoff[j] + (uint32_t)(kbase + k0 + piece * 8))) : zero4();
+    {
+      const bool okx = !masked || xpiece * 8 < krem;
+      if (HALF)
+        rxh = okx ? *reinterpret_cast<const uint2*>(p.in + (aoff[j] + (uint32_t)(kbase + k0 + xpiece * 8 + xhalf * 4)))
+                  : make_uint2(0u, 0u);
+      else
+        rx[j] = okx ? ld16(p.in + (aoff[j] + (uint32_t)(kbase + k0 + xpiece * 8))) : zero4();
+    }
   };
   int buf = 0;
   uint16_t* slice = wl[wave];
@@ -172,7 +186,10 @@ __global__ __launch_bounds__(64 * NWV) void grouped_gemm_kernel(GemmParams p) {
     uint16_t* xb = xl[buf];
 #pragma unroll
     for (int j = 0; j < XPT; ++j)
-      *reinterpret_cast<u32x4_t*>(&xb[xr[j] * KC + ((piece ^ (xr[j] & 15)) << 3)]) = rx[j];
+      if (HALF)
+        *reinterpret_cast<uint2*>(&xb[xr[j] * KC + ((xpiece ^ (xr[j] & 15)) << 3) + xhalf * 4]) = rxh;
+      else
+        *reinterpret_cast<u32x4_t*>(&xb[xr[j] * KC + ((xpiece ^ (xr[j] & 15)) << 3)]) = rx[j];
     buf ^= 1;
     if (next_kind) load(next_k0, next_kind == 2);
     lds_barrier();
@@ -233,13 +250,20 @@ __global__ __launch_bounds__(64 * NWV) void grouped_gemm_kernel(GemmParams p) {
     }
 }
 
-template <int MODE, int RF>
-void launch_rf(const GemmParams& gp, int64_t cap_rows, hipStream_t st) {
-  // 8 wavefronts (128 weight rows) share each 32-row tile's staged fragments
-  constexpr int NWV = MODE == 0 ? 4 * RF : (RF == 2 ? 8 : 4);
+template <int MODE, int RF, int NWV>
+void launch_nwv(const GemmParams& gp, int64_t cap_rows, hipStream_t st) {
   const int ncol = MODE == 0 ? (gp.I + NWV * 8 - 1) / (NWV * 8) : (gp.H + NWV * 16 - 1) / (NWV * 16);
   dim3 grid(ncol, (unsigned)((cap_rows + RF * 16 - 1) / (RF * 16)), MODE == 1 ? gp.ksplit : 1);
   grouped_gemm_kernel<MODE, RF, NWV><<<grid, NWV * 64, 0, st>>>(gp);
+}
+
+template <int MODE, int RF>
+void launch_rf(const GemmParams& gp, int64_t cap_rows, hipStream_t st) {
+  // 8 wavefronts (128 weight rows) share each tile's staged fragments, except
+  // gate_up's 16-row tiles (measured: 233 -> 236 us with 8 at the decode
+  // shape, while the down GEMM there went 120 -> 117 us)
+  constexpr int NWV = MODE == 0 ? 4 * RF : 8;
+  launch_nwv<MODE, RF, NWV>(gp, cap_rows, st);
 }
 
 }  // namespace
