@@ -62,24 +62,26 @@ __device__ __forceinline__ void stage_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <int BM_, int BK_, int NS_>
+template <int BM_, int BN_, int BK_, int NS_>
 struct DmaCfg {
-  static constexpr int BM = BM_, BN = BM_;    // square tiles
+  static constexpr int BM = BM_, BN = BN_;    // tile rows (pairs) and columns (weight rows)
   static constexpr int BK = BK_;              // K depth of one stage
   static constexpr int NS = NS_;              // stages in the LDS ring
   static constexpr int WN = BN / 64, NW = 2 * WN, NT = 64 * NW;  // wavefronts: 2 x WN
   static constexpr int MI = BM / 64, NI = 2;  // 32x32 blocks per wavefront
   static constexpr int CPR = BK / 8;          // 16-byte chunks per tile row
   static constexpr int PROW = BK * 2;         // bytes per tile row in LDS
-  static constexpr int TILE = BM * PROW;      // A and W tiles alike
-  static constexpr int STAGE = 2 * TILE;
+  static constexpr int ATILE = BM * PROW;     // A tile (rows x K slice)
+  static constexpr int WTILE = BN * PROW;     // W tile (weight rows x K slice)
+  static constexpr int STAGE = ATILE + WTILE;
   static constexpr int RING = NS * STAGE;
   static constexpr int LDS = RING + 2 * BM * 4;  // ring + per-row validity and top-k weight
-  static constexpr int WROWS = BM / NW;           // tile rows each wavefront copies (32)
   static constexpr int ROWS_PER_COPY = 1024 / PROW;
-  static constexpr int NC = WROWS / ROWS_PER_COPY;  // 1 KB copies per wavefront per operand per stage
+  static constexpr int AROWS = BM / NW, WROWS = BN / NW;  // tile rows each wavefront copies
+  static constexpr int NCA = AROWS / ROWS_PER_COPY;       // 1 KB copies per wavefront per stage: A
+  static constexpr int NCW = WROWS / ROWS_PER_COPY;       // and W
   static_assert(BK == 32 || BK == 64, "stage depth");
-  static_assert(WROWS == 32, "copy layout");
+  static_assert(NCA >= 1 && NCA * ROWS_PER_COPY == AROWS && NCW * ROWS_PER_COPY == WROWS, "copy layout");
   static_assert(LDS <= 160 * 1024, "LDS ring exceeds 160 KB");
   static_assert(NS >= 2, "ring needs two stages");
 
@@ -93,8 +95,9 @@ struct DmaCfg {
 
 template <int MODE, class C, int WAVES_PER_SIMD>
 __global__ __launch_bounds__(C::NT, WAVES_PER_SIMD) void grouped_gemm_dma_kernel(GemmParams p) {
-  constexpr int BM = C::BM, BN = C::BN, BK = C::BK, NS = C::NS, MI = C::MI, NI = C::NI, NC = C::NC;
-  constexpr int WROWS = C::WROWS, RPC = C::ROWS_PER_COPY, CPR = C::CPR, PROW = C::PROW;
+  constexpr int BM = C::BM, BN = C::BN, BK = C::BK, NS = C::NS, MI = C::MI, NI = C::NI;
+  constexpr int NCA = C::NCA, NCW = C::NCW, AROWS = C::AROWS, WROWS = C::WROWS;
+  constexpr int RPC = C::ROWS_PER_COPY, CPR = C::CPR, PROW = C::PROW;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -130,24 +133,31 @@ __global__ __launch_bounds__(C::NT, WAVES_PER_SIMD) void grouped_gemm_dma_kernel
     return min(ntc * BN + c, p.N - 1);
   };
 
-  // Copies: wavefront w fills tile rows [32w, 32w+32) of A and of W, NC
-  // copies of RPC rows each; lane l lands at row R0 + l / CPR, slot l % CPR,
-  // which holds logical chunk lchunk.
+  // Copies: wavefront w fills A tile rows [AROWS w, AROWS (w+1)) and W tile
+  // rows [WROWS w, WROWS (w+1)), NCA and NCW copies of RPC rows each; lane l
+  // lands at row R0 + l / CPR, slot l % CPR, which holds logical chunk
+  // alchunk / wlchunk.
   const int lrow = lane / CPR, lslot = lane % CPR;
-  uint32_t a_off[NC];  // byte offsets into the A buffer (x or h)
-  const uint16_t* b_src[NC];
-  int lchunk[NC];
+  uint32_t a_off[NCA];  // byte offsets into the A buffer (x or h)
+  int alchunk[NCA];
+  const uint16_t* b_src[NCW];
+  int wlchunk[NCW];
   const uint16_t* Wexp = p.W + (size_t)e * p.N * p.K;
   const buf_rsrc_t a_rs = make_rsrc(p.in, p.in_bytes);
 #pragma unroll
-  for (int i = 0; i < NC; ++i) {
-    const int r = wave * WROWS + i * RPC + lrow;
-    lchunk[i] = C::swz(r, lslot);  // the swizzle is an involution
+  for (int i = 0; i < NCA; ++i) {
+    const int r = wave * AROWS + i * RPC + lrow;
+    alchunk[i] = C::swz(r, lslot);  // the swizzle is an involution
     const int grow = row0 + r;
     const int pr = p.sorted[grow];
     const int arow = MODE == 0 ? pr / p.topk : grow;  // x row of the token, or the h row
-    a_off[i] = pr < p.P ? (uint32_t)(arow * p.K + lchunk[i] * 8) * 2u : kBufNone;
-    b_src[i] = Wexp + (size_t)tile_col(r) * p.K + lchunk[i] * 8;
+    a_off[i] = pr < p.P ? (uint32_t)(arow * p.K + alchunk[i] * 8) * 2u : kBufNone;
+  }
+#pragma unroll
+  for (int i = 0; i < NCW; ++i) {
+    const int r = wave * WROWS + i * RPC + lrow;
+    wlchunk[i] = C::swz(r, lslot);
+    b_src[i] = Wexp + (size_t)tile_col(r) * p.K + wlchunk[i] * 8;
   }
 
   const int ntile = (p.K + BK - 1) / BK;  // the last stage may be partial
@@ -155,30 +165,41 @@ __global__ __launch_bounds__(C::NT, WAVES_PER_SIMD) void grouped_gemm_dma_kernel
   auto issue = [&](int s, auto nt_c) {
     constexpr bool NTL = decltype(nt_c)::value;
     char* A = smem + (s % NS) * C::STAGE;
-    char* B = A + C::TILE;
+    char* B = A + C::ATILE;
     const int k0 = s * BK;
-#pragma unroll
-    for (int i = 0; i < NC; ++i) {
-      const int k = k0 + lchunk[i] * 8;
-      const int koff = k < p.K ? k0 : p.K - 8 - lchunk[i] * 8;  // clamped: a valid address
-      const int roff = (wave * WROWS + i * RPC) * PROW;
+    auto ldA = [&](int i) {
+      const int k = k0 + alchunk[i] * 8;
+      const int koff = k < p.K ? k0 : p.K - 8 - alchunk[i] * 8;  // clamped: a valid address
+      const int roff = (wave * AROWS + i * RPC) * PROW;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rs, (lds_char*)(A + roff), 16, (int)(a_off[i] + (uint32_t)koff * 2u), 0, 0, 0);
+    };
+    auto ldW = [&](int i) {
+      const int k = k0 + wlchunk[i] * 8;
+      const int koff = k < p.K ? k0 : p.K - 8 - wlchunk[i] * 8;
+      const int roff = (wave * WROWS + i * RPC) * PROW;
       // cache policy operand 2: non-temporal
       __builtin_amdgcn_global_load_lds((const void*)(b_src[i] + koff), (lds_char*)(B + roff), 16, 0, NTL ? 2 : 0);
-    }
+    };
+    // all A copies of the stage, then all W copies: at 256 x 256 this order
+    // ran the Qwen3-MoE-like gate_up in 273 us against 283 us with each A
+    // copy followed by its W copy (three alternating runs on one box)
+#pragma unroll
+    for (int i = 0; i < NCA; ++i) ldA(i);
+#pragma unroll
+    for (int i = 0; i < NCW; ++i) ldW(i);
   };
   // zero this lane's chunks of stage s that lie beyond K (after they landed)
   auto zero_tail = [&](int s) {
     char* A = smem + (s % NS) * C::STAGE;
-    char* B = A + C::TILE;
+    char* B = A + C::ATILE;
 #pragma unroll
-    for (int i = 0; i < NC; ++i) {
-      if (s * BK + lchunk[i] * 8 >= p.K) {
-        const int o = (wave * WROWS + i * RPC + lrow) * PROW + lslot * 16;
-        *reinterpret_cast<u32x4_t*>(A + o) = zero4();
-        *reinterpret_cast<u32x4_t*>(B + o) = zero4();
-      }
-    }
+    for (int i = 0; i < NCA; ++i)
+      if (s * BK + alchunk[i] * 8 >= p.K)
+        *reinterpret_cast<u32x4_t*>(A + (wave * AROWS + i * RPC + lrow) * PROW + lslot * 16) = zero4();
+#pragma unroll
+    for (int i = 0; i < NCW; ++i)
+      if (s * BK + wlchunk[i] * 8 >= p.K)
+        *reinterpret_cast<u32x4_t*>(B + (wave * WROWS + i * RPC + lrow) * PROW + lslot * 16) = zero4();
   };
 
   f32x16_t acc[MI][NI];
@@ -201,7 +222,7 @@ __global__ __launch_bounds__(C::NT, WAVES_PER_SIMD) void grouped_gemm_dma_kernel
   u32x4_t af[2][MI], bf[2][NI];
   auto frag = [&](int s, int kk, int set) {
     const char* A = smem + (s % NS) * C::STAGE;
-    const char* B = A + C::TILE;
+    const char* B = A + C::ATILE;
     const int ch = 2 * kk + khalf;
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
@@ -237,7 +258,7 @@ __global__ __launch_bounds__(C::NT, WAVES_PER_SIMD) void grouped_gemm_dma_kernel
   // the barrier together with the first fragment reads of the next stage,
   // must not wait for those reads.
   constexpr int KK = BK / 16;  // MFMA K slices per stage (even)
-  constexpr int VM_AHEAD = 2 * NC * (NS - 2) < 63 ? 2 * NC * (NS - 2) : 63;
+  constexpr int VM_AHEAD = (NCA + NCW) * (NS - 2) < 63 ? (NCA + NCW) * (NS - 2) : 63;
   auto kloop = [&](auto live_c, auto nt_c) {
     constexpr bool LIVE = decltype(live_c)::value;
     // prologue: every ring slot gets a stage; wait for stage 0
@@ -365,7 +386,7 @@ int launch_dma(const GemmParams& gp_in, int mode, int64_t cap_rows, hipStream_t 
 
 // 256 x 256 tiles, 8 wavefronts, two 64-deep stages (128 KB of LDS)
 int launch_gemm_prefill(const GemmParams& gp, int mode, int64_t cap_rows, hipStream_t st) {
-  return launch_dma<DmaCfg<256, 64, 2>, 2>(gp, mode, cap_rows, st);
+  return launch_dma<DmaCfg<256, 256, 64, 2>, 2>(gp, mode, cap_rows, st);
 }
 
 // 128 x 128 tiles, 4 wavefronts, two 64-deep stages (64 KB of LDS, two
@@ -373,7 +394,7 @@ int launch_gemm_prefill(const GemmParams& gp, int mode, int64_t cap_rows, hipStr
 // three workgroups per CU and a 4-stage ring with two: the 64-deep stages win
 // (16-byte chunks of 128-byte row pieces instead of 64-byte ones).
 int launch_gemm_dma128(const GemmParams& gp, int mode, int64_t cap_rows, hipStream_t st) {
-  return launch_dma<DmaCfg<128, 64, 2>, 2>(gp, mode, cap_rows, st);
+  return launch_dma<DmaCfg<128, 128, 64, 2>, 2>(gp, mode, cap_rows, st);
 }
 
 }  // namespace moelora
