@@ -40,9 +40,15 @@ def _sparse_pm1(rng, shape, per_row):
     return out
 
 
-def make(seed: int = 5) -> synth.Inputs:
+# shapes of the bit-exact test: K multiple of 64 and rank 16; then K with a
+# remainder (1000 = 15*64 + 40, 520 = 8*64 + 8) and a rank that is not a
+# multiple of 16 (24), which exercise the masked K tails and rank columns
+SHAPES = {"even": dict(H=1024, I=512, r=16), "ragged": dict(H=1000, I=520, r=24)}
+
+
+def make(seed: int = 5, shape: str = "even") -> synth.Inputs:
     """The workload's routing and adapter ids, with integer data and weights."""
-    wl = EXACT_WL
+    wl = replace(EXACT_WL, **SHAPES[shape])
     base = synth.make_inputs(wl)
     rng = np.random.default_rng(seed)
     T, H, I, E, L, r = wl.T, wl.H, wl.I, wl.E, wl.L, wl.r

@@ -16,8 +16,9 @@ def orc():
     return oracle.Oracle()
 
 
-def test_exact_inputs_premise(orc):
-    inp = exact_inputs.make()
+@pytest.mark.parametrize("shape", sorted(exact_inputs.SHAPES))
+def test_exact_inputs_premise(orc, shape):
+    inp = exact_inputs.make(shape=shape)
     x = pins.f64(inp.x)
     assert np.all(x[:, 0] == exact_inputs.GATE)
     assert np.all(np.abs(x[:, 1:]) <= 1)

@@ -222,17 +222,18 @@ def test_shrink_stage_matches_reference():
     assert checked > 20
 
 
+@pytest.mark.parametrize("shape", ["even", "ragged"])
 @pytest.mark.parametrize("bm", [0, 16, 32, 64, 128, 256])
-def test_exact_small_integer_layer(bm):
+def test_exact_small_integer_layer(bm, shape):
     """Small-integer inputs make every intermediate exact (exact_inputs.py):
     the layer output must equal the exact values the fp64 reference gives
     (exact_inputs.exact) bit for bit, with and without adapters, in every GEMM family and through the
     split-K shrinks' atomics."""
     import lora_moe_amd as lm
     import exact_inputs
-    inp = exact_inputs.make()
+    inp = exact_inputs.make(shape=shape)
     wl = inp.wl
-    log(f"exact integers bm={bm}: T={wl.T} H={wl.H} I={wl.I} E={wl.E} k={wl.topk} L={wl.L} r={wl.r}")
+    log(f"exact integers ({shape}) bm={bm}: T={wl.T} H={wl.H} I={wl.I} E={wl.E} k={wl.topk} L={wl.L} r={wl.r}")
     dev = to_device(inp)
     y, shape, ws = run_gpu(dev, wl, bm)
     assert lm.moe_lora_device_errors(shape, ws) == 0
