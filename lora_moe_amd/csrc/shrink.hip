@@ -11,7 +11,7 @@
 // every row as contiguous 32-byte pieces per lane.
 //
 // One work item = (tile of <= 16*RFS rows of one (expert, adapter) segment,
-// K split).  A workgroup of 4 wavefronts walks the split's 64-wide K steps
+// K split, block of z columns: all r, or 16 when work items are few).  A workgroup of 4 wavefronts walks the split's 64-wide K steps
 // interleaved by wavefront, issuing the loads of 2 or 4 of its steps before
 // their MFMAs; each wavefront accumulates the whole tile
 // [16*RFS x 16*NFR] with bf16 MFMA 16x16x32.  The four partial tiles are added
@@ -35,6 +35,7 @@ struct ShrinkParams {
   const int32_t* hdr;
   float* z;            // [cap_rows][r]
   int K, E, r, topk, splits, steps_per_split, nsteps, use_atomic;
+  int ncb, cpb;        // column blocks per tile, z columns per block
 };
 
 // U = K steps of one wavefront whose loads are issued together before their
@@ -48,10 +49,12 @@ __global__ __launch_bounds__(256) void lora_shrink_kernel(ShrinkParams p) {
   __shared__ float red[2][RFS * 16][NFR * 16 + 1];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int m = lane & 15, kq = lane >> 4;
-  const int nitems = p.hdr[HDR_NTILES] * p.splits;
+  const int nitems = p.hdr[HDR_NTILES] * p.splits * p.ncb;
 
   for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
-    const int ti = item / p.splits, sp = item - ti * p.splits;
+    const int cb = item % p.ncb, rest = item / p.ncb;
+    const int ti = rest / p.splits, sp = rest - ti * p.splits;
+    const int q0 = cb * p.cpb;  // first z column of this item
     const LoraTile tl = p.tiles[ti];
 
     const uint16_t* arow[RFS];
@@ -68,7 +71,7 @@ __global__ __launch_bounds__(256) void lora_shrink_kernel(ShrinkParams p) {
     const uint16_t* brow[NFR];
 #pragma unroll
     for (int nf = 0; nf < NFR; ++nf) {
-      const int q = min(nf * 16 + m, p.r - 1);  // columns past r repeat a valid one
+      const int q = min(q0 + nf * 16 + m, p.r - 1);  // columns past r repeat a valid one
       brow[nf] = p.A + (((size_t)tl.l * p.E + tl.e) * p.r + q) * p.K;
     }
 
@@ -151,9 +154,9 @@ __global__ __launch_bounds__(256) void lora_shrink_kernel(ShrinkParams p) {
         for (int nf = 0; nf < NFR; ++nf)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int row = rf * 16 + 4 * kq + i, q = nf * 16 + m;
-            if (row < tl.n && q < p.r) {
-              const float v = acc[rf][nf][i] + red[0][row][q];
+            const int row = rf * 16 + 4 * kq + i, q = q0 + nf * 16 + m;
+            if (row < tl.n && q < p.r && q < q0 + p.cpb) {
+              const float v = acc[rf][nf][i] + red[0][row][nf * 16 + m];
               float* dst = p.z + (size_t)(tl.row0 + row) * p.r + q;
               if (p.use_atomic)
                 __hip_atomic_fetch_add(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -187,7 +190,7 @@ void launch_t(const ShrinkParams& sp, bool even, int grid, hipStream_t st) {
 
 template <int MODE, int RFS>
 void launch_nfr(const ShrinkParams& sp, bool even, int grid, hipStream_t st) {
-  switch ((sp.r + 15) / 16) {
+  switch ((sp.cpb + 15) / 16) {
     case 1: launch_t<MODE, RFS, 1>(sp, even, grid, st); break;
     case 2: launch_t<MODE, RFS, 2>(sp, even, grid, st); break;
     case 3: launch_t<MODE, RFS, 3>(sp, even, grid, st); break;
@@ -207,19 +210,32 @@ static int shrink_row_frags(const Layout& L) {
   return (int)(L.TS / 16);
 }
 
+// Expected number of shrink tiles: at most one per touched (expert, adapter)
+// segment plus one per TS adapter rows.
+static int64_t shrink_tiles_est(const Layout& L) {
+  return std::max<int64_t>(1, std::min<int64_t>(L.max_tiles, std::min<int64_t>(L.P, (int64_t)L.E * L.L)));
+}
+
+// Blocks of z columns per tile, each a work item of its own.  With few work
+// items (under 4 per CU) each tile's columns become items of 16 columns,
+// reading their own rows of A (A is [r][K]) and the tile's x rows again: the
+// CUs that drew two whole tiles bound the kernel, and at the GPT-OSS-like
+// shape (364 tiles, r = 32) the two shrinks went 21.4 + 22.0 -> 18.7 + 20.0 us.
+static int shrink_col_blocks(const Layout& L, int splits) {
+  return (L.r % 16 == 0 && shrink_tiles_est(L) * splits < 1024) ? L.r / 16 : 1;
+}
+
 ShrinkPlan plan_shrink(const Layout& L, int K) {
   ShrinkPlan sp;
   const int nsteps = (K + 63) / 64;
-  // expected number of shrink tiles: at most one per touched (expert, adapter)
-  // segment plus one per TS adapter rows
-  const int64_t est = std::max<int64_t>(1, std::min<int64_t>(L.max_tiles, std::min<int64_t>(L.P, (int64_t)L.E * L.L)));
+  const int64_t est = shrink_tiles_est(L);
   // K splits only while the tiles alone leave the chip short of work: with
   // 384 or more tiles (1.5 per CU) a single split measured as fast or faster
   // (no atomics, and the align then has no accumulators to clear)
   int splits = est >= 384 ? 1 : (int)std::max<int64_t>(1, 2048 / est);
   splits = std::min(splits, std::max(1, nsteps / 4));  // >= 4 steps: one per wavefront
   sp.splits = splits;
-  const int64_t items = L.max_tiles * splits;
+  const int64_t items = L.max_tiles * splits * shrink_col_blocks(L, splits);
   sp.grid = (int)std::max<int64_t>(1, std::min<int64_t>(items, 4096));
   return sp;
 }
@@ -244,6 +260,8 @@ int launch_shrink(const Layout& L, int mode, const uint16_t* in, const uint16_t*
   sp.nsteps = (K + 63) / 64;
   sp.steps_per_split = (sp.nsteps + pl.splits - 1) / pl.splits;
   sp.use_atomic = pl.splits > 1;
+  sp.ncb = shrink_col_blocks(L, pl.splits);
+  sp.cpb = L.r / sp.ncb;
   const bool even = (K % 64) == 0;
   const int rfs = shrink_row_frags(L);
   if (mode == 0) {
