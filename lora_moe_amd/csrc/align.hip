@@ -105,10 +105,20 @@ __device__ __forceinline__ void write_pads_and_blocks(int32_t* __restrict__ sort
                                                       const int* n, int E, int P, int bm,
                                                       int64_t cap_rows, int64_t cap_blocks) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  for (int e = wave; e < E; e += nw) {
-    const int a = eoff[e], b = eoff[e + 1];
-    for (int row = a + n[e] + lane; row < b; row += 64) sorted[row] = P;
-    for (int blk = a / bm + lane; blk < b / bm; blk += 64) bexp[blk] = e;
+  if (nw == 1) {
+    // one wavefront: a lane per expert, so the experts' LDS reads overlap
+    // instead of following one another (decode align 8.2 -> 7.1 us)
+    for (int e = lane; e < E; e += 64) {
+      const int a = eoff[e], b = eoff[e + 1];
+      for (int row = a + n[e]; row < b; ++row) sorted[row] = P;
+      for (int blk = a / bm; blk < b / bm; ++blk) bexp[blk] = e;
+    }
+  } else {
+    for (int e = wave; e < E; e += nw) {
+      const int a = eoff[e], b = eoff[e + 1];
+      for (int row = a + n[e] + lane; row < b; row += 64) sorted[row] = P;
+      for (int blk = a / bm + lane; blk < b / bm; blk += 64) bexp[blk] = e;
+    }
   }
   const int num_padded = eoff[E];
   for (int64_t row = num_padded + threadIdx.x; row < cap_rows; row += blockDim.x) sorted[row] = P;
