@@ -66,7 +66,7 @@ def stage_bytes_flops(wl, work):
 def kernel_sources(stage: str, block_m: int) -> list:
     """Source files the kernel of `stage` is built from at this block_m."""
     if stage.startswith("gemm"):
-        fam = ["gemm.hip"] if block_m <= 64 else ["gemm_dma.hip", "gemm_expand.h"]
+        fam = ["gemm.hip"] if block_m <= 32 else ["gemm_dma.hip", "gemm_expand.h"]
     elif stage.startswith("shrink"):
         fam = ["shrink.hip"]
     elif stage.startswith("align"):

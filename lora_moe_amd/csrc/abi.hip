@@ -40,16 +40,18 @@ static int resolve_bm(const moe_lora_shape* s) {
   const int64_t touched = std::max<int64_t>(1, std::min<int64_t>(s->E, P));
   const int64_t rows = (P + touched - 1) / touched;
   // up to ~24 rows per expert the weight stream dominates (streaming GEMM
-  // family); up to a few dozen a 128-row tile reads each expert's weights
-  // once (LDS-tiled family); beyond that the 256 x 256 tiles, which read the
-  // gathered x rows half as often per column (padding rows cost no traffic)
-  // and each expert's weights once per 256 rows
+  // family); up to a few dozen a 64- or 128-row tile reads each expert's
+  // weights once (LDS-tiled family: 64 rows while the expert's rows fit with
+  // a third to spare for uneven routing); beyond that the 256 x 256 tiles,
+  // which read the gathered x rows half as often per column (padding rows
+  // cost no traffic) and each expert's weights once per 256 rows
   if (rows <= 16) return 16;
   if (rows <= 24) return 32;
   // few experts with wide weights (dense layers): the tiled grids would be
   // too small to fill the GPU (the down projection has one 128-column tile
   // per expert and 128 output columns), so stream instead
   if (touched * ((s->H + 127) / 128) < 512) return 32;
+  if (rows <= 48) return 64;
   if (rows < 96) return 128;
   return 256;
 }
@@ -83,7 +85,7 @@ int make_layout(const moe_lora_shape* s, Layout* L) {
   // small (few experts with wide weights, e.g. dense layers): each split
   // writes its own partial slab of d and the combine adds the slabs in order.
   L->dsplit = 1;
-  if (L->bm <= 64) {
+  if (L->bm <= 32) {
     const int64_t tile_rows = L->bm >= 32 ? 32 : 16;
     // the split count is sized for ~1024 workgroups of an estimated tile
     // grid; at 16-row tiles it counts 64-column tiles (the measured best

@@ -17,11 +17,11 @@
 //   epilogue adds the expand (first split only) and multiplies by the pair's
 //   top-k weight; d is stored fp32, one slab per K split.
 //
-// This family serves small row counts per expert (block_m <= 64, decode):
+// This family serves small row counts per expert (block_m <= 32, decode):
 // every weight byte is used by one row tile only, so the kernel is a weight
 // stream and is organised around HBM efficiency -- see the kernel comment.
 // Row tiles hold 16 or 32 rows of a single expert (expert runs are padded to
-// block_m, a multiple of the tile).
+// block_m, the tile's row count).
 #include "device_util.h"
 #include "internal.h"
 
@@ -311,7 +311,12 @@ int launch_gemm(const Layout& L, int mode, const uint16_t* in, const int32_t* lo
     if (rc) return rc;
     return hipGetLastError() == hipSuccess ? MOE_LORA_OK : MOE_LORA_EHIP;
   }
-  // 16- or 32-row tiles (a 64-row block is two tiles of one expert)
+  if (L.bm == 64) {
+    const int rc = launch_gemm_dma64(gp, mode, L.cap_rows, st);
+    if (rc) return rc;
+    return hipGetLastError() == hipSuccess ? MOE_LORA_OK : MOE_LORA_EHIP;
+  }
+  // 16- or 32-row tiles
   const int RF = L.bm >= 32 ? 2 : 1;
   if (mode == 0) {
     if (RF == 2) launch_rf<0, 2>(gp, L.cap_rows, st);

@@ -1,5 +1,6 @@
-// Grouped GEMM with LDS-DMA staging for batches with many rows per expert:
-// square tiles of 128 x 128 (block_m = 128) or 256 x 256 (block_m = 256).
+// Grouped GEMM with LDS-DMA staging for batches with dozens of rows per
+// expert or more: tiles of 64 x 128 (block_m = 64), 128 x 128 (block_m = 128)
+// or 256 x 256 (block_m = 256).
 //
 // Same contract as the register-streaming family in gemm.hip (one GEMM per
 // expert over its sorted rows; the LoRA expand z * B added to the base output
@@ -395,6 +396,15 @@ int launch_gemm_prefill(const GemmParams& gp, int mode, int64_t cap_rows, hipStr
 // (16-byte chunks of 128-byte row pieces instead of 64-byte ones).
 int launch_gemm_dma128(const GemmParams& gp, int mode, int64_t cap_rows, hipStream_t st) {
   return launch_dma<DmaCfg<128, 128, 64, 2>, 2>(gp, mode, cap_rows, st);
+}
+
+// 64 x 128 tiles, 4 wavefronts of 32 x 64 outputs, two 64-deep stages (48 KB
+// of LDS, three workgroups per CU).  At ~32 rows per expert (GPT-OSS-like
+// shape) this ran gate_up in 208-211 us and down in 105-106 us against
+// 234-239 and 140-142 us for the 128 x 128 tiles, whose second half of rows
+// is padding; a 3-stage ring (two workgroups per CU) ran down in 129-130 us.
+int launch_gemm_dma64(const GemmParams& gp, int mode, int64_t cap_rows, hipStream_t st) {
+  return launch_dma<DmaCfg<64, 128, 64, 2>, 3>(gp, mode, cap_rows, st);
 }
 
 }  // namespace moelora

@@ -171,7 +171,7 @@ def test_edge_cases():
     assert lm.moe_lora_device_errors(shape, ws) == 4
 
 
-@pytest.mark.parametrize("bm", [0, 32, 128, 256])
+@pytest.mark.parametrize("bm", [0, 32, 64, 128, 256])
 def test_routing_extremes(bm):
     """Every token to every expert (topk = E), and every token to one expert
     (several row tiles of one expert, the others untouched)."""
@@ -186,7 +186,7 @@ def test_routing_extremes(bm):
 
 
 @pytest.mark.parametrize("T,E,L", [(200, 4, 100), (600, 64, 200)])
-@pytest.mark.parametrize("bm", [0, 32, 128, 256])
+@pytest.mark.parametrize("bm", [0, 32, 64, 128, 256])
 def test_more_than_64_adapters(T, E, L, bm):
     """L > 64 adapters: the tiled expand scans adapter ids 64 at a time; the
     align's (expert, slot) table has E x (L + 1) buckets (12864 at E = 64,
