@@ -102,6 +102,8 @@ def measured_traffic(kernel: str, workload: str, block_m: int):
             vals[k.strip()] = v.strip()
     if vals.get("kernel_source_sha") != kernel_source_sha(kernel, block_m):
         return None
+    if vals.get("block_m") != str(block_m):  # counted at another tile size
+        return None
     try:
         return float(vals["traffic_bytes_per_launch"])
     except (KeyError, ValueError):

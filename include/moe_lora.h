@@ -63,7 +63,7 @@ typedef struct moe_lora_shape {
   int32_t L;        /* adapters resident in the A/B stacks (>= 1)                 */
   int32_t r;        /* adapter rank                                               */
   int32_t block_m;  /* rows per block shared by every op of the layer: one of     */
-                    /* 16, 32, 64, 128, 256, or 0 to choose it from the shape     */
+                    /* 16, 32, 64, 128, 192, 256, or 0 to choose it from shape    */
   float lora_scale; /* s above                                                    */
 } moe_lora_shape;
 
@@ -110,7 +110,8 @@ typedef struct {
  * provided that distance is at most max_dist (max_dist <= 0: no limit) and
  * the shape's workspace layout is valid with that block_m; otherwise the
  * built-in choice (moe_lora_resolve_block_m).  Entries with a block_m
- * outside {16, 32, 64, 128, 256} or a non-positive key field are skipped.
+ * outside {16, 32, 64, 128, 192, 256} or a non-positive key field are
+ * skipped.
  * table may be NULL when n == 0.  Returns a negative status when the shape
  * is invalid.  Host only, pure: the table is read, not kept. */
 int moe_lora_tune_block_m(const moe_lora_shape* shape, const moe_lora_tune_entry* table, int32_t n,

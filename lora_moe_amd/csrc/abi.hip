@@ -16,7 +16,7 @@ static int check_shape(const moe_lora_shape* s) {
       s->L <= 0 || s->r <= 0)
     return MOE_LORA_EINVAL;
   const int bm = s->block_m;
-  if (!(bm == 0 || bm == 16 || bm == 32 || bm == 64 || bm == 128 || bm == 256)) return MOE_LORA_EINVAL;
+  if (!(bm == 0 || bm == 16 || bm == 32 || bm == 64 || bm == 128 || bm == 192 || bm == 256)) return MOE_LORA_EINVAL;
   if (s->H % 8 || s->I % 8) return MOE_LORA_EALIGN;
   if (s->r % 8 || s->r > 128) return MOE_LORA_EUNSUPPORTED;
   if ((int64_t)s->E * (s->L + 1) > kAlignMaxBuckets) return MOE_LORA_EUNSUPPORTED;
@@ -40,11 +40,13 @@ static int resolve_bm(const moe_lora_shape* s) {
   const int64_t touched = std::max<int64_t>(1, std::min<int64_t>(s->E, P));
   const int64_t rows = (P + touched - 1) / touched;
   // up to ~24 rows per expert the weight stream dominates (streaming GEMM
-  // family); up to a few dozen a 64- or 128-row tile reads each expert's
-  // weights once (LDS-tiled family: 64 rows while the expert's rows fit with
-  // a third to spare for uneven routing); beyond that the 256 x 256 tiles,
-  // which read the gathered x rows half as often per column (padding rows
-  // cost no traffic) and each expert's weights once per 256 rows
+  // family); beyond that an LDS-tiled GEMM whose row tile holds an expert's
+  // rows with about a third to spare for uneven routing (64 rows up to 48,
+  // 192 rows up to 144), so that each expert's weights are read once and no
+  // wavefront holds only padding rows; 128 rows in between; from ~150 rows
+  // the 256 x 256 tiles, which read the gathered x rows half as often per
+  // column (padding rows cost no traffic) and each expert's weights once per
+  // 256 rows
   if (rows <= 16) return 16;
   if (rows <= 24) return 32;
   // few experts with wide weights (dense layers): the tiled grids would be
@@ -53,6 +55,7 @@ static int resolve_bm(const moe_lora_shape* s) {
   if (touched * ((s->H + 127) / 128) < 512) return 32;
   if (rows <= 48) return 64;
   if (rows < 96) return 128;
+  if (rows <= 144) return 192;
   return 256;
 }
 
@@ -185,7 +188,7 @@ int moe_lora_tune_block_m(const moe_lora_shape* shape, const moe_lora_tune_entry
   for (int32_t i = 0; table && i < n; ++i) {
     const moe_lora_tune_entry& t = table[i];
     const int bm = t.block_m;
-    if (bm != 16 && bm != 32 && bm != 64 && bm != 128 && bm != 256) continue;
+    if (bm != 16 && bm != 32 && bm != 64 && bm != 128 && bm != 192 && bm != 256) continue;
     const int32_t ek[6] = {t.rows_per_expert, t.H, t.I, t.E, t.r, t.L};
     double d = 0.0;
     bool ok = true;

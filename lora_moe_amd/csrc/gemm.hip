@@ -301,6 +301,11 @@ int launch_gemm(const Layout& L, int mode, const uint16_t* in, const int32_t* lo
   gp.ksplit = mode == 1 ? L.dsplit : 1;
   gp.d_slab = L.cap_rows * (int64_t)L.H;
   gp.s = L.s;
+  if (L.bm == 192) {
+    const int rc = launch_gemm_dma192(gp, mode, L.cap_rows, st);
+    if (rc) return rc;
+    return hipGetLastError() == hipSuccess ? MOE_LORA_OK : MOE_LORA_EHIP;
+  }
   if (L.bm >= 256) {
     const int rc = launch_gemm_prefill(gp, mode, L.cap_rows, st);
     if (rc) return rc;

@@ -1,6 +1,6 @@
 // Grouped GEMM with LDS-DMA staging for batches with dozens of rows per
-// expert or more: tiles of 64 x 128 (block_m = 64), 128 x 128 (block_m = 128)
-// or 256 x 256 (block_m = 256).
+// expert or more: tiles of 64 x 128 (block_m = 64), 128 x 128 (block_m =
+// 128), 192 x 256 (block_m = 192) or 256 x 256 (block_m = 256).
 //
 // Same contract as the register-streaming family in gemm.hip (one GEMM per
 // expert over its sorted rows; the LoRA expand z * B added to the base output
@@ -413,6 +413,16 @@ int launch_gemm_prefill(const GemmParams& gp, int mode, int64_t cap_rows, hipStr
 // (16-byte chunks of 128-byte row pieces instead of 64-byte ones).
 int launch_gemm_dma128(const GemmParams& gp, int mode, int64_t cap_rows, hipStream_t st) {
   return launch_dma<DmaCfg<128, 128, 64, 2>, 2>(gp, mode, cap_rows, st);
+}
+
+// 192 x 256 tiles, 8 wavefronts of 96 x 64 outputs, two 64-deep stages (113
+// KB of LDS, one workgroup per CU).  At ~128 rows per expert (Qwen3-MoE-like
+// shape: 101-160) every expert fits one tile and no wavefront is all
+// padding; the layer ran 0.572-0.573 ms against 0.596 ms with 256 x 256
+// tiles (two alternating runs on one box).  At the DeepSeek-like shape it was
+// slower (9.24 against 9.01 ms).
+int launch_gemm_dma192(const GemmParams& gp, int mode, int64_t cap_rows, hipStream_t st) {
+  return launch_dma<DmaCfg<192, 256, 64, 2>, 2>(gp, mode, cap_rows, st);
 }
 
 // 64 x 128 tiles, 4 wavefronts of 32 x 64 outputs, two 64-deep stages (48 KB

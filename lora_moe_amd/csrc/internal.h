@@ -168,6 +168,7 @@ int launch_gemm(const Layout& L, int mode, const uint16_t* x, const int32_t* lor
 int launch_gemm_prefill(const GemmParams& gp, int mode, int64_t cap_rows, hipStream_t st);
 int launch_gemm_dma128(const GemmParams& gp, int mode, int64_t cap_rows, hipStream_t st);
 int launch_gemm_dma64(const GemmParams& gp, int mode, int64_t cap_rows, hipStream_t st);
+int launch_gemm_dma192(const GemmParams& gp, int mode, int64_t cap_rows, hipStream_t st);
 
 int launch_combine(const Layout& L, void* ws, uint16_t* y, hipStream_t st);
 

@@ -18,7 +18,7 @@ import os
 import statistics
 import sys
 
-CANDIDATES = (16, 32, 64, 128, 256)
+CANDIDATES = (16, 32, 64, 128, 192, 256)
 
 
 def time_layer(lm, shape, dev, y, iters: int, warmup: int) -> float:

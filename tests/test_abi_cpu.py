@@ -51,8 +51,8 @@ def test_workspace_and_block_m(lib, n):
     bm = lm.moe_lora_resolve_block_m(s)
     # the built-in choice: 16-row streaming tiles at <= 16 rows per expert,
     # 32-row ones for the dense layer, 64 x 128 tiles at ~32 rows per expert
-    # (GPT-OSS-like), 256 x 256 from ~100 rows per expert
-    assert bm == {1: 16, 2: 16, 3: 64, 4: 256, 5: 256, 6: 32}[n]
+    # (GPT-OSS-like), 192 x 256 at ~128 (Qwen3-MoE-like), 256 x 256 at ~256
+    assert bm == {1: 16, 2: 16, 3: 64, 4: 192, 5: 256, 6: 32}[n]
     ws = lm.moe_lora_workspace_bytes(s)
     P = wl.T * wl.topk
     cap = P + wl.E * (bm - 1)
@@ -163,7 +163,7 @@ def test_committed_tuning_table_is_valid(lib):
     table = lm.load_tuning()
     byname = {w.name: w for w in synth.WORKLOADS.values()}
     for e in doc["entries"]:
-        assert e["block_m"] in (16, 32, 64, 128, 256)
+        assert e["block_m"] in (16, 32, 64, 128, 192, 256)
         assert str(e["block_m"]) in e["ms"] and min(e["ms"], key=e["ms"].get) == str(e["block_m"])
         wl = byname[e["workload"]]
         shape = lm.make_shape(wl.T, wl.H, wl.I, wl.E, wl.topk, wl.L, wl.r, 0, wl.scale, tuning=table)

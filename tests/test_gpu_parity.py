@@ -50,7 +50,7 @@ def check_align_exact(T, k, E, L, bm, ids, lids, what):
 
 
 @pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 6])
-@pytest.mark.parametrize("bm", [16, 64, 256])
+@pytest.mark.parametrize("bm", [16, 64, 192, 256])
 def test_align_bitexact_workloads(n, bm):
     wl = synth.WORKLOADS[n]
     ids, _ = synth.make_routing(wl)
@@ -63,7 +63,7 @@ def test_align_adversarial():
     for name, T, k, E, L, bm, ids, lids in pins.align_cases():
         if T == 0:
             continue
-        for b in sorted({16, 32, 128} | ({bm} if bm in (16, 32, 64, 128, 256) else set())):
+        for b in sorted({16, 32, 128} | ({bm} if bm in (16, 32, 64, 128, 192, 256) else set())):
             check_align_exact(T, k, E, L, b, ids, lids, f"{name} bm={b}")
     rng = np.random.default_rng(9)
     # many chunks, one hot expert, ragged P
@@ -122,7 +122,7 @@ def test_dense_split_k(I, bm):
     full_check(synth.make_inputs(wl), bm, f"dense I={I} bm={bm}")
 
 
-@pytest.mark.parametrize("bm", [0, 16, 32, 64, 128, 256])
+@pytest.mark.parametrize("bm", [0, 16, 32, 64, 128, 192, 256])
 def test_tiny_workload(bm):
     inp = synth.make_inputs(1)
     full_check(inp, bm, f"tiny bm={bm}")
@@ -133,7 +133,7 @@ def test_tiny_scale_and_seed():
     full_check(inp, 0, "tiny seed 3 scale 0.5", scale=0.5)
 
 
-@pytest.mark.parametrize("bm", [0, 64, 128, 256])
+@pytest.mark.parametrize("bm", [0, 64, 128, 192, 256])
 @pytest.mark.parametrize("H,I,r", [(104, 104, 8), (104, 1000, 24), (1000, 104, 16), (2880, 2880, 64),
                                    (256, 512, 128), (64, 40, 8), (24, 16, 8)])
 def test_ragged_tails(H, I, r, bm):
@@ -171,7 +171,7 @@ def test_edge_cases():
     assert lm.moe_lora_device_errors(shape, ws) == 4
 
 
-@pytest.mark.parametrize("bm", [0, 32, 64, 128, 256])
+@pytest.mark.parametrize("bm", [0, 32, 64, 128, 192, 256])
 def test_routing_extremes(bm):
     """Every token to every expert (topk = E), and every token to one expert
     (several row tiles of one expert, the others untouched)."""
@@ -186,7 +186,7 @@ def test_routing_extremes(bm):
 
 
 @pytest.mark.parametrize("T,E,L", [(200, 4, 100), (600, 64, 200)])
-@pytest.mark.parametrize("bm", [0, 32, 64, 128, 256])
+@pytest.mark.parametrize("bm", [0, 32, 64, 128, 192, 256])
 def test_more_than_64_adapters(T, E, L, bm):
     """L > 64 adapters: the tiled expand scans adapter ids 64 at a time; the
     align's (expert, slot) table has E x (L + 1) buckets (12864 at E = 64,
@@ -223,7 +223,7 @@ def test_shrink_stage_matches_reference():
 
 
 @pytest.mark.parametrize("shape", ["even", "ragged"])
-@pytest.mark.parametrize("bm", [0, 16, 32, 64, 128, 256])
+@pytest.mark.parametrize("bm", [0, 16, 32, 64, 128, 192, 256])
 def test_exact_small_integer_layer(bm, shape):
     """Small-integer inputs make every intermediate exact (exact_inputs.py):
     the layer output must equal the exact values the fp64 reference gives

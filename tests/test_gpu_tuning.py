@@ -14,7 +14,7 @@ def test_layer_at_tuned_block_m(n):
     table = lm.load_tuning()
     wl = synth.WORKLOADS[n]
     shape = lm.make_shape(wl.T, wl.H, wl.I, wl.E, wl.topk, wl.L, wl.r, 0, wl.scale, tuning=table)
-    assert shape.block_m in (16, 32, 64, 128, 256)
+    assert shape.block_m in (16, 32, 64, 128, 192, 256)
     full_check(synth.make_inputs(wl), shape.block_m, f"workload {n} at tuned block_m {shape.block_m}")
 
 
@@ -28,7 +28,7 @@ def test_tune_sweep_writes_a_valid_table(tmp_path):
     assert tune.main(["--workloads", "1", "--iters", "3", "--warmup", "1", "--out", str(out)]) == 0
     doc = json.loads(out.read_text())
     (e,) = doc["entries"]
-    assert e["workload"] == "tiny" and e["block_m"] in (16, 32, 64, 128, 256)
+    assert e["workload"] == "tiny" and e["block_m"] in (16, 32, 64, 128, 192, 256)
     assert min(e["ms"], key=e["ms"].get) == str(e["block_m"])
     wl = synth.WORKLOADS[1]
     shape = lm.make_shape(wl.T, wl.H, wl.I, wl.E, wl.topk, wl.L, wl.r, 0, wl.scale,
