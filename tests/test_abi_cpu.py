@@ -62,6 +62,20 @@ def test_workspace_and_block_m(lib, n):
     assert lm.moe_lora_resolve_block_m(s2) == 64
 
 
+def test_block_m_heuristic_boundaries(lib):
+    """The built-in block_m at each edge of its rows-per-expert ranges (64
+    experts top-8: T = 8 * rows gives T * 8 / 64 = rows per expert; H = 2048
+    gives the tiled grids enough column tiles), and the streaming fallback for
+    a single expert."""
+    want = {16: 16, 17: 32, 24: 32, 25: 64, 48: 64, 49: 128, 95: 128, 96: 192, 144: 192,
+            145: 256, 1000: 256}
+    for rows, bm in want.items():
+        s = lm.make_shape(8 * rows, 2048, 768, 64, 8, 4, 16)
+        assert lm.moe_lora_resolve_block_m(s) == bm, rows
+    # one expert with wide weights: 40 column tiles of 128 < 512 -> streaming
+    assert lm.moe_lora_resolve_block_m(lm.make_shape(200, 5120, 25600, 1, 1, 8, 16)) == 32
+
+
 def test_bad_shapes(lib):
     good = dict(T=4, H=64, I=32, E=4, topk=2, L=2, r=8)
     cases = [
