@@ -81,7 +81,7 @@ def test_bad_shapes(lib):
     cases = [
         (dict(T=-1), lm.MOE_LORA_EINVAL), (dict(H=0), lm.MOE_LORA_EINVAL),
         (dict(topk=5), lm.MOE_LORA_EINVAL), (dict(L=0), lm.MOE_LORA_EINVAL),
-        (dict(block_m=48), lm.MOE_LORA_EINVAL), (dict(H=60), lm.MOE_LORA_EALIGN),
+        (dict(block_m=48), lm.MOE_LORA_EINVAL), (dict(block_m=96), lm.MOE_LORA_EINVAL), (dict(H=60), lm.MOE_LORA_EALIGN),
         (dict(I=36), lm.MOE_LORA_EALIGN), (dict(r=12), lm.MOE_LORA_EUNSUPPORTED),
         (dict(r=136), lm.MOE_LORA_EUNSUPPORTED), (dict(E=8000, L=2), lm.MOE_LORA_EUNSUPPORTED),
     ]
