@@ -150,8 +150,10 @@ int moe_lora_align(const moe_lora_shape* shape, const int32_t* topk_ids, const i
  * (slot j = j-th choice, bit-exact); weights = softmax over the k chosen
  * logits (fp32), i.e. the full softmax's top-k probabilities renormalised.
  *
- *   logits        device [T][E] fp32 (finite; a non-finite logit is never
- *                 chosen, and a slot left without an eligible expert gets -1)
+ *   logits        device [T][E] fp32.  A non-finite logit (NaN, +inf, -inf)
+ *                 is never chosen; a slot left without a finite logit gets
+ *                 expert -1 and weight 0 (the align counts and drops it) and
+ *                 the chosen experts share the weight.
  *   topk_ids      device [T][topk] int32, written
  *   topk_weights  device [T][topk] fp32, written
  * shape->topk must be at most 64 (MOE_LORA_EUNSUPPORTED otherwise).  Async on

@@ -15,9 +15,10 @@
 // its experts (lane, lane + 64, ...) for the best eligible one and a
 // butterfly of lane exchanges picks the wavefront's best.  Lane j keeps
 // choice j; the softmax runs across lanes 0..k-1 (k <= 64).  Comparisons are
-// exact fp32 comparisons, so the chosen ids are bit-exact; a non-finite
-// logit is never chosen (the slot gets expert -1, which the align counts and
-// drops).
+// exact fp32 comparisons, so the chosen ids are bit-exact.  A non-finite
+// logit (NaN, +inf, -inf) is never chosen: slots left without a finite
+// logit get expert -1 and weight 0 (the align counts and drops such pairs),
+// and the chosen ones share the weight.
 #pragma once
 
 #include "device_util.h"
@@ -27,6 +28,12 @@ namespace moelora {
 // a before b in the choice order: larger logit, or equal logit and lower index
 __device__ __forceinline__ bool before(float va, int ea, float vb, int eb) {
   return va > vb || (va == vb && ea < eb);
+}
+
+// x (logit of expert e) may be chosen after the previous choice (pv, pe):
+// it is finite and comes after that choice in the order
+__device__ __forceinline__ bool eligible(float pv, int pe, float x, int e) {
+  return __builtin_isfinite(x) && before(pv, pe, x, e);
 }
 
 // Routes token t with one wavefront (all 64 lanes call it); on return lane j
@@ -53,7 +60,7 @@ __device__ __forceinline__ void route_token(const float* __restrict__ lg, int E,
 #pragma unroll
       for (int i = 0; i < R; ++i) {
         const int e = lane + 64 * i;
-        if (e < E && before(pv, pe, v[i], e) && (be < 0 || before(v[i], e, bv, be))) {
+        if (e < E && eligible(pv, pe, v[i], e) && (be < 0 || before(v[i], e, bv, be))) {
           bv = v[i];
           be = e;
         }
@@ -61,7 +68,7 @@ __device__ __forceinline__ void route_token(const float* __restrict__ lg, int E,
     } else {
       for (int e = lane; e < E; e += 64) {
         const float x = lg[e];
-        if (before(pv, pe, x, e) && (be < 0 || before(x, e, bv, be))) {
+        if (eligible(pv, pe, x, e) && (be < 0 || before(x, e, bv, be))) {
           bv = x;
           be = e;
         }
@@ -110,7 +117,7 @@ __device__ __forceinline__ void route_token_thread(const float* __restrict__ lg,
     int be = -1;
     for (int e = 0; e < E; ++e) {
       const float x = lg[e];
-      if (before(pv, pe, x, e) && (be < 0 || before(x, e, bv, be))) {
+      if (eligible(pv, pe, x, e) && (be < 0 || before(x, e, bv, be))) {
         bv = x;
         be = e;
       }

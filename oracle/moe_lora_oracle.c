@@ -278,8 +278,12 @@ int orc_align(int T, int k, int E, int L, int block_m, const int32_t* topk_ids,
  *   - experts in descending logit order, equal logits by ascending index
  *     (slot j holds the j-th choice);
  *   - weights = softmax over the k chosen logits, which equals the full
- *     softmax's top-k probabilities renormalised to sum to one.
- * logits [T][E] float (finite), ids [T][k] int32, w [T][k] double.
+ *     softmax's top-k probabilities renormalised to sum to one;
+ *   - a logit that is not a finite number (NaN, +inf, -inf) is never chosen:
+ *     it has no place in a descending order that a softmax can weight.  When
+ *     fewer than k finite logits remain, the slots left over get expert -1
+ *     and weight 0, and the chosen ones share the weight.
+ * logits [T][E] float, ids [T][k] int32, w [T][k] double.
  * Returns 0, or -1 for k outside [1, E]. */
 int orc_route(int T, int E, int k, const float* logits, int32_t* ids, double* w) {
   if (k < 1 || k > E) return -1;
@@ -287,20 +291,29 @@ int orc_route(int T, int E, int k, const float* logits, int32_t* ids, double* w)
   if (!taken) return -1;
   for (int t = 0; t < T; ++t) {
     const float* lg = logits + (size_t)t * E;
+    int32_t* id = ids + (size_t)t * k;
+    double* wt = w + (size_t)t * k;
     memset(taken, 0, (size_t)E);
+    int nch = 0;  /* slots that received an expert */
     for (int j = 0; j < k; ++j) {
       int best = -1;
       for (int e = 0; e < E; ++e) {
-        if (taken[e]) continue;
+        if (taken[e] || !isfinite(lg[e])) continue;
         if (best < 0 || (double)lg[e] > (double)lg[best]) best = e;  /* strict: ties keep the lower index */
       }
+      id[j] = best;
+      if (best < 0) continue;
       taken[best] = 1;
-      ids[(size_t)t * k + j] = best;
+      ++nch;
     }
-    const double m = (double)lg[ids[(size_t)t * k]];  /* the largest chosen logit */
+    if (nch == 0) {
+      for (int j = 0; j < k; ++j) wt[j] = 0.0;
+      continue;
+    }
+    const double m = (double)lg[id[0]];  /* the largest chosen logit */
     double sum = 0.0;
-    for (int j = 0; j < k; ++j) sum += exp((double)lg[ids[(size_t)t * k + j]] - m);
-    for (int j = 0; j < k; ++j) w[(size_t)t * k + j] = exp((double)lg[ids[(size_t)t * k + j]] - m) / sum;
+    for (int j = 0; j < nch; ++j) sum += exp((double)lg[id[j]] - m);
+    for (int j = 0; j < k; ++j) wt[j] = j < nch ? exp((double)lg[id[j]] - m) / sum : 0.0;
   }
   free(taken);
   return 0;

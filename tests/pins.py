@@ -383,15 +383,19 @@ ALIGN_PINS = [pin_align_examples, pin_align_comparison_sort, pin_align_invariant
 def route_by_sorting(logits, k):
     """Top-k by sorting (expert, logit) pairs on (-logit, expert) -- an
     independent statement of "largest first, ties to the lower index" -- and
-    the weights from scipy's softmax over the chosen logits."""
+    the weights from scipy's softmax over the chosen logits.  Non-finite
+    logits are left out of the sort; slots past the finite ones get -1 and
+    weight 0."""
     from scipy.special import softmax
     T, E = logits.shape
-    ids = np.zeros((T, k), np.int32)
+    ids = np.full((T, k), -1, np.int32)
     w = np.zeros((T, k))
     for t in range(T):
-        order = sorted(range(E), key=lambda e: (-float(logits[t, e]), e))[:k]
-        ids[t] = order
-        w[t] = softmax(logits[t, order].astype(np.float64))
+        fin = [e for e in range(E) if np.isfinite(logits[t, e])]
+        order = sorted(fin, key=lambda e: (-float(logits[t, e]), e))[:k]
+        ids[t, :len(order)] = order
+        if order:
+            w[t, :len(order)] = softmax(logits[t, order].astype(np.float64))
     return ids, w
 
 
@@ -404,13 +408,22 @@ def router_cases():
     # ties: logits on a coarse grid
     lg = rng.integers(-2, 3, size=(8, 10)).astype(np.float32)
     cases.append(("grid ties", lg, 3))
+    # non-finite logits scattered among finite ones, and rows with fewer
+    # finite logits than k
+    lg = rng.standard_normal((6, 9)).astype(np.float32)
+    lg[rng.random((6, 9)) < 0.3] = np.nan
+    lg[0, 2] = np.inf
+    lg[1, 4] = -np.inf
+    lg[2, :7] = -np.inf
+    lg[3, :] = np.nan
+    cases.append(("non-finite", lg, 4))
     return cases
 
 
 def pin_router_examples(orc):
     data = json.load(open(os.path.join(GOLDEN, "router_examples.json")))
     for ex in data["examples"]:
-        ids, w = orc.route(np.array(ex["logits"], np.float32), ex["k"])
+        ids, w = orc.route(np.array([[float(v) for v in row] for row in ex["logits"]], np.float32), ex["k"])
         assert ids.tolist() == ex["ids"], f"{ex['name']}: ids {ids.tolist()}"
         close(w, np.array(ex["weights"]), rtol=ex.get("weights_rtol", 1e-14), what=ex["name"])
 

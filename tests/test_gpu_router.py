@@ -52,18 +52,56 @@ def test_router_matches_reference(T, E, k, ties, bias):
     assert err <= 1e-6
 
 
-def test_router_skips_nonfinite():
-    """A NaN or -inf logit is never chosen while finite ones remain."""
-    lg = logits_for(4, 16, seed=5)
+def nonfinite_logits(T, E, seed):
+    lg = logits_for(T, E, seed=seed)
     lg[0, 3] = np.nan
     lg[1, :] = -np.inf
-    lg[1, 7] = 0.5
-    lg[2, 0] = np.inf
-    ids, w = gpu_route(lg, 2)
-    assert 3 not in ids[0].tolist()
-    assert ids[1, 0] == 7
-    assert ids[2, 0] == 0
-    assert np.all(np.isfinite(w[[0, 3]]))
+    lg[1, 7] = 0.5            # one finite logit: slot 0 gets it, the rest -1
+    lg[2, 0] = np.inf         # +inf is not chosen either
+    lg[3, :] = np.nan         # nothing eligible
+    lg[4, ::2] = np.inf
+    return lg
+
+
+@pytest.mark.parametrize("E", [16, 200])
+def test_router_nonfinite_matches_reference(E):
+    """Non-finite logits (NaN, +inf, -inf) are never chosen; slots without a
+    finite logit get -1 and weight 0: ids bit-exact and weights within 1e-6
+    of the reference, every weight finite."""
+    k = 3
+    lg = nonfinite_logits(8, E, seed=5)
+    ids, w = gpu_route(lg, k)
+    rids, rw = oracle.Oracle().route(lg, k)
+    assert rids[1].tolist() == [7, -1, -1] and rids[3].tolist() == [-1, -1, -1]
+    assert 0 not in rids[2].tolist()
+    assert np.array_equal(ids, rids), f"ids {ids.tolist()} vs {rids.tolist()}"
+    assert np.all(np.isfinite(w))
+    assert float(np.max(np.abs(w - rw))) <= 1e-6
+
+
+def test_route_align_nonfinite_matches_reference():
+    """The same through the fused router + align kernel (one thread per
+    token): the -1 slots are dropped and counted by the align."""
+    import lora_moe_amd as lm
+    T, E, k, L = 8, 16, 3, 2
+    lg = nonfinite_logits(T, E, seed=6)
+    lids = np.zeros(T, np.int32)
+    shape = lm.make_shape(T, 64, 64, E, k, L, 8, 16)
+    ws = lm.alloc_workspace(shape)
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    lm.moe_lora_route_align(shape, torch.from_numpy(lg).cuda(), torch.from_numpy(lids).cuda(), ids, w, ws)
+    torch.cuda.synchronize()
+    o = oracle.Oracle()
+    rids, rw = o.route(lg, k)
+    assert np.array_equal(ids.cpu().numpy(), rids)
+    wg = w.cpu().numpy()
+    assert np.all(np.isfinite(wg)) and float(np.max(np.abs(wg - rw))) <= 1e-6
+    got = gpu_views(shape, ws)
+    want = o.align(T, k, E, L, 16, rids, lids, got["cap_rows"], got["cap_blocks"])
+    for name in ("sorted_ids", "expert_off", "pos_of_pair"):
+        assert np.array_equal(got[name], want[name]), name
+    assert got["err_count"] == want["err_count"] == int((rids < 0).sum())
 
 
 @pytest.mark.parametrize("T,E,k,L,bm", [(16, 8, 2, 8, 16), (32, 64, 8, 5, 32), (100, 64, 8, 5, 32), (300, 32, 4, 16, 128),

@@ -54,10 +54,12 @@ MUTANTS = [
      "if (best < 0 || (double)lg[e] >= (double)lg[best]) best = e;"),
     ("router_smallest_first", "if (best < 0 || (double)lg[e] > (double)lg[best]) best = e;",
      "if (best < 0 || (double)lg[e] < (double)lg[best]) best = e;"),
-    ("router_full_softmax", "for (int j = 0; j < k; ++j) sum += exp((double)lg[ids[(size_t)t * k + j]] - m);",
+    ("router_full_softmax", "for (int j = 0; j < nch; ++j) sum += exp((double)lg[id[j]] - m);",
      "for (int j = 0; j < E; ++j) sum += exp((double)lg[j] - m);"),
-    ("router_unnormalised", "w[(size_t)t * k + j] = exp((double)lg[ids[(size_t)t * k + j]] - m) / sum;",
-     "w[(size_t)t * k + j] = exp((double)lg[ids[(size_t)t * k + j]] - m);"),
+    ("router_unnormalised", "wt[j] = j < nch ? exp((double)lg[id[j]] - m) / sum : 0.0;",
+     "wt[j] = j < nch ? exp((double)lg[id[j]] - m) : 0.0;"),
+    ("router_chooses_nonfinite", "if (taken[e] || !isfinite(lg[e])) continue;",
+     "if (taken[e] || isnan(lg[e])) continue;"),
 ]
 
 
