@@ -3,12 +3,16 @@
 
 Prints ONE JSON line: tokens/s of the whole layer, the roofline position of
 the dominant kernel (HIP-event durations measured inside the timed region),
-and the CPU reference timed on the host cores as a baseline.
+the other synthetic workloads' layer rates, and the CPU reference timed on
+the host cores as a baseline.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 5]
 
-Default workload: the pages' illustrative expert (hidden 4096, intermediate
-11008, rank 32), 8 experts top-2, 8 adapters, 16 decode tokens.
+Each timed step is one align + forward call with L2 and the 256 MB MALL
+flushed before it (a 512 MB fill outside the events); ``value`` is T over
+the median call time.  Default workload: the DeepSeek-like prefill layer
+(8192 tokens, hidden 7168, intermediate 2048, 256 experts top-8, 8 adapters
+of rank 64), the largest shape and the one whose MFMA rate is the target.
 """
 from __future__ import annotations
 
@@ -16,6 +20,7 @@ import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -25,21 +30,24 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE-LoRA layer tokens/s at 1 GPU; % HBM roofline (decode) / % MFMA peak (prefill)"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+FLUSH_MB = 512                 # > L2 (8 x 4 MB) + MALL (256 MB)
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", type=int, default=2, help="synthetic workload number 1..6")
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=5, help="synthetic workload number 1..6")
     ap.add_argument("--block-m", type=int, default=0)
+    ap.add_argument("--others", default="1,2,3,4,6",
+                    help="further workloads summarised under 'workloads' ('' for none)")
+    ap.add_argument("--other-steps", type=int, default=10)
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the warm, graph and from-logits timings of the main workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the reference baseline sample")
-    ap.add_argument("--cold-iters", type=int, default=-1,
-                    help="extra per-call timings with L2 and MALL flushed before each call "
-                         "(default 20, 10 for workload 5; 0 disables)")
     ap.add_argument("--read-probe-mb", type=int, default=0,
                     help="time a bf16 reduction and a device copy over this many MiB (attainable HBM rates)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
@@ -148,29 +156,49 @@ def read_probe(mb, iters=10):
     print(json.dumps(out), flush=True)
 
 
-def cold_timing(step, iters, flush_mb=512):
-    """Per-call times of align+forward with the caches flushed first: a
-    flush_mb-MB fill before every call evicts L2 and the 256 MB MALL; the fill
-    is outside the events.  Median and minimum in ms."""
+def flushed_calls(step, iters, scratch, profiler=None):
+    """Per-call milliseconds of `iters` align + forward calls, each after a
+    fill of `scratch` (outside the events) that evicts L2 and the MALL."""
     import torch
-    scratch = torch.empty(flush_mb << 20, dtype=torch.uint8, device="cuda")
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(iters)]
     for a, b in ev:
         scratch.fill_(1)
         a.record()
-        step()
+        step(profiler)
         b.record()
     torch.cuda.synchronize()
-    ts = sorted(a.elapsed_time(b) for a, b in ev)
-    del scratch
-    return {"iters": iters, "median_ms": ts[len(ts) // 2], "min_ms": ts[0],
-            "flush_bytes_before_each": flush_mb << 20}
+    return [a.elapsed_time(b) for a, b in ev]
+
+
+def warm_calls(step, iters):
+    """Mean milliseconds of back-to-back calls (no flush)."""
+    import torch
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(iters):
+        step()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / iters
+
+
+def layer_fracs(work, ms):
+    s = ms * 1e-3
+    return {"hbm_frac": work["bytes"] / s / (HBM_PEAK_GBS * 1e9),
+            "mfma_frac": work["flops"] / s / (MFMA_BF16_PEAK_TFLOPS * 1e12)}
+
+
+def binding(work):
+    """The roofline that bounds the layer: MFMA when its arithmetic intensity
+    is above the ridge (312.5 flop/B), HBM otherwise."""
+    ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    return "mfma" if work["flops"] / max(work["bytes"], 1) >= ridge else "hbm"
 
 
 def cpu_baseline(inp, target_s):
     """The fp64 reference on the host cores over a bounded sample of the same
-    workload's tokens; returns tokens/s and what was run."""
+    workload's tokens (the first n, with the weight slabs they read generated
+    on the host); returns tokens/s and what was run."""
     import numpy as np
 
     import oracle
@@ -181,18 +209,48 @@ def cpu_baseline(inp, target_s):
     # calibrate with one token per thread, then size the sample for ~target_s
     n0 = min(wl.T, nthreads)
     toks = np.arange(n0, dtype=np.int32)
-    synth.host_slabs_for_tokens(inp, np.arange(wl.T))
+    synth.host_slabs_for_tokens(inp, toks)
     t0 = time.perf_counter()
     oracle.layer_from_inputs(inp, tokens=toks, oracle=o, nthreads=nthreads)
     dt = time.perf_counter() - t0
     n = n0 * max(1, int(round(target_s / max(dt, 1e-3))))
     toks = (np.arange(n) % wl.T).astype(np.int32)
+    synth.host_slabs_for_tokens(inp, np.unique(toks))
     t0 = time.perf_counter()
     oracle.layer_from_inputs(inp, tokens=toks, oracle=o, nthreads=nthreads)
     dt = time.perf_counter() - t0
     return {"value": n / dt, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
-            "sample": f"{n} token evaluations of workload {wl.name} (tokens cycled 0..{wl.T - 1}),"
-                      f" fp64, {dt:.1f} s wall"}
+            "sample": f"{n} token evaluations of workload {wl.name} (tokens 0..{min(n, wl.T) - 1}"
+                      f"{', cycled' if n > wl.T else ''}), fp64, {dt:.1f} s wall"}
+
+
+def run_other(lm, synth, n, steps, scratch):
+    """Flushed median of one more workload (generated, timed, freed)."""
+    import torch
+    wl = synth.WORKLOADS[n]
+    print(f"bench: workload {n} ({wl.name})", file=sys.stderr, flush=True)
+    dev, inp = synth.device_inputs(wl, touched_only=True)
+    work = synth.algorithmic_work(wl, inp.topk_ids, inp.lora_ids)
+    shape = lm.make_shape(wl.T, wl.H, wl.I, wl.E, wl.topk, wl.L, wl.r, 0, wl.scale)
+    ws = lm.alloc_workspace(shape)
+    y = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda")
+
+    def step(prof=None):
+        lm.moe_lora_align(shape, dev["topk_ids"], dev["lora_ids"], ws, profiler=prof)
+        lm.moe_lora_forward(shape, dev["x"], dev["topk_ids"], dev["topk_weights"], dev["lora_ids"],
+                            dev["W_gu"], dev["W_down"], dev["A_gu"], dev["B_gu"], dev["A_down"],
+                            dev["B_down"], ws, y, profiler=prof)
+
+    for _ in range(3):
+        step()
+    ts = flushed_calls(step, steps, scratch)
+    med = statistics.median(ts)
+    out = {"workload": wl.name, "block_m": lm.moe_lora_resolve_block_m(shape),
+           "flushed_median_ms": med, "flushed_min_ms": min(ts), "tokens_per_s": wl.T / (med * 1e-3),
+           "bound": binding(work), **layer_fracs(work, med)}
+    del dev, ws, y
+    torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -217,51 +275,51 @@ def main():
     wl = synth.WORKLOADS[args.workload]
     print(f"bench: generating workload {args.workload} ({wl.name}) on the device", file=sys.stderr,
           flush=True)
-    dev, inp = synth.device_inputs(wl, touched_only=True)
+    dev, inp = synth.device_inputs(wl, touched_only=True, keep_host=not args.no_cpu_baseline)
     work = synth.algorithmic_work(wl, inp.topk_ids, inp.lora_ids)
     shape = lm.make_shape(wl.T, wl.H, wl.I, wl.E, wl.topk, wl.L, wl.r, args.block_m, wl.scale)
     bm = lm.moe_lora_resolve_block_m(shape)
     ws = lm.alloc_workspace(shape)
     y = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda")
     stream = torch.cuda.current_stream()
+    scratch = torch.empty(FLUSH_MB << 20, dtype=torch.uint8, device="cuda")
 
-    def step(st=stream):
-        lm.moe_lora_align(shape, dev["topk_ids"], dev["lora_ids"], ws, st)
+    def step(prof=None, st=stream):
+        lm.moe_lora_align(shape, dev["topk_ids"], dev["lora_ids"], ws, st, profiler=prof)
         lm.moe_lora_forward(shape, dev["x"], dev["topk_ids"], dev["topk_weights"], dev["lora_ids"],
                             dev["W_gu"], dev["W_down"], dev["A_gu"], dev["B_gu"], dev["A_down"],
-                            dev["B_down"], ws, y, st)
+                            dev["B_down"], ws, y, st, profiler=prof)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     print(f"bench: warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
 
-    # untimed pass with events around every stage: the per-stage breakdown,
-    # and which stage dominates
+    # untimed pass with events around every stage (flushed calls, like the
+    # timed ones): the per-stage breakdown, and which stage dominates
     nbreak = max(1, min(args.steps, 10))
-    lm.moe_lora_profile_begin(nbreak)
-    for _ in range(nbreak):
-        step()
-    torch.cuda.synchronize()
-    stage_ms, calls = lm.moe_lora_profile_end()
+    prof = lm.Profiler(nbreak)
+    flushed_calls(step, nbreak, scratch, prof)
+    stage_ms, calls = prof.read()
+    prof.close()
     per_stage = {k: v / max(calls, 1) for k, v in stage_ms.items()}
     sbf = stage_bytes_flops(wl, work)
     dom = max(sbf, key=lambda s: per_stage.get(s, 0.0))
 
-    # timed region: events only around the dominant stage's kernel (two event
-    # records per step on the launch stream)
-    lm.moe_lora_profile_begin(args.steps, [dom])
+    # timed region: K flushed calls, events around each call and, inside it,
+    # around the dominant stage's kernel (on the launch stream)
+    prof = lm.Profiler(args.steps, [dom])
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
+    call_ms = flushed_calls(step, args.steps, scratch, prof)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    dom_ms, dom_calls = lm.moe_lora_profile_end()
-    print(f"bench: timed {args.steps} steps in {elapsed:.3f} s", file=sys.stderr, flush=True)
+    dom_ms, dom_calls = prof.read()
+    prof.close()
+    print(f"bench: timed {args.steps} flushed steps in {elapsed:.3f} s", file=sys.stderr, flush=True)
 
-    ms_per_step = elapsed * 1e3 / args.steps
-    value = wl.T * args.steps / elapsed
+    ms_per_step = statistics.median(call_ms)
+    value = wl.T / (ms_per_step * 1e-3)
     dom_avg_ms = dom_ms[dom] / max(dom_calls, 1)
     dur_s = dom_avg_ms * 1e-3
     ai = sbf[dom]["flops"] / max(sbf[dom]["bytes"], 1)
@@ -274,11 +332,10 @@ def main():
         achieved = sbf[dom]["flops"] / dur_s / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS}
-    roof.update({"kernel": dom, "avg_launch_ms": dom_avg_ms,
+    roof.update({"traffic": measured_traffic(dom, wl.name, bm), "kernel": dom,
+                 "avg_launch_ms": dom_avg_ms,
                  "alg_bytes_per_launch": sbf[dom]["bytes"], "alg_flops_per_launch": sbf[dom]["flops"],
-                 "traffic": measured_traffic(dom, wl.name, bm),
                  "kernel_source_sha": kernel_source_sha(dom, bm)})
-    layer_s = ms_per_step * 1e-3
     out = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
@@ -287,66 +344,72 @@ def main():
                    "topk": wl.topk, "L": wl.L, "r": wl.r,
                    "block_m": bm, "seed": wl.seed},
         "roofline": roof,
-        "layer": {"alg_bytes": work["bytes"], "alg_flops": work["flops"],
-                  "hbm_frac": work["bytes"] / layer_s / (HBM_PEAK_GBS * 1e9),
-                  "mfma_frac": work["flops"] / layer_s / (MFMA_BF16_PEAK_TFLOPS * 1e12),
+        "timing": {"per_step": "one align + forward call after a 512 MB fill (L2 and MALL "
+                               "cold), HIP events around the call; value and ms_per_step from "
+                               "the median call", "median_ms": ms_per_step,
+                   "min_ms": min(call_ms), "max_ms": max(call_ms),
+                   "wall_s_timed_region": elapsed},
+        "layer": {"alg_bytes": work["bytes"], "alg_flops": work["flops"], "bound": binding(work),
+                  **layer_fracs(work, ms_per_step),
                   "experts_touched": work["experts_touched"],
                   "adapter_expert_pairs_touched": work["pairs_touched"]},
         "stages_ms": per_stage,
-        "stages_ms_note": f"average of {calls} untimed calls with events around every stage",
+        "stages_ms_note": f"average of {calls} untimed flushed calls with events around every stage",
     }
-    # the path from router logits: moe_lora_route_align (router fused into the
-    # align for small batches) + moe_lora_forward.  The logits are built so the
-    # router reproduces the workload's routing: log(w) at each chosen expert,
-    # -1e30 elsewhere (softmax of log w over the chosen experts is w itself).
-    logits = torch.full((wl.T, wl.E), -1e30, dtype=torch.float32, device="cuda")
-    logits.scatter_(1, dev["topk_ids"].long(), torch.log(dev["topk_weights"].clamp_min(1e-30)))
-    r_ids = torch.empty_like(dev["topk_ids"])
-    r_w = torch.empty_like(dev["topk_weights"])
+    if not args.no_extras:
+        out["warm"] = {"ms_per_step": warm_calls(step, args.steps),
+                       "note": "back-to-back calls, caches warm"}
+        # the path from router logits: moe_lora_route_align (router fused into
+        # the align for small batches) + moe_lora_forward.  The logits are built
+        # so the router reproduces the workload's routing: log(w) at each chosen
+        # expert, -1e30 elsewhere (softmax of log w over the chosen experts is w).
+        logits = torch.full((wl.T, wl.E), -1e30, dtype=torch.float32, device="cuda")
+        logits.scatter_(1, dev["topk_ids"].long(), torch.log(dev["topk_weights"].clamp_min(1e-30)))
+        r_ids = torch.empty_like(dev["topk_ids"])
+        r_w = torch.empty_like(dev["topk_weights"])
 
-    def step_routed():
-        lm.moe_lora_route_align(shape, logits, dev["lora_ids"], r_ids, r_w, ws, stream)
-        lm.moe_lora_forward(shape, dev["x"], r_ids, r_w, dev["lora_ids"],
-                            dev["W_gu"], dev["W_down"], dev["A_gu"], dev["B_gu"], dev["A_down"],
-                            dev["B_down"], ws, y, stream)
+        def step_routed():
+            lm.moe_lora_route_align(shape, logits, dev["lora_ids"], r_ids, r_w, ws, stream)
+            lm.moe_lora_forward(shape, dev["x"], r_ids, r_w, dev["lora_ids"],
+                                dev["W_gu"], dev["W_down"], dev["A_gu"], dev["B_gu"], dev["A_down"],
+                                dev["B_down"], ws, y, stream)
 
-    for _ in range(args.warmup):
-        step_routed()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step_routed()
-    torch.cuda.synchronize()
-    routed_s = (time.perf_counter() - t0) / args.steps
-    out["from_logits"] = {"ms_per_step": routed_s * 1e3, "tokens_per_s": wl.T / routed_s,
-                          "note": "moe_lora_route_align + moe_lora_forward from logits that "
-                                  "reproduce the workload's routing"}
-    # the same step captured once in a HIP graph and replayed (no per-launch
-    # host work, launches queued back to back)
-    g = torch.cuda.CUDAGraph()
-    gs = torch.cuda.Stream()
-    gs.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(gs):
-        with torch.cuda.graph(g, stream=gs):
-            step(gs)
-    torch.cuda.current_stream().wait_stream(gs)
-    for _ in range(args.warmup):
-        g.replay()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        g.replay()
-    torch.cuda.synchronize()
-    graph_s = (time.perf_counter() - t0) / args.steps
-    out["graph"] = {"ms_per_step": graph_s * 1e3, "tokens_per_s": wl.T / graph_s,
-                    "note": "align + forward captured once in a HIP graph, replayed"}
-    del g
-    cold_iters = args.cold_iters if args.cold_iters >= 0 else (10 if args.workload == 5 else 20)
-    if cold_iters > 0:
-        out["cold"] = cold_timing(step, cold_iters)
+        for _ in range(args.warmup):
+            step_routed()
+        out["from_logits"] = {"ms_per_step": warm_calls(step_routed, args.steps),
+                              "note": "moe_lora_route_align + moe_lora_forward from logits that "
+                                      "reproduce the workload's routing, warm"}
+        # the same step captured once in a HIP graph and replayed
+        g = torch.cuda.CUDAGraph()
+        gs = torch.cuda.Stream()
+        gs.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(gs):
+            with torch.cuda.graph(g, stream=gs):
+                step(None, gs)
+        torch.cuda.current_stream().wait_stream(gs)
+        for _ in range(args.warmup):
+            g.replay()
+        out["graph"] = {"ms_per_step": warm_calls(g.replay, args.steps),
+                        "note": "align + forward captured once in a HIP graph, replayed, warm"}
+        del g
+    # the host reference runs while the GPU is idle, then the other workloads
     if not args.no_cpu_baseline:
         print("bench: timing the CPU reference", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    del dev, ws, y
+    torch.cuda.empty_cache()
+    others = [int(w) for w in args.others.split(",") if w.strip()] if args.others else []
+    if others:
+        out["workloads"] = {"note": "flushed median of align + forward per workload, "
+                                    f"{args.other_steps} calls, block_m chosen by the library",
+                            args.workload: {"workload": wl.name, "block_m": bm,
+                                            "flushed_median_ms": ms_per_step,
+                                            "flushed_min_ms": min(call_ms),
+                                            "tokens_per_s": value, "bound": binding(work),
+                                            **layer_fracs(work, ms_per_step)}}
+        for n in others:
+            if n != args.workload:
+                out["workloads"][n] = run_other(lm, synth, n, args.other_steps, scratch)
     print(json.dumps(out), flush=True)
 
 

@@ -87,7 +87,25 @@ typedef struct moe_lora_views {
   int64_t cap_blocks;    /* ceil(cap_rows / block_m)                                         */
   int32_t block_m;       /* block size in effect (resolved when the shape says 0)           */
   int32_t d_splits;      /* K splits of the down GEMM (1 unless few experts, wide weights)  */
+  uint16_t* h_lo;        /* [cap_rows][I] bf16 remainder h - rne(h) when I >= 4096, else NULL */
 } moe_lora_views;
+
+/* Device pointers to the align outputs inside a workspace (see
+ * moe_lora_align_view); the same regions as the first eight moe_lora_views
+ * fields, read-only. */
+typedef struct moe_lora_align_ptrs {
+  const int32_t* sorted_ids;   /* [cap_rows]                                              */
+  const int32_t* expert_off;   /* [E+1]                                                   */
+  const int32_t* seg_start;    /* [E*(L+1)]                                               */
+  const int32_t* seg_cnt;      /* [E*(L+1)]                                               */
+  const int32_t* block_expert; /* [cap_blocks]                                            */
+  const int32_t* pos_of_pair;  /* [T*topk]                                                */
+  const int32_t* num_padded;   /* [1]                                                     */
+  const int32_t* err_count;    /* [1]                                                     */
+} moe_lora_align_ptrs;
+
+/* Opaque stage-timing recorder owned by the caller (moe_lora_profiler_create). */
+typedef struct moe_lora_profiler moe_lora_profiler;
 
 /* block_m used for this shape (the shape's own value when non-zero), or a
  * negative status when the shape is invalid.  Host only, pure. */
@@ -95,7 +113,8 @@ int moe_lora_resolve_block_m(const moe_lora_shape* shape);
 
 /* One entry of a tile-configuration table, the result of an offline sweep
  * (the pages' tuned kernel configurations per shape: "Multi-LoRA for MoE
- * models", section "Kernel optimizations").  Key: the shape class, with
+ * models", section "Tuning kernel configurations for Amazon SageMaker AI and
+ * Amazon Bedrock").  Key: the shape class, with
  * rows_per_expert = ceil(T*topk / min(E, T*topk)) of the swept shape; value:
  * the block_m measured fastest for it. */
 typedef struct {
@@ -174,8 +193,18 @@ int moe_lora_route_align(const moe_lora_shape* shape, const float* logits, const
  * work).  For tests and tools that inspect the align or intermediates. */
 int moe_lora_workspace_view(const moe_lora_shape* shape, void* workspace, moe_lora_views* out);
 
+/* Device pointers to the align outputs in `workspace` for this shape (host
+ * only, no GPU work, nothing is read): sorted_ids, expert_off, seg_start,
+ * seg_cnt, block_expert, pos_of_pair, num_padded, err_count as written by
+ * moe_lora_align (layouts in moe_lora_views).  MOE_LORA_EINVAL for a null
+ * workspace or out, or an invalid shape's status. */
+int moe_lora_align_view(const moe_lora_shape* shape, const void* workspace, moe_lora_align_ptrs* out);
+
 /* The layer forward.  Requires a preceding moe_lora_align with the same
- * shape, ids and workspace on the same stream.
+ * shape, ids and workspace on the same stream, and each forward needs an
+ * align of its own: the align clears the shrink accumulators in the
+ * workspace, and a forward whose shrinks split K adds into them, so a second
+ * forward after the same align would add the adapters' shrink results twice.
  *   x            device [T][H] bf16
  *   topk_ids     device [T][topk] int32 (as given to the align)
  *   topk_weights device [T][topk] float
@@ -183,8 +212,11 @@ int moe_lora_workspace_view(const moe_lora_shape* shape, void* workspace, moe_lo
  *   W_gu, W_down, A_gu, B_gu, A_down, B_down   device bf16, layouts above
  *   y            device [T][H] bf16 output, overwritten (round to nearest even)
  * Accumulation is fp32 everywhere; the gate_up result stays fp32 through the
- * SiLU; h is stored bf16.  With split-K shrinks the fp32 sums are added with
- * atomics, so y may differ between runs in the last bits. */
+ * SiLU; h is stored bf16, and from I = 4096 on also as its bf16 remainder
+ * (h - rne(h)), which the down GEMM multiplies too (a down GEMM that deep
+ * then runs on 16- or 32-row tiles whatever block_m is).  With split-K
+ * shrinks the fp32 sums are added with atomics, so y may differ between runs
+ * in the last bits. */
 int moe_lora_forward(const moe_lora_shape* shape, const uint16_t* x, const int32_t* topk_ids,
                      const float* topk_weights, const int32_t* lora_ids, const uint16_t* W_gu,
                      const uint16_t* W_down, const uint16_t* A_gu, const uint16_t* B_gu,
@@ -199,20 +231,37 @@ int moe_lora_device_errors(const moe_lora_shape* shape, const void* workspace,
 /* Human-readable name of a status code (static string). */
 const char* moe_lora_status_str(int status);
 
-/* Stage timing with HIP events, for benchmarks.  moe_lora_profile_begin
- * creates events for up to max_calls align+forward calls and starts
- * recording around the kernel launches of the stages whose bit is set in
- * stage_mask (bit s = stage s; 0xffffffff for all) in later calls, on their
- * streams.  Each recorded stage adds two event records to the stream, so a
- * timed region that brackets one stage perturbs the rest the least;
- * moe_lora_profile_end waits for the recorded events, writes the summed time
- * of each stage in milliseconds to stage_ms[0..n) (n <= moe_lora_stage_count())
- * and the number of recorded calls to *calls, then stops recording.
- * Process-wide state: not for concurrent use from several host threads. */
+/* Stage timing with HIP events, for benchmarks and tools.  The recorder is
+ * the caller's object: moe_lora_profiler_create makes one for up to
+ * max_calls align+forward calls, recording the stages whose bit is set in
+ * stage_mask (bit s = stage s of moe_lora_stage_name; 0xffffffff for all).
+ * The *_timed variants of align, route_align and forward take it as their
+ * last argument (NULL: nothing is recorded, exactly the plain call) and
+ * record two events around each selected stage's launches on the call's
+ * stream; a call counts once its forward is enqueued, and calls past
+ * max_calls are not recorded.  moe_lora_profiler_read waits for the recorded
+ * events and writes each stage's summed milliseconds to stage_ms[0..n)
+ * (n <= moe_lora_stage_count()) and the recorded calls to *calls.
+ * A recorder is used by one host thread at a time; the library itself keeps
+ * no state between calls. */
 int moe_lora_stage_count(void);
 const char* moe_lora_stage_name(int stage);
-int moe_lora_profile_begin(int max_calls, uint32_t stage_mask);
-int moe_lora_profile_end(float* stage_ms, int n, int* calls);
+int moe_lora_profiler_create(int max_calls, uint32_t stage_mask, moe_lora_profiler** out);
+int moe_lora_profiler_read(moe_lora_profiler* prof, float* stage_ms, int n, int* calls);
+void moe_lora_profiler_destroy(moe_lora_profiler* prof);
+int moe_lora_align_timed(const moe_lora_shape* shape, const int32_t* topk_ids,
+                         const int32_t* lora_ids, void* workspace, size_t ws_bytes, void* stream,
+                         moe_lora_profiler* prof);
+int moe_lora_route_align_timed(const moe_lora_shape* shape, const float* logits,
+                               const int32_t* lora_ids, int32_t* topk_ids, float* topk_weights,
+                               void* workspace, size_t ws_bytes, void* stream,
+                               moe_lora_profiler* prof);
+int moe_lora_forward_timed(const moe_lora_shape* shape, const uint16_t* x, const int32_t* topk_ids,
+                           const float* topk_weights, const int32_t* lora_ids,
+                           const uint16_t* W_gu, const uint16_t* W_down, const uint16_t* A_gu,
+                           const uint16_t* B_gu, const uint16_t* A_down, const uint16_t* B_down,
+                           void* workspace, size_t ws_bytes, uint16_t* y, void* stream,
+                           moe_lora_profiler* prof);
 
 #ifdef __cplusplus
 }

@@ -46,7 +46,15 @@ class moe_lora_views(ctypes.Structure):
         "sorted_ids", "expert_off", "seg_start", "seg_cnt", "block_expert", "pos_of_pair",
         "num_padded", "err_count", "z_gu", "z_down", "h", "d")] + [
         ("cap_rows", ctypes.c_int64), ("cap_blocks", ctypes.c_int64), ("block_m", ctypes.c_int32),
-        ("d_splits", ctypes.c_int32)]
+        ("d_splits", ctypes.c_int32), ("h_lo", ctypes.c_void_p)]
+
+
+ALIGN_VIEW_FIELDS = ("sorted_ids", "expert_off", "seg_start", "seg_cnt", "block_expert",
+                     "pos_of_pair", "num_padded", "err_count")
+
+
+class moe_lora_align_ptrs(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ALIGN_VIEW_FIELDS]
 
 
 class moe_lora_tune_entry(ctypes.Structure):
@@ -103,14 +111,22 @@ def load_library(path: str = LIB_PATH):
     lib.moe_lora_workspace_bytes.restype = ctypes.c_size_t
     lib.moe_lora_align.argtypes = [sp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.moe_lora_align.restype = i32
+    lib.moe_lora_align_timed.argtypes = [sp, vp, vp, vp, ctypes.c_size_t, vp, vp]
+    lib.moe_lora_align_timed.restype = i32
+    lib.moe_lora_align_view.argtypes = [sp, vp, ctypes.POINTER(moe_lora_align_ptrs)]
+    lib.moe_lora_align_view.restype = i32
     lib.moe_lora_route.argtypes = [sp, vp, vp, vp, vp]
     lib.moe_lora_route.restype = i32
     lib.moe_lora_route_align.argtypes = [sp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.moe_lora_route_align.restype = i32
+    lib.moe_lora_route_align_timed.argtypes = [sp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp, vp]
+    lib.moe_lora_route_align_timed.restype = i32
     lib.moe_lora_workspace_view.argtypes = [sp, vp, ctypes.POINTER(moe_lora_views)]
     lib.moe_lora_workspace_view.restype = i32
     lib.moe_lora_forward.argtypes = [sp] + [vp] * 11 + [ctypes.c_size_t, vp, vp]
     lib.moe_lora_forward.restype = i32
+    lib.moe_lora_forward_timed.argtypes = [sp] + [vp] * 11 + [ctypes.c_size_t, vp, vp, vp]
+    lib.moe_lora_forward_timed.restype = i32
     lib.moe_lora_device_errors.argtypes = [sp, vp, ctypes.POINTER(ctypes.c_int32), vp]
     lib.moe_lora_device_errors.restype = i32
     lib.moe_lora_status_str.argtypes = [i32]
@@ -119,11 +135,13 @@ def load_library(path: str = LIB_PATH):
     lib.moe_lora_stage_count.restype = i32
     lib.moe_lora_stage_name.argtypes = [i32]
     lib.moe_lora_stage_name.restype = ctypes.c_char_p
-    lib.moe_lora_profile_begin.argtypes = [i32, ctypes.c_uint32]
-    lib.moe_lora_profile_begin.restype = i32
-    lib.moe_lora_profile_end.argtypes = [ctypes.POINTER(ctypes.c_float), i32,
-                                         ctypes.POINTER(ctypes.c_int)]
-    lib.moe_lora_profile_end.restype = i32
+    lib.moe_lora_profiler_create.argtypes = [i32, ctypes.c_uint32, ctypes.POINTER(vp)]
+    lib.moe_lora_profiler_create.restype = i32
+    lib.moe_lora_profiler_read.argtypes = [vp, ctypes.POINTER(ctypes.c_float), i32,
+                                           ctypes.POINTER(ctypes.c_int)]
+    lib.moe_lora_profiler_read.restype = i32
+    lib.moe_lora_profiler_destroy.argtypes = [vp]
+    lib.moe_lora_profiler_destroy.restype = None
     _lib = lib
     return lib
 
@@ -137,11 +155,60 @@ def _ptr(t, name: str):
     """Device address of a contiguous tensor (None -> NULL)."""
     if t is None:
         return None
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a device tensor")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
     return t.data_ptr()
+
+
+def layer_operand_specs(shape) -> dict:
+    """Expected (shape, dtype name) of every tensor the calls take, from the
+    layer sizes in ``shape``."""
+    T, H, I, E, k, L, r = shape.T, shape.H, shape.I, shape.E, shape.topk, shape.L, shape.r
+    return dict(
+        x=((T, H), "bfloat16"), topk_ids=((T, k), "int32"), topk_weights=((T, k), "float32"),
+        lora_ids=((T,), "int32"), W_gu=((E, 2 * I, H), "bfloat16"), W_down=((E, H, I), "bfloat16"),
+        A_gu=((L, E, r, H), "bfloat16"), B_gu=((L, E, 2 * I, r), "bfloat16"),
+        A_down=((L, E, r, I), "bfloat16"), B_down=((L, E, H, r), "bfloat16"),
+        y=((T, H), "bfloat16"), logits=((T, E), "float32"))
+
+
+def check_operands(shape, workspace=None, **tensors) -> None:
+    """Raise ValueError unless every given tensor has the dtype and shape the
+    kernels assume for ``shape``, is contiguous, and all of them (workspace
+    included) are device tensors on one device; the workspace must be a uint8
+    tensor of at least moe_lora_workspace_bytes(shape) bytes.  Runs before
+    any launch: a wrong dtype (int64 ids from torch.topk, say) or a short
+    weight stack would otherwise be read as something else, or past its end."""
+    specs = layer_operand_specs(shape)
+    devices = set()
+    for name, t in tensors.items():
+        if t is None:
+            raise ValueError(f"{name} is required")
+        want_shape, want_dtype = specs[name]
+        got_dtype = str(t.dtype).replace("torch.", "")
+        if got_dtype != want_dtype:
+            raise ValueError(f"{name}: dtype {got_dtype}, expected {want_dtype}")
+        if tuple(t.shape) != want_shape:
+            raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {want_shape}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        devices.add(t.device)
+    if workspace is not None:
+        if str(workspace.dtype) != "torch.uint8" or workspace.dim() != 1:
+            raise ValueError("workspace must be a 1-D uint8 tensor (alloc_workspace)")
+        need = moe_lora_workspace_bytes(shape)
+        if need == 0:
+            raise MoeLoraError("moe_lora_workspace_bytes", MOE_LORA_EINVAL)
+        if workspace.numel() < need:
+            raise ValueError(f"workspace holds {workspace.numel()} bytes, the shape needs {need}")
+        devices.add(workspace.device)
+    for d in devices:
+        if d.type != "cuda":
+            raise ValueError(f"operands must be device tensors (got one on {d})")
+    if len(devices) > 1:
+        raise ValueError(f"operands on several devices: {sorted(str(d) for d in devices)}")
 
 
 def _stream(stream):
@@ -171,40 +238,61 @@ def alloc_workspace(shape: moe_lora_shape, device="cuda"):
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
+def _prof(profiler):
+    return None if profiler is None else profiler.handle
+
+
 def moe_lora_route(shape, logits, topk_ids, topk_weights, stream=None) -> None:
     """Top-k experts and weights of each token from fp32 logits [T, E] into
     topk_ids [T, k] (int32) and topk_weights [T, k] (fp32)."""
+    check_operands(shape, logits=logits, topk_ids=topk_ids, topk_weights=topk_weights)
     _check("moe_lora_route", load_library().moe_lora_route(
         ctypes.byref(shape), _ptr(logits, "logits"), _ptr(topk_ids, "topk_ids"),
         _ptr(topk_weights, "topk_weights"), _stream(stream)))
 
 
 def moe_lora_route_align(shape, logits, lora_ids, topk_ids, topk_weights, workspace,
-                         stream=None) -> None:
+                         stream=None, profiler=None) -> None:
     """moe_lora_route then moe_lora_align on the routed ids (one kernel for
     small batches)."""
-    _check("moe_lora_route_align", load_library().moe_lora_route_align(
+    check_operands(shape, workspace, logits=logits, lora_ids=lora_ids, topk_ids=topk_ids,
+                   topk_weights=topk_weights)
+    _check("moe_lora_route_align", load_library().moe_lora_route_align_timed(
         ctypes.byref(shape), _ptr(logits, "logits"), _ptr(lora_ids, "lora_ids"),
         _ptr(topk_ids, "topk_ids"), _ptr(topk_weights, "topk_weights"),
         _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
-        _stream(stream)))
+        _stream(stream), _prof(profiler)))
 
 
-def moe_lora_align(shape, topk_ids, lora_ids, workspace, stream=None) -> None:
-    _check("moe_lora_align", load_library().moe_lora_align(
+def moe_lora_align(shape, topk_ids, lora_ids, workspace, stream=None, profiler=None) -> None:
+    check_operands(shape, workspace, topk_ids=topk_ids, lora_ids=lora_ids)
+    _check("moe_lora_align", load_library().moe_lora_align_timed(
         ctypes.byref(shape), _ptr(topk_ids, "topk_ids"), _ptr(lora_ids, "lora_ids"),
         _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
-        _stream(stream)))
+        _stream(stream), _prof(profiler)))
 
 
 def moe_lora_forward(shape, x, topk_ids, topk_weights, lora_ids, W_gu, W_down, A_gu, B_gu,
-                     A_down, B_down, workspace, y, stream=None) -> None:
-    _check("moe_lora_forward", load_library().moe_lora_forward(
+                     A_down, B_down, workspace, y, stream=None, profiler=None) -> None:
+    check_operands(shape, workspace, x=x, topk_ids=topk_ids, topk_weights=topk_weights,
+                   lora_ids=lora_ids, W_gu=W_gu, W_down=W_down, A_gu=A_gu, B_gu=B_gu,
+                   A_down=A_down, B_down=B_down, y=y)
+    _check("moe_lora_forward", load_library().moe_lora_forward_timed(
         ctypes.byref(shape), _ptr(x, "x"), _ptr(topk_ids, "topk_ids"),
         _ptr(topk_weights, "topk_weights"), _ptr(lora_ids, "lora_ids"), _ptr(W_gu, "W_gu"),
         _ptr(W_down, "W_down"), _ptr(A_gu, "A_gu"), _ptr(B_gu, "B_gu"), _ptr(A_down, "A_down"),
         _ptr(B_down, "B_down"), _ptr(workspace, "workspace"),
-        workspace.numel() * workspace.element_size(), _ptr(y, "y"), _stream(stream)))
+        workspace.numel() * workspace.element_size(), _ptr(y, "y"), _stream(stream),
+        _prof(profiler)))
+
+
+def moe_lora_align_view(shape, workspace) -> dict:
+    """Device addresses (ints) of the align outputs in ``workspace``."""
+    v = moe_lora_align_ptrs()
+    _check("moe_lora_align_view", load_library().moe_lora_align_view(
+        ctypes.byref(shape), ctypes.c_void_p(workspace if isinstance(workspace, int)
+                                             else workspace.data_ptr()), ctypes.byref(v)))
+    return {n: getattr(v, n) for n in ALIGN_VIEW_FIELDS}
 
 
 def moe_lora_workspace_view(shape, workspace) -> moe_lora_views:
@@ -242,6 +330,7 @@ def workspace_tensors(shape, workspace) -> dict:
         z_down=region(v.z_down, cap * shape.r, torch.float32).view(cap, shape.r),
         h=region(v.h, cap * shape.I, torch.bfloat16).view(cap, shape.I),
         d=region(v.d, v.d_splits * cap * shape.H, torch.float32).view(v.d_splits, cap, shape.H),
+        h_lo=(region(v.h_lo, cap * shape.I, torch.bfloat16).view(cap, shape.I) if v.h_lo else None),
         cap_rows=cap, cap_blocks=capb, block_m=v.block_m, d_splits=v.d_splits)
 
 
@@ -260,25 +349,42 @@ def moe_lora_stage_name(i: int) -> str:
     return load_library().moe_lora_stage_name(int(i)).decode()
 
 
-def moe_lora_profile_begin(max_calls: int, stages=None) -> None:
-    """Record HIP events around the named stages (all when None) of the next
-    max_calls align+forward calls."""
-    mask = 0xFFFFFFFF
-    if stages is not None:
-        names = [moe_lora_stage_name(i) for i in range(moe_lora_stage_count())]
-        mask = 0
-        for s in stages:
-            mask |= 1 << names.index(s)
-    _check("moe_lora_profile_begin", load_library().moe_lora_profile_begin(int(max_calls), mask))
+class Profiler:
+    """A caller-owned stage-timing recorder (moe_lora_profiler_create): pass
+    it as ``profiler=`` to align / route_align / forward; ``read()`` waits
+    for the recorded events and returns the summed milliseconds per stage
+    name and the number of recorded calls."""
 
+    def __init__(self, max_calls: int, stages=None):
+        mask = 0xFFFFFFFF
+        if stages is not None:
+            names = [moe_lora_stage_name(i) for i in range(moe_lora_stage_count())]
+            mask = 0
+            for st in stages:
+                mask |= 1 << names.index(st)
+        h = ctypes.c_void_p()
+        _check("moe_lora_profiler_create", load_library().moe_lora_profiler_create(
+            int(max_calls), mask, ctypes.byref(h)))
+        self.handle = h
 
-def moe_lora_profile_end() -> tuple[dict, int]:
-    """Summed milliseconds per stage name, and the number of recorded calls."""
-    n = moe_lora_stage_count()
-    arr = (ctypes.c_float * n)()
-    calls = ctypes.c_int(0)
-    _check("moe_lora_profile_end", load_library().moe_lora_profile_end(arr, n, ctypes.byref(calls)))
-    return {moe_lora_stage_name(i): float(arr[i]) for i in range(n)}, int(calls.value)
+    def read(self) -> tuple[dict, int]:
+        n = moe_lora_stage_count()
+        arr = (ctypes.c_float * n)()
+        calls = ctypes.c_int(0)
+        _check("moe_lora_profiler_read", load_library().moe_lora_profiler_read(
+            self.handle, arr, n, ctypes.byref(calls)))
+        return {moe_lora_stage_name(i): float(arr[i]) for i in range(n)}, int(calls.value)
+
+    def close(self) -> None:
+        if self.handle:
+            load_library().moe_lora_profiler_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def fused_moe_lora(x, topk_ids, topk_weights, lora_ids, W_gu, W_down, A_gu, B_gu, A_down, B_down,
@@ -289,10 +395,15 @@ def fused_moe_lora(x, topk_ids, topk_weights, lora_ids, W_gu, W_down, A_gu, B_gu
     int32; W_gu [E,2I,H]; W_down [E,H,I]; A_gu [L,E,r,H]; B_gu [L,E,2I,r];
     A_down [L,E,r,I]; B_down [L,E,H,r] (all bf16)."""
     import torch
+    for name, t, nd in (("x", x, 2), ("topk_ids", topk_ids, 2), ("W_gu", W_gu, 3), ("A_gu", A_gu, 4)):
+        if t.dim() != nd:
+            raise ValueError(f"{name}: {t.dim()} dimensions, expected {nd}")
     T, H = x.shape
     E, twoI, _ = W_gu.shape
     L, _, r, _ = A_gu.shape
     shape = make_shape(T, H, twoI // 2, E, topk_ids.shape[1], L, r, block_m, lora_scale)
+    check_operands(shape, x=x, topk_ids=topk_ids, topk_weights=topk_weights, lora_ids=lora_ids,
+                   W_gu=W_gu, W_down=W_down, A_gu=A_gu, B_gu=B_gu, A_down=A_down, B_down=B_down)
     if workspace is None:
         workspace = alloc_workspace(shape, x.device)
     if y is None:
@@ -305,4 +416,4 @@ def fused_moe_lora(x, topk_ids, topk_weights, lora_ids, W_gu, W_down, A_gu, B_gu
 
 __all__ = [n for n in dir() if n.startswith("moe_lora") or n in (
     "make_shape", "alloc_workspace", "workspace_tensors", "fused_moe_lora", "load_library",
-    "MoeLoraError")]
+    "MoeLoraError", "Profiler", "check_operands", "layer_operand_specs")]

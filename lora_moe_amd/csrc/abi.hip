@@ -2,6 +2,7 @@
 // dispatch and stage timing.  Declarations and contracts: include/moe_lora.h.
 #include <algorithm>
 #include <cmath>
+#include <new>
 #include <vector>
 
 #include "internal.h"
@@ -98,6 +99,7 @@ int make_layout(const moe_lora_shape* s, Layout* L) {
     const int64_t chunks = std::max<int64_t>(1, L->I / 128);
     L->dsplit = (int)std::min<int64_t>(std::min<int64_t>(8, chunks), std::max<int64_t>(1, (1024 + tiles - 1) / tiles));
   }
+  L->hsplit = L->I >= kHsplitMinI;
   size_t o = 0;
   auto take = [&](size_t bytes) {
     size_t at = o;
@@ -118,46 +120,41 @@ int make_layout(const moe_lora_shape* s, Layout* L) {
   L->off_zgu = take(sizeof(float) * L->cap_rows * L->r);
   L->off_zd = take(sizeof(float) * L->cap_rows * L->r);
   L->off_h = take(sizeof(uint16_t) * L->cap_rows * L->I);
+  L->off_hlo = L->hsplit ? take(sizeof(uint16_t) * L->cap_rows * L->I) : 0;
   L->off_d = take(sizeof(float) * L->dsplit * L->cap_rows * L->H);
   L->total = o;
   return MOE_LORA_OK;
 }
 
+}  // namespace moelora
+
 // ------------------------------------------------------------------ stage timing
 
-namespace {
-struct Profiler {
-  bool on = false;
+// A caller-owned recorder: events [call][stage][start, stop] and the stages
+// recorded per call.
+struct moe_lora_profiler {
   int max_calls = 0;
   int call = 0;
   uint32_t mask = 0;
-  std::vector<hipEvent_t> ev;  // [call][stage][start, stop]
+  std::vector<hipEvent_t> ev;
   std::vector<uint32_t> recorded;
 };
-Profiler g_prof;
 
-void prof_release() {
-  for (hipEvent_t e : g_prof.ev) hipEventDestroy(e);
-  g_prof.ev.clear();
-  g_prof.recorded.clear();
-  g_prof.on = false;
-  g_prof.max_calls = g_prof.call = 0;
-}
-}  // namespace
+namespace moelora {
 
-void prof_stage_begin(int stage, hipStream_t st) {
-  if (!g_prof.on || g_prof.call >= g_prof.max_calls || !(g_prof.mask & (1u << stage))) return;
-  hipEventRecord(g_prof.ev[((size_t)g_prof.call * ST_COUNT + stage) * 2], st);
+void prof_stage_begin(moe_lora_profiler* pr, int stage, hipStream_t st) {
+  if (!pr || pr->call >= pr->max_calls || !(pr->mask & (1u << stage))) return;
+  hipEventRecord(pr->ev[((size_t)pr->call * ST_COUNT + stage) * 2], st);
 }
 
-void prof_stage_end(int stage, hipStream_t st) {
-  if (!g_prof.on || g_prof.call >= g_prof.max_calls || !(g_prof.mask & (1u << stage))) return;
-  hipEventRecord(g_prof.ev[((size_t)g_prof.call * ST_COUNT + stage) * 2 + 1], st);
-  g_prof.recorded[g_prof.call] |= 1u << stage;
+void prof_stage_end(moe_lora_profiler* pr, int stage, hipStream_t st) {
+  if (!pr || pr->call >= pr->max_calls || !(pr->mask & (1u << stage))) return;
+  hipEventRecord(pr->ev[((size_t)pr->call * ST_COUNT + stage) * 2 + 1], st);
+  pr->recorded[pr->call] |= 1u << stage;
 }
 
-void prof_call_done() {
-  if (g_prof.on && g_prof.call < g_prof.max_calls) g_prof.call++;
+void prof_call_done(moe_lora_profiler* pr) {
+  if (pr && pr->call < pr->max_calls) pr->call++;
 }
 
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -242,11 +239,29 @@ int moe_lora_workspace_view(const moe_lora_shape* shape, void* workspace, moe_lo
   out->cap_rows = L.cap_rows;
   out->cap_blocks = L.cap_blocks;
   out->block_m = L.bm;
+  out->h_lo = w.hlo;
   return MOE_LORA_OK;
 }
 
-int moe_lora_align(const moe_lora_shape* shape, const int32_t* topk_ids, const int32_t* lora_ids,
-                   void* workspace, size_t ws_bytes, void* stream) {
+int moe_lora_align_view(const moe_lora_shape* shape, const void* workspace, moe_lora_align_ptrs* out) {
+  Layout L;
+  int rc = make_layout(shape, &L);
+  if (rc) return rc;
+  if (!workspace || !out) return MOE_LORA_EINVAL;
+  WsPtrs w = ws_ptrs(const_cast<void*>(workspace), L);
+  out->sorted_ids = w.sorted;
+  out->expert_off = w.eoff;
+  out->seg_start = w.segstart;
+  out->seg_cnt = w.segcnt;
+  out->block_expert = w.bexp;
+  out->pos_of_pair = w.pos;
+  out->num_padded = w.hdr + HDR_NUM_PADDED;
+  out->err_count = w.hdr + HDR_ERR;
+  return MOE_LORA_OK;
+}
+
+int moe_lora_align_timed(const moe_lora_shape* shape, const int32_t* topk_ids, const int32_t* lora_ids,
+                         void* workspace, size_t ws_bytes, void* stream, moe_lora_profiler* prof) {
   Layout L;
   int rc = make_layout(shape, &L);
   if (rc) return rc;
@@ -254,7 +269,12 @@ int moe_lora_align(const moe_lora_shape* shape, const int32_t* topk_ids, const i
   if (!topk_ids || !lora_ids) return MOE_LORA_EINVAL;
   if (!workspace || ws_bytes < L.total) return MOE_LORA_EWORKSPACE;
   if (!aligned16(workspace)) return MOE_LORA_EALIGN;
-  return launch_align(L, topk_ids, lora_ids, workspace, (hipStream_t)stream);
+  return launch_align(L, topk_ids, lora_ids, workspace, (hipStream_t)stream, prof);
+}
+
+int moe_lora_align(const moe_lora_shape* shape, const int32_t* topk_ids, const int32_t* lora_ids,
+                   void* workspace, size_t ws_bytes, void* stream) {
+  return moe_lora_align_timed(shape, topk_ids, lora_ids, workspace, ws_bytes, stream, nullptr);
 }
 
 int moe_lora_route(const moe_lora_shape* shape, const float* logits, int32_t* topk_ids,
@@ -265,15 +285,12 @@ int moe_lora_route(const moe_lora_shape* shape, const float* logits, int32_t* to
   if (L.T == 0) return MOE_LORA_OK;
   if (!logits || !topk_ids || !topk_weights) return MOE_LORA_EINVAL;
   if (L.k > 64) return MOE_LORA_EUNSUPPORTED;
-  prof_stage_begin(ST_ROUTE, (hipStream_t)stream);
-  rc = launch_router(L, logits, topk_ids, topk_weights, (hipStream_t)stream);
-  prof_stage_end(ST_ROUTE, (hipStream_t)stream);
-  return rc;
+  return launch_router(L, logits, topk_ids, topk_weights, (hipStream_t)stream);
 }
 
-int moe_lora_route_align(const moe_lora_shape* shape, const float* logits, const int32_t* lora_ids,
-                         int32_t* topk_ids, float* topk_weights, void* workspace, size_t ws_bytes,
-                         void* stream) {
+int moe_lora_route_align_timed(const moe_lora_shape* shape, const float* logits, const int32_t* lora_ids,
+                               int32_t* topk_ids, float* topk_weights, void* workspace, size_t ws_bytes,
+                               void* stream, moe_lora_profiler* prof) {
   Layout L;
   int rc = make_layout(shape, &L);
   if (rc) return rc;
@@ -282,20 +299,27 @@ int moe_lora_route_align(const moe_lora_shape* shape, const float* logits, const
   if (L.k > 64) return MOE_LORA_EUNSUPPORTED;
   if (!workspace || ws_bytes < L.total) return MOE_LORA_EWORKSPACE;
   if (!aligned16(workspace)) return MOE_LORA_EALIGN;
-  return launch_align(L, topk_ids, lora_ids, workspace, (hipStream_t)stream, logits, topk_ids,
+  return launch_align(L, topk_ids, lora_ids, workspace, (hipStream_t)stream, prof, logits, topk_ids,
                       topk_weights);
 }
 
-int moe_lora_forward(const moe_lora_shape* shape, const uint16_t* x, const int32_t* topk_ids,
-                     const float* topk_weights, const int32_t* lora_ids, const uint16_t* W_gu,
-                     const uint16_t* W_down, const uint16_t* A_gu, const uint16_t* B_gu,
-                     const uint16_t* A_down, const uint16_t* B_down, void* workspace,
-                     size_t ws_bytes, uint16_t* y, void* stream) {
+int moe_lora_route_align(const moe_lora_shape* shape, const float* logits, const int32_t* lora_ids,
+                         int32_t* topk_ids, float* topk_weights, void* workspace, size_t ws_bytes,
+                         void* stream) {
+  return moe_lora_route_align_timed(shape, logits, lora_ids, topk_ids, topk_weights, workspace, ws_bytes,
+                                    stream, nullptr);
+}
+
+int moe_lora_forward_timed(const moe_lora_shape* shape, const uint16_t* x, const int32_t* topk_ids,
+                           const float* topk_weights, const int32_t* lora_ids, const uint16_t* W_gu,
+                           const uint16_t* W_down, const uint16_t* A_gu, const uint16_t* B_gu,
+                           const uint16_t* A_down, const uint16_t* B_down, void* workspace,
+                           size_t ws_bytes, uint16_t* y, void* stream, moe_lora_profiler* prof) {
   Layout L;
   int rc = make_layout(shape, &L);
   if (rc) return rc;
   if (L.T == 0) {
-    prof_call_done();
+    prof_call_done(prof);
     return MOE_LORA_OK;
   }
   const void* ptrs[] = {x, topk_ids, topk_weights, lora_ids, W_gu, W_down, A_gu, B_gu, A_down, B_down, y};
@@ -308,27 +332,36 @@ int moe_lora_forward(const moe_lora_shape* shape, const uint16_t* x, const int32
   hipStream_t st = (hipStream_t)stream;
   WsPtrs w = ws_ptrs(workspace, L);
 
-  prof_stage_begin(ST_SHRINK_GU, st);
+  prof_stage_begin(prof, ST_SHRINK_GU, st);
   rc = launch_shrink(L, 0, x, A_gu, w.zgu, workspace, st);
-  prof_stage_end(ST_SHRINK_GU, st);
+  prof_stage_end(prof, ST_SHRINK_GU, st);
   if (rc) return rc;
-  prof_stage_begin(ST_GEMM_GU, st);
+  prof_stage_begin(prof, ST_GEMM_GU, st);
   rc = launch_gemm(L, 0, x, lora_ids, topk_weights, W_gu, B_gu, workspace, st);
-  prof_stage_end(ST_GEMM_GU, st);
+  prof_stage_end(prof, ST_GEMM_GU, st);
   if (rc) return rc;
-  prof_stage_begin(ST_SHRINK_DOWN, st);
+  prof_stage_begin(prof, ST_SHRINK_DOWN, st);
   rc = launch_shrink(L, 1, w.h, A_down, w.zd, workspace, st);
-  prof_stage_end(ST_SHRINK_DOWN, st);
+  prof_stage_end(prof, ST_SHRINK_DOWN, st);
   if (rc) return rc;
-  prof_stage_begin(ST_GEMM_DOWN, st);
+  prof_stage_begin(prof, ST_GEMM_DOWN, st);
   rc = launch_gemm(L, 1, nullptr, lora_ids, topk_weights, W_down, B_down, workspace, st);
-  prof_stage_end(ST_GEMM_DOWN, st);
+  prof_stage_end(prof, ST_GEMM_DOWN, st);
   if (rc) return rc;
-  prof_stage_begin(ST_COMBINE, st);
+  prof_stage_begin(prof, ST_COMBINE, st);
   rc = launch_combine(L, workspace, y, st);
-  prof_stage_end(ST_COMBINE, st);
-  prof_call_done();
+  prof_stage_end(prof, ST_COMBINE, st);
+  prof_call_done(prof);
   return rc;
+}
+
+int moe_lora_forward(const moe_lora_shape* shape, const uint16_t* x, const int32_t* topk_ids,
+                     const float* topk_weights, const int32_t* lora_ids, const uint16_t* W_gu,
+                     const uint16_t* W_down, const uint16_t* A_gu, const uint16_t* B_gu,
+                     const uint16_t* A_down, const uint16_t* B_down, void* workspace,
+                     size_t ws_bytes, uint16_t* y, void* stream) {
+  return moe_lora_forward_timed(shape, x, topk_ids, topk_weights, lora_ids, W_gu, W_down, A_gu, B_gu,
+                                A_down, B_down, workspace, ws_bytes, y, stream, nullptr);
 }
 
 int moe_lora_device_errors(const moe_lora_shape* shape, const void* workspace, int32_t* host_count,
@@ -370,46 +403,50 @@ const char* moe_lora_stage_name(int stage) {
   return (stage >= 0 && stage < ST_COUNT) ? names[stage] : "unknown";
 }
 
-int moe_lora_profile_begin(int max_calls, uint32_t stage_mask) {
-  if (max_calls <= 0) return MOE_LORA_EINVAL;
-  prof_release();
-  g_prof.ev.resize((size_t)max_calls * ST_COUNT * 2);
-  for (auto& e : g_prof.ev)
+int moe_lora_profiler_create(int max_calls, uint32_t stage_mask, moe_lora_profiler** out) {
+  if (max_calls <= 0 || !out) return MOE_LORA_EINVAL;
+  *out = nullptr;
+  moe_lora_profiler* pr = new (std::nothrow) moe_lora_profiler;
+  if (!pr) return MOE_LORA_EHIP;
+  pr->ev.assign((size_t)max_calls * ST_COUNT * 2, nullptr);
+  for (auto& e : pr->ev)
     // no system-scope fence: a plain event between two kernels adds a
     // ~10 us bubble, which would distort the stages it brackets
     if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) {
       e = nullptr;
-      prof_release();
+      moe_lora_profiler_destroy(pr);
       return MOE_LORA_EHIP;
     }
-  g_prof.recorded.assign(max_calls, 0u);
-  g_prof.max_calls = max_calls;
-  g_prof.call = 0;
-  g_prof.mask = stage_mask;
-  g_prof.on = true;
+  pr->recorded.assign(max_calls, 0u);
+  pr->max_calls = max_calls;
+  pr->mask = stage_mask;
+  *out = pr;
   return MOE_LORA_OK;
 }
 
-int moe_lora_profile_end(float* stage_ms, int n, int* calls) {
-  if (!stage_ms || n < 0 || n > ST_COUNT) return MOE_LORA_EINVAL;
+int moe_lora_profiler_read(moe_lora_profiler* pr, float* stage_ms, int n, int* calls) {
+  if (!pr || !stage_ms || n < 0 || n > ST_COUNT) return MOE_LORA_EINVAL;
   for (int s = 0; s < n; ++s) stage_ms[s] = 0.f;
-  int rc = MOE_LORA_OK;
-  const int ncalls = std::min(g_prof.call, g_prof.max_calls);
-  for (int c = 0; c < ncalls && rc == MOE_LORA_OK; ++c)
+  const int ncalls = std::min(pr->call, pr->max_calls);
+  for (int c = 0; c < ncalls; ++c)
     for (int s = 0; s < n; ++s) {
-      if (!(g_prof.recorded[c] & (1u << s))) continue;
-      hipEvent_t a = g_prof.ev[((size_t)c * ST_COUNT + s) * 2];
-      hipEvent_t b = g_prof.ev[((size_t)c * ST_COUNT + s) * 2 + 1];
+      if (!(pr->recorded[c] & (1u << s))) continue;
+      hipEvent_t a = pr->ev[((size_t)c * ST_COUNT + s) * 2];
+      hipEvent_t b = pr->ev[((size_t)c * ST_COUNT + s) * 2 + 1];
       float ms = 0.f;
-      if (hipEventSynchronize(b) != hipSuccess || hipEventElapsedTime(&ms, a, b) != hipSuccess) {
-        rc = MOE_LORA_EHIP;
-        break;
-      }
+      if (hipEventSynchronize(b) != hipSuccess || hipEventElapsedTime(&ms, a, b) != hipSuccess)
+        return MOE_LORA_EHIP;
       stage_ms[s] += ms;
     }
   if (calls) *calls = ncalls;
-  prof_release();
-  return rc;
+  return MOE_LORA_OK;
+}
+
+void moe_lora_profiler_destroy(moe_lora_profiler* pr) {
+  if (!pr) return;
+  for (hipEvent_t e : pr->ev)
+    if (e) hipEventDestroy(e);
+  delete pr;
 }
 
 }  // extern "C"

@@ -422,7 +422,8 @@ __global__ __launch_bounds__(1024) void align_small_kernel(
 }  // namespace
 
 int launch_align(const Layout& L, const int32_t* topk_ids, const int32_t* lora_ids, void* ws,
-                 hipStream_t st, const float* logits, int32_t* ids_out, float* w_out) {
+                 hipStream_t st, moe_lora_profiler* pr, const float* logits, int32_t* ids_out,
+                 float* w_out) {
   WsPtrs w = ws_ptrs(ws, L);
   const int P = (int)L.P, NB = (int)L.NB, C = (int)L.C;
   if (P <= 0) return MOE_LORA_OK;  // no pairs: nothing to sort
@@ -434,15 +435,15 @@ int launch_align(const Layout& L, const int32_t* topk_ids, const int32_t* lora_i
   // only for decode-sized batches; beyond that its own kernel (a wavefront per
   // token, all tokens at once) runs first and the align reads its output.
   if (logits && !(small && P <= kFusedRouteMaxPairs)) {
-    prof_stage_begin(ST_ROUTE, st);
+    prof_stage_begin(pr, ST_ROUTE, st);
     const int rc = launch_router(L, logits, ids_out, w_out, st);
-    prof_stage_end(ST_ROUTE, st);
+    prof_stage_end(pr, ST_ROUTE, st);
     if (rc) return rc;
     topk_ids = ids_out;
     logits = nullptr;
   }
   if (small) {
-    prof_stage_begin(ST_ALIGN_PLACE, st);
+    prof_stage_begin(pr, ST_ALIGN_PLACE, st);
     const size_t lds = small_lds;
     // one thread per pair (whole wavefronts): fewer wavefronts, cheaper barriers
     const int nthreads = std::min(kSmallMaxPairs, (P + 63) / 64 * 64);
@@ -450,15 +451,15 @@ int launch_align(const Layout& L, const int32_t* topk_ids, const int32_t* lora_i
         logits ? nullptr : topk_ids, lora_ids, P, L.k, L.E, L.L, L.bm, L.cap_rows, L.cap_blocks, (int)L.TS, L.r, zero_gu,
         zero_d, w.hdr, w.sorted, w.eoff, w.segstart, w.segcnt, w.bexp, w.pos, w.tiles, w.zgu, w.zd,
         logits, ids_out, w_out);
-    prof_stage_end(ST_ALIGN_PLACE, st);
+    prof_stage_end(pr, ST_ALIGN_PLACE, st);
     return hipGetLastError() == hipSuccess ? MOE_LORA_OK : MOE_LORA_EHIP;
   }
-  prof_stage_begin(ST_ALIGN_COUNT, st);
+  prof_stage_begin(pr, ST_ALIGN_COUNT, st);
   align_count_kernel<<<C, kAlignChunk, (kAlignChunk + 1 + NB) * sizeof(int), st>>>(
       topk_ids, lora_ids, P, L.k, L.E, L.L, NB, C, w.chunk, w.chunkerr, w.rank);
   align_bucket_scan_kernel<<<(NB + 3) / 4, 256, 0, st>>>(NB, C, w.chunk, w.segcnt);
-  prof_stage_end(ST_ALIGN_COUNT, st);
-  prof_stage_begin(ST_ALIGN_PLACE, st);
+  prof_stage_end(pr, ST_ALIGN_COUNT, st);
+  prof_stage_begin(pr, ST_ALIGN_PLACE, st);
   const size_t off_lds = sizeof(int) * (16 + 2 * (size_t)L.E + 1 + NB);
   if (off_lds > 64 * 1024) {  // above the default dynamic LDS limit (at most 115 KB here)
     static std::atomic<uint64_t> attr_done{0};
@@ -472,7 +473,7 @@ int launch_align(const Layout& L, const int32_t* topk_ids, const int32_t* lora_i
   align_place_kernel<<<(P + 255) / 256, 256, 0, st>>>(topk_ids, lora_ids, P, L.k, L.E, L.L, C, L.r,
                                                       zero_gu, zero_d, w.chunk, w.rank, w.segstart,
                                                       w.sorted, w.pos, w.zgu, w.zd);
-  prof_stage_end(ST_ALIGN_PLACE, st);
+  prof_stage_end(pr, ST_ALIGN_PLACE, st);
   return hipGetLastError() == hipSuccess ? MOE_LORA_OK : MOE_LORA_EHIP;
 }
 

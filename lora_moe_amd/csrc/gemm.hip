@@ -80,8 +80,13 @@ __device__ __forceinline__ float expand_dot(const float* __restrict__ z,
 // layer's down GEMM (32 real rows) fetched half a byte of h per weight byte
 // and ran at 4 TB/s; with 8 its time fell 64 -> 58 us.  With 16-row tiles
 // and 8 wavefronts each thread stages 8 bytes instead of 16.
-template <int MODE, int RF, int NWV>
+//
+// HL (mode 1 only): h arrives as a bf16 pair hi (p.in) + lo (p.in_lo) and
+// each weight fragment meets both, so the product carries h to about 16
+// significant bits; the lo fragments are staged beside the hi ones.
+template <int MODE, int RF, int NWV, bool HL>
 __global__ __launch_bounds__(64 * NWV) void grouped_gemm_kernel(GemmParams p) {
+  static_assert(!HL || MODE == 1, "the hi + lo pair feeds the down GEMM only");
   constexpr int KC = 128;
   // row-fragment pieces staged per thread per chunk; with more threads than
   // 16-byte pieces (16 rows, 8 wavefronts) each thread stages 8 bytes
@@ -90,11 +95,16 @@ __global__ __launch_bounds__(64 * NWV) void grouped_gemm_kernel(GemmParams p) {
   static_assert(HALF ? RF * 8 == NWV : XPT * NWV == RF * 4, "row tile pieces must divide over the threads");
   __shared__ __attribute__((aligned(16))) uint16_t wl[NWV][16 * KC];
   __shared__ __attribute__((aligned(16))) uint16_t xl[2][RF * 16 * KC];
+  __shared__ __attribute__((aligned(16))) uint16_t xll[HL ? 2 : 1][HL ? RF * 16 * KC : 8];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps chunk math scalar
   const int m = lane & 15, kq = lane >> 4;
   const int row0 = blockIdx.y * (RF * 16);
   if (row0 >= p.hdr[HDR_NUM_PADDED]) return;
+  // mode 1 may run on tiles smaller than block_m (h as hi + lo); padding
+  // rows close an expert's run, so a tile whose first row is padding is all
+  // padding and has no output
+  if (MODE == 1 && p.sorted[row0] >= p.P) return;
   const int e = p.bexp[row0 / p.bm];
 
   // weight row held by fragment column c (0..15) of this wavefront
@@ -148,8 +158,8 @@ __global__ __launch_bounds__(64 * NWV) void grouped_gemm_kernel(GemmParams p) {
   const int kbase = kc0 * KC;  // first K element of this split
   const int rot = nfull ? (int)((blockIdx.x * 7u + blockIdx.y * 3u) % (unsigned)nfull) : 0;
 
-  u32x4_t rw[4], rx[XPT];
-  uint2 rxh;  // HALF: this thread's 8 bytes
+  u32x4_t rw[4], rx[XPT], rxl[XPT];
+  uint2 rxh, rxhl;  // HALF: this thread's 8 bytes (hi, lo)
   auto load = [&](int k0, bool masked) {
     const bool ok = !masked || piece * 8 < krem;
 #pragma unroll
@@ -159,11 +169,15 @@ __global__ __launch_bounds__(64 * NWV) void grouped_gemm_kernel(GemmParams p) {
     for (int j = 0; j < XPT; ++j)
     {
       const bool okx = !masked || xpiece * 8 < krem;
-      if (HALF)
-        rxh = okx ? *reinterpret_cast<const uint2*>(p.in + (aoff[j] + (uint32_t)(kbase + k0 + xpiece * 8 + xhalf * 4)))
-                  : make_uint2(0u, 0u);
-      else
-        rx[j] = okx ? ld16(p.in + (aoff[j] + (uint32_t)(kbase + k0 + xpiece * 8))) : zero4();
+      if (HALF) {
+        const uint32_t o = aoff[j] + (uint32_t)(kbase + k0 + xpiece * 8 + xhalf * 4);
+        rxh = okx ? *reinterpret_cast<const uint2*>(p.in + o) : make_uint2(0u, 0u);
+        if (HL) rxhl = okx ? *reinterpret_cast<const uint2*>(p.in_lo + o) : make_uint2(0u, 0u);
+      } else {
+        const uint32_t o = aoff[j] + (uint32_t)(kbase + k0 + xpiece * 8);
+        rx[j] = okx ? ld16(p.in + o) : zero4();
+        if (HL) rxl[j] = okx ? ld16(p.in_lo + o) : zero4();
+      }
     }
   };
   int buf = 0;
@@ -184,12 +198,18 @@ __global__ __launch_bounds__(64 * NWV) void grouped_gemm_kernel(GemmParams p) {
       *reinterpret_cast<u32x4_t*>(&slice[fr * KC + ((piece ^ fr) << 3)]) = rw[i];
     }
     uint16_t* xb = xl[buf];
+    uint16_t* xbl = xll[HL ? buf : 0];
 #pragma unroll
-    for (int j = 0; j < XPT; ++j)
-      if (HALF)
-        *reinterpret_cast<uint2*>(&xb[xr[j] * KC + ((xpiece ^ (xr[j] & 15)) << 3) + xhalf * 4]) = rxh;
-      else
-        *reinterpret_cast<u32x4_t*>(&xb[xr[j] * KC + ((xpiece ^ (xr[j] & 15)) << 3)]) = rx[j];
+    for (int j = 0; j < XPT; ++j) {
+      const int o = xr[j] * KC + ((xpiece ^ (xr[j] & 15)) << 3);
+      if (HALF) {
+        *reinterpret_cast<uint2*>(&xb[o + xhalf * 4]) = rxh;
+        if (HL) *reinterpret_cast<uint2*>(&xbl[o + xhalf * 4]) = rxhl;
+      } else {
+        *reinterpret_cast<u32x4_t*>(&xb[o]) = rx[j];
+        if (HL) *reinterpret_cast<u32x4_t*>(&xbl[o]) = rxl[j];
+      }
+    }
     buf ^= 1;
     if (next_kind) load(next_k0, next_kind == 2);
     lds_barrier();
@@ -199,9 +219,10 @@ __global__ __launch_bounds__(64 * NWV) void grouped_gemm_kernel(GemmParams p) {
           *reinterpret_cast<const u32x4_t*>(&slice[m * KC + (((4 * s + kq) ^ m) << 3)]);
 #pragma unroll
       for (int rf = 0; rf < RF; ++rf) {
-        const u32x4_t a =
-            *reinterpret_cast<const u32x4_t*>(&xb[(rf * 16 + m) * KC + (((4 * s + kq) ^ m) << 3)]);
+        const int o = (rf * 16 + m) * KC + (((4 * s + kq) ^ m) << 3);
+        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(&xb[o]);
         acc[rf] = mfma_16x16x32(a, b, acc[rf]);
+        if (HL) acc[rf] = mfma_16x16x32(*reinterpret_cast<const u32x4_t*>(&xbl[o]), b, acc[rf]);
       }
     }
   };
@@ -241,8 +262,12 @@ __global__ __launch_bounds__(64 * NWV) void grouped_gemm_kernel(GemmParams p) {
       if (MODE == 0) {
         const float up = __shfl_xor(v, 8, 64);  // lane m < 8: gate; m + 8: its up
         const int j = blockIdx.x * (NWV * 8) + wave * 8 + m;
-        if (m < 8 && j < p.I)
-          p.h_out[(size_t)row * p.I + j] = f32_to_bf16(real ? silu_f32(v) * up : 0.f);
+        if (m < 8 && j < p.I) {
+          const float hv = real ? silu_f32(v) * up : 0.f;
+          const uint16_t hb = f32_to_bf16(hv);
+          p.h_out[(size_t)row * p.I + j] = hb;
+          if (p.hlo_out) p.hlo_out[(size_t)row * p.I + j] = f32_to_bf16(hv - bf16_to_f32(hb));
+        }
       } else {
         const int n = blockIdx.x * (NWV * 16) + wave * 16 + m;
         if (real && n < p.N) p.d_out[split * p.d_slab + (size_t)row * p.H + n] = v * p.topk_w[pr];
@@ -250,20 +275,20 @@ __global__ __launch_bounds__(64 * NWV) void grouped_gemm_kernel(GemmParams p) {
     }
 }
 
-template <int MODE, int RF, int NWV>
+template <int MODE, int RF, int NWV, bool HL>
 void launch_nwv(const GemmParams& gp, int64_t cap_rows, hipStream_t st) {
   const int ncol = MODE == 0 ? (gp.I + NWV * 8 - 1) / (NWV * 8) : (gp.H + NWV * 16 - 1) / (NWV * 16);
   dim3 grid(ncol, (unsigned)((cap_rows + RF * 16 - 1) / (RF * 16)), MODE == 1 ? gp.ksplit : 1);
-  grouped_gemm_kernel<MODE, RF, NWV><<<grid, NWV * 64, 0, st>>>(gp);
+  grouped_gemm_kernel<MODE, RF, NWV, HL><<<grid, NWV * 64, 0, st>>>(gp);
 }
 
-template <int MODE, int RF>
+template <int MODE, int RF, bool HL = false>
 void launch_rf(const GemmParams& gp, int64_t cap_rows, hipStream_t st) {
   // 8 wavefronts (128 weight rows) share each tile's staged fragments, except
   // gate_up's 16-row tiles (measured: 233 -> 236 us with 8 at the decode
   // shape, while the down GEMM there went 120 -> 117 us)
   constexpr int NWV = MODE == 0 ? 4 * RF : 8;
-  launch_nwv<MODE, RF, NWV>(gp, cap_rows, st);
+  launch_nwv<MODE, RF, NWV, HL>(gp, cap_rows, st);
 }
 
 }  // namespace
@@ -274,6 +299,8 @@ int launch_gemm(const Layout& L, int mode, const uint16_t* in, const int32_t* lo
   WsPtrs w = ws_ptrs(ws, L);
   GemmParams gp;
   gp.in = mode == 0 ? in : w.h;
+  gp.in_lo = mode == 1 ? w.hlo : nullptr;
+  gp.hlo_out = mode == 0 ? w.hlo : nullptr;
   gp.in_bytes = (uint32_t)((mode == 0 ? L.T * (int64_t)L.H : L.cap_rows * (int64_t)L.I) * 2);
   gp.W = W;
   gp.B = B;
@@ -301,6 +328,13 @@ int launch_gemm(const Layout& L, int mode, const uint16_t* in, const int32_t* lo
   gp.ksplit = mode == 1 ? L.dsplit : 1;
   gp.d_slab = L.cap_rows * (int64_t)L.H;
   gp.s = L.s;
+  if (mode == 1 && L.hsplit) {
+    // h as hi + lo: the streaming kernel, on 16-row tiles at block_m 16 and
+    // 32-row tiles otherwise (block_m is a multiple of 32 then)
+    if (L.bm >= 32) launch_rf<1, 2, true>(gp, L.cap_rows, st);
+    else launch_rf<1, 1, true>(gp, L.cap_rows, st);
+    return hipGetLastError() == hipSuccess ? MOE_LORA_OK : MOE_LORA_EHIP;
+  }
   if (L.bm == 192) {
     const int rc = launch_gemm_dma192(gp, mode, L.cap_rows, st);
     if (rc) return rc;

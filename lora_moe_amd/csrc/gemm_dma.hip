@@ -350,14 +350,22 @@ __global__ __launch_bounds__(C::NT, WAVES_PER_SIMD) void grouped_gemm_dma_kernel
       for (int g = 0; g < 4; ++g) {
         const int j = ntc * (BN / 2) + wn * 32 + 8 * g + 4 * khalf;
         if (j < p.I) {
-          uint32_t hv[4];
+          uint32_t hv[4], lv[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            hv[i] = f32_to_bf16(silu_f32(acc[mi][0][4 * g + i]) * acc[mi][1][4 * g + i]);
+          for (int i = 0; i < 4; ++i) {
+            const float v = silu_f32(acc[mi][0][4 * g + i]) * acc[mi][1][4 * g + i];
+            hv[i] = f32_to_bf16(v);
+            lv[i] = f32_to_bf16(v - bf16_to_f32((uint16_t)hv[i]));
+          }
           uint2 pk;
           pk.x = hv[0] | (hv[1] << 16);
           pk.y = hv[2] | (hv[3] << 16);
           *reinterpret_cast<uint2*>(p.h_out + (size_t)row * p.I + j) = pk;
+          if (p.hlo_out) {  // deep down GEMM: h's bf16 remainder too
+            pk.x = lv[0] | (lv[1] << 16);
+            pk.y = lv[2] | (lv[3] << 16);
+            *reinterpret_cast<uint2*>(p.hlo_out + (size_t)row * p.I + j) = pk;
+          }
         }
       }
     } else {

@@ -18,6 +18,13 @@ namespace moelora {
 constexpr int kAlignChunk = 512;       // pairs per workgroup in the align count pass
 constexpr int kAlignMaxBuckets = 14336;  // E*(L+1) limit: one int per bucket in LDS
 constexpr int kHdrInts = 64;
+// From this intermediate size on, h reaches the down GEMM as a bf16 pair
+// hi + lo (hi = rne(h), lo = rne(h - hi)) instead of hi alone: the rounding
+// of h is the largest error of the layer and grows with the down GEMM's
+// depth I (in an fp64 emulation of the rounding points: 0.885 of the
+// tolerance at I = 11008 and 2.41 at I = 25600 with bf16 h, 0.31 and 0.35
+// with the pair; 0.29 at I = 2880)
+constexpr int kHsplitMinI = 4096;
 
 // header slots (int32) at the start of the workspace
 enum { HDR_NUM_PADDED = 0, HDR_ERR = 1, HDR_NTILES = 2 };
@@ -28,8 +35,9 @@ struct Layout {
   float s;
   int64_t P, cap_rows, cap_blocks, NB, C, TS, max_tiles;
   int dsplit;  // K splits of the down GEMM (d holds one partial slab per split)
+  int hsplit;  // h also stored as its bf16 remainder lo (I >= kHsplitMinI)
   size_t off_hdr, off_sorted, off_eoff, off_segstart, off_segcnt, off_bexp, off_pos;
-  size_t off_chunk, off_chunkerr, off_rank, off_tiles, off_zgu, off_zd, off_h, off_d, total;
+  size_t off_chunk, off_chunkerr, off_rank, off_tiles, off_zgu, off_zd, off_h, off_hlo, off_d, total;
 };
 
 // Fills `L` from the shape; returns MOE_LORA_OK or an error code.
@@ -57,6 +65,7 @@ struct WsPtrs {
   float* zgu;
   float* zd;
   uint16_t* h;
+  uint16_t* hlo;  // nullptr unless hsplit
   float* d;
 };
 
@@ -77,6 +86,7 @@ inline WsPtrs ws_ptrs(void* base, const Layout& L) {
   w.zgu = reinterpret_cast<float*>(b + L.off_zgu);
   w.zd = reinterpret_cast<float*>(b + L.off_zd);
   w.h = reinterpret_cast<uint16_t*>(b + L.off_h);
+  w.hlo = L.hsplit ? reinterpret_cast<uint16_t*>(b + L.off_hlo) : nullptr;
   w.d = reinterpret_cast<float*>(b + L.off_d);
   return w;
 }
@@ -84,6 +94,7 @@ inline WsPtrs ws_ptrs(void* base, const Layout& L) {
 // Arguments of the grouped GEMM kernels (both families).
 struct GemmParams {
   const uint16_t* in;      // mode 0: x [T][K]; mode 1: h [cap_rows][K]
+  const uint16_t* in_lo;   // mode 1 with hsplit: h's bf16 remainder [cap_rows][K]
   uint32_t in_bytes;       // size of that buffer (< 2^31, checked by the ABI)
   const uint16_t* W;       // [E][N][K]
   const uint16_t* B;       // [L][E][N][r]
@@ -96,6 +107,7 @@ struct GemmParams {
   const int32_t* lora_ids;
   const float* topk_w;
   uint16_t* h_out;         // mode 0: [cap_rows][I]
+  uint16_t* hlo_out;       // mode 0 with hsplit: h - rne(h), bf16 [cap_rows][I]; else nullptr
   float* d_out;            // mode 1: [cap_rows][H]
   int K, N, I, H, E, L, r, topk, P, bm, nsteps;
   int ncol, nrowt;  // tiled family: column tiles and row tiles of the launch
@@ -118,10 +130,11 @@ enum Stage {
   ST_COUNT
 };
 
-// Records stage start/stop events around a launch when profiling is on.
-void prof_stage_begin(int stage, hipStream_t st);
-void prof_stage_end(int stage, hipStream_t st);
-void prof_call_done();
+// Stage start/stop events recorded into a caller-owned profiler (nullptr:
+// nothing is recorded); a call counts once its forward is enqueued.
+void prof_stage_begin(moe_lora_profiler* pr, int stage, hipStream_t st);
+void prof_stage_end(moe_lora_profiler* pr, int stage, hipStream_t st);
+void prof_call_done(moe_lora_profiler* pr);
 
 // ------------------------------------------------------------------ launchers
 
@@ -144,8 +157,8 @@ inline int ensure_dynamic_lds(const void* fn, int bytes, std::atomic<uint64_t>& 
 // logits != nullptr: route first (top-k and weights from logits [T][E]) into
 // ids_out / w_out, then align on those ids; topk_ids is then unused.
 int launch_align(const Layout& L, const int32_t* topk_ids, const int32_t* lora_ids, void* ws,
-                 hipStream_t st, const float* logits = nullptr, int32_t* ids_out = nullptr,
-                 float* w_out = nullptr);
+                 hipStream_t st, moe_lora_profiler* pr, const float* logits = nullptr,
+                 int32_t* ids_out = nullptr, float* w_out = nullptr);
 int launch_router(const Layout& L, const float* logits, int32_t* ids, float* w, hipStream_t st);
 
 struct ShrinkPlan {

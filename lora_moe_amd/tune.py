@@ -1,12 +1,14 @@
 """Offline sweep for the tile-configuration table (GPU).
 
 For each synthetic workload, times ``moe_lora_align + moe_lora_forward`` at
-every block_m the library has tiles for (16, 32 and 64: the register-streaming
-GEMM; 128 and 256: the LDS-DMA GEMM; block_m also sets the align padding and
-the shrink tile), and writes the fastest per shape class as a table that
+every block_m the library has tiles for (16 and 32: the register-streaming
+GEMM; 64, 128, 192 and 256: the LDS-DMA GEMM with 64 x 128, 128 x 128,
+192 x 256 and 256 x 256 tiles; block_m also sets the align padding and the
+shrink tile), and writes the fastest per shape class as a table that
 ``load_tuning`` / ``moe_lora_tune_block_m`` read.  The pages tune their
 kernel configurations per shape in the same spirit ("Multi-LoRA for MoE
-models", section "Kernel optimizations").
+models", section "Tuning kernel configurations for Amazon SageMaker AI and
+Amazon Bedrock").
 
     python -m lora_moe_amd.tune --workloads 2,3,4,5,6 --out lora_moe_amd/tuning/gfx950.json
 """

@@ -317,12 +317,16 @@ def device_inputs(wl, seed=None, touched_only=True, device="cuda", keep_host=Fal
         if keep_host:
             host_w[spec.name][spec.index].reshape(-1)[:] = buf
     inp = Inputs(wl, x, topk_ids, topk_weights, lora_ids, **host_w)
+    inp.extra["host_weights"] = bool(keep_host)  # host stacks hold every slab drawn
     return dev, inp
 
 
 def host_slabs_for_tokens(inp: Inputs, tokens) -> None:
     """Fill the host weight stacks of ``inp`` with the slabs that the given
-    tokens read (for a CPU reference on a sample of tokens)."""
+    tokens read (for a CPU reference on a sample of tokens).  A no-op when
+    the bundle already holds every drawn slab (device_inputs(keep_host=True))."""
+    if inp.extra.get("host_weights"):
+        return
     wl = inp.wl
     ids = inp.topk_ids[tokens]
     lids = inp.lora_ids[tokens]

@@ -24,14 +24,11 @@ def shape_for(wl, block_m=0):
 
 
 def check_shapes(dev, wl):
-    """Host-side check that operand shapes match what the kernels assume."""
-    T, H, I, E, k, L, r = wl.T, wl.H, wl.I, wl.E, wl.topk, wl.L, wl.r
-    want = dict(x=(T, H), topk_ids=(T, k), topk_weights=(T, k), lora_ids=(T,), W_gu=(E, 2 * I, H),
-                W_down=(E, H, I), A_gu=(L, E, r, H), B_gu=(L, E, 2 * I, r), A_down=(L, E, r, I),
-                B_down=(L, E, H, r))
-    for n, s in want.items():
-        assert tuple(dev[n].shape) == s, (n, tuple(dev[n].shape), s)
-        assert dev[n].is_contiguous(), n
+    """Host-side check that operand dtypes and shapes match what the kernels
+    assume (the package's own check, run before every launch anyway)."""
+    lm.check_operands(shape_for(wl), **{n: dev[n] for n in (
+        "x", "topk_ids", "topk_weights", "lora_ids", "W_gu", "W_down", "A_gu", "B_gu", "A_down",
+        "B_down")})
 
 
 def run_gpu(dev, wl, block_m=0, lora_ids=None, workspace=None):
@@ -61,20 +58,10 @@ def to_device(inp):
     return out
 
 
-def dense_tol_scale(I):
-    """Tolerance factor for layers beyond the stated workloads' down-projection
-    depth.  The dominant error is h rounded to bf16 (relative 2^-9 per element)
-    feeding the down GEMM, so its absolute size grows with sqrt(I); the stated
-    tolerance holds with margin up to I = 2048 at the DeepSeek-like shape
-    (max err/tol ~0.7), so a layer with larger I gets sqrt(I / 2048)."""
-    return max(1.0, float(np.sqrt(I / 2048.0)))
-
-
-def compare(y_gpu, y_ref, what="", tol_scale=1.0):
-    """Element-wise |gpu - ref| <= atol + rtol*|ref| (both times tol_scale) and
-    relative L2 <= 1e-2."""
+def compare(y_gpu, y_ref, what=""):
+    """Element-wise |gpu - ref| <= 1e-2 + 1e-2*|ref| and relative L2 <= 1e-2."""
     err = np.abs(y_gpu - y_ref)
-    bound = tol_scale * (ATOL + RTOL * np.abs(y_ref))
+    bound = ATOL + RTOL * np.abs(y_ref)
     bad = err > bound
     rel_l2 = float(np.linalg.norm(y_gpu - y_ref) / max(np.linalg.norm(y_ref), 1e-30))
     worst = float(np.max(err / bound)) if err.size else 0.0

@@ -182,3 +182,87 @@ def test_committed_tuning_table_is_valid(lib):
         wl = byname[e["workload"]]
         shape = lm.make_shape(wl.T, wl.H, wl.I, wl.E, wl.topk, wl.L, wl.r, 0, wl.scale, tuning=table)
         assert shape.block_m == e["block_m"]
+
+
+# ------------------------------------------------------------------ views, operand checks, h hi + lo
+
+FAKE_BASE = 1 << 20
+
+
+def _fake_ws():
+    return type("T", (), {"is_cuda": True, "is_contiguous": lambda self: True,
+                          "data_ptr": lambda self: FAKE_BASE})()
+
+
+@pytest.mark.parametrize("n", [1, 3, 5])
+def test_align_view_matches_workspace_view(lib, n):
+    """moe_lora_align_view (host only) points at the same align regions as
+    moe_lora_workspace_view, and refuses a null workspace or output."""
+    s = shape_of(synth.WORKLOADS[n])
+    v = lm.moe_lora_workspace_view(s, _fake_ws())
+    a = lm.moe_lora_align_view(s, FAKE_BASE)
+    for name in lm.ALIGN_VIEW_FIELDS:
+        assert a[name] == getattr(v, name), name
+    assert lib.moe_lora_align_view(ctypes.byref(s), None, ctypes.byref(lm.moe_lora_align_ptrs())) == \
+        lm.MOE_LORA_EINVAL
+    assert lib.moe_lora_align_view(ctypes.byref(s), FAKE_BASE, None) == lm.MOE_LORA_EINVAL
+    bad = lm.make_shape(4, 64, 32, 4, 2, 2, 12)
+    assert lib.moe_lora_align_view(ctypes.byref(bad), FAKE_BASE, ctypes.byref(lm.moe_lora_align_ptrs())) == \
+        lm.MOE_LORA_EUNSUPPORTED
+
+
+@pytest.mark.parametrize("I,split", [(2048, False), (4088, False), (4096, True), (25600, True)])
+def test_h_lo_region_from_4096(lib, I, split):
+    """From I = 4096 on the workspace holds h's bf16 remainder beside h."""
+    s = lm.make_shape(32, 512, I, 4, 2, 2, 16)
+    v = lm.moe_lora_workspace_view(s, _fake_ws())
+    assert bool(v.h_lo) == split
+    if split:
+        assert v.h_lo % 256 == 0 and v.h_lo >= v.h + v.cap_rows * I * 2
+        assert v.d >= v.h_lo + v.cap_rows * I * 2
+
+
+def test_operand_checks_refuse_before_launch():
+    """Wrong dtypes, shapes, non-contiguous or host tensors are refused with
+    ValueError before anything is launched (CPU tensors: the device check
+    comes last, so dtype and shape errors are seen first)."""
+    torch = pytest.importorskip("torch")
+    T, H, I, E, k, L, r = 6, 64, 32, 4, 2, 3, 8
+    shape = lm.make_shape(T, H, I, E, k, L, r)
+    bf = torch.bfloat16
+    ok = dict(x=torch.zeros(T, H, dtype=bf), topk_ids=torch.zeros(T, k, dtype=torch.int32),
+              topk_weights=torch.zeros(T, k), lora_ids=torch.zeros(T, dtype=torch.int32),
+              W_gu=torch.zeros(E, 2 * I, H, dtype=bf), W_down=torch.zeros(E, H, I, dtype=bf),
+              A_gu=torch.zeros(L, E, r, H, dtype=bf), B_gu=torch.zeros(L, E, 2 * I, r, dtype=bf),
+              A_down=torch.zeros(L, E, r, I, dtype=bf), B_down=torch.zeros(L, E, H, r, dtype=bf))
+    ws = torch.zeros(lm.moe_lora_workspace_bytes(shape), dtype=torch.uint8)
+    y = torch.zeros(T, H, dtype=bf)
+
+    def forward(**over):
+        a = dict(ok, **over)
+        lm.moe_lora_forward(shape, a["x"], a["topk_ids"], a["topk_weights"], a["lora_ids"], a["W_gu"],
+                            a["W_down"], a["A_gu"], a["B_gu"], a["A_down"], a["B_down"], ws, y)
+
+    cases = [
+        (dict(topk_ids=ok["topk_ids"].long()), "topk_ids: dtype int64"),      # torch.topk's dtype
+        (dict(lora_ids=ok["lora_ids"].long()), "lora_ids: dtype int64"),
+        (dict(topk_weights=ok["topk_weights"].half()), "topk_weights: dtype float16"),
+        (dict(x=ok["x"].float()), "x: dtype float32"),
+        (dict(W_down=torch.zeros(E, H, I - 8, dtype=bf)), "W_down: shape"),
+        (dict(B_gu=torch.zeros(L, E, I, r, dtype=bf)), "B_gu: shape"),
+        (dict(B_down=torch.zeros(L - 1, E, H, r, dtype=bf)), "B_down: shape"),
+        (dict(x=torch.zeros(H, T, dtype=bf).t()), "x must be contiguous"),
+        ({}, "device tensors"),
+    ]
+    for over, msg in cases:
+        with pytest.raises(ValueError, match=msg):
+            forward(**over)
+    with pytest.raises(ValueError, match="topk_ids: dtype int64"):
+        lm.moe_lora_align(shape, ok["topk_ids"].long(), ok["lora_ids"], ws)
+    with pytest.raises(ValueError, match="workspace holds"):
+        lm.moe_lora_align(shape, ok["topk_ids"], ok["lora_ids"], ws[:16])
+    with pytest.raises(ValueError, match="dtype int64"):
+        lm.fused_moe_lora(ok["x"], ok["topk_ids"].long(), ok["topk_weights"], ok["lora_ids"],
+                          ok["W_gu"], ok["W_down"], ok["A_gu"], ok["B_gu"], ok["A_down"], ok["B_down"])
+    with pytest.raises(ValueError, match="logits: shape"):
+        lm.moe_lora_route(shape, torch.zeros(T, E + 1), ok["topk_ids"], ok["topk_weights"])

@@ -10,8 +10,8 @@ import numpy as np
 import pytest
 
 import synth
-from gpu_common import (compare, compare_delta, dense_tol_scale, gpu_views, log, oracle_tokens, run_gpu,
-                        sample_tokens, shape_for, to_device)
+from gpu_common import (compare, compare_delta, gpu_views, log, oracle_tokens, run_gpu, sample_tokens,
+                        shape_for, to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -94,7 +94,7 @@ def full_check(inp, block_m=0, what="", scale=None, errors=0):
     log(f"layer {what}: T={wl.T} H={wl.H} I={wl.I} E={wl.E} k={wl.topk} L={wl.L} r={wl.r} bm={block_m}")
     dev = to_device(inp)
     y, shape, ws = run_gpu(dev, wl, block_m)
-    # invalid ids plus GEMM waits for in-launch shrink workgroups that gave up
+    # the invalid ids the align met
     assert lm.moe_lora_device_errors(shape, ws) == errors, what
     ref = oracle_tokens(inp, None)
     compare(y, ref, what)
@@ -249,28 +249,94 @@ def test_exact_small_integer_layer(bm, shape):
 
 # ------------------------------------------------------------------ full-size workloads
 
-@pytest.mark.parametrize("n,ntok", [(2, 16), (3, 24), (4, 24), (5, 8), (6, 16)])
-def test_workload_full_size_sampled(n, ntok):
-    """The benchmarked launch configuration at full size; the reference runs on
-    a sample of tokens."""
+def full_size_tokens(n, wl, inp, shape, ws):
+    """Tokens the reference checks at full size: every token of workloads 2,
+    3, 4 and 6; for the DeepSeek-like one 256 seeded tokens plus the tokens
+    of the hot expert's first and last row tiles and of every expert whose
+    rows fit one tile (from the align outputs of the run under test)."""
+    if n != 5:
+        return np.arange(wl.T, dtype=np.int32)
+    v = gpu_views(shape, ws)
+    bm, P = v["block_m"], wl.T * wl.topk
+    eoff, sorted_ids = v["expert_off"], v["sorted_ids"]
+    counts = np.bincount(inp.topk_ids.reshape(-1), minlength=wl.E)
+    hot = int(np.argmax(counts))
+    pick = set(sample_tokens(wl.T, 256).tolist())
+    first = sorted_ids[eoff[hot]:eoff[hot] + bm]
+    last_tile = eoff[hot] + (counts[hot] - 1) // bm * bm
+    last = sorted_ids[last_tile:eoff[hot + 1]]
+    for rows in (first[:8], first[-8:], last[:8], last[last < P][-8:]):
+        pick |= {int(p) // wl.topk for p in rows if p < P}
+    single = [e for e in range(wl.E) if 0 < counts[e] <= bm]
+    for e in single[:16]:
+        pr = sorted_ids[eoff[e]]
+        pick.add(int(pr) // wl.topk)
+    log(f"workload 5: hot expert {hot} ({counts[hot]} rows, tiles {eoff[hot]}..{eoff[hot + 1]}), "
+        f"{len(single)} single-tile experts, {len(pick)} tokens")
+    return np.array(sorted(pick), dtype=np.int32)
+
+
+@pytest.mark.parametrize("n", [2, 3, 4, 5, 6])
+def test_workload_full_size(n):
+    """The benchmarked launch configuration at full size against the
+    reference: every token of workloads 2-4 and 6, a few hundred chosen
+    tokens of the DeepSeek-like one (its reference costs seconds per hundred
+    tokens); the stated tolerance everywhere."""
+    import lora_moe_amd as lm
     wl = synth.WORKLOADS[n]
     log(f"workload {n} ({wl.name}): generating on device")
-    dev, inp = synth.device_inputs(wl, touched_only=True)
-    toks = sample_tokens(wl.T, ntok)
-    synth.host_slabs_for_tokens(inp, toks)
+    dev, inp = synth.device_inputs(wl, touched_only=True, keep_host=True)
     y, shape, ws = run_gpu(dev, wl)
-    import lora_moe_amd as lm
-    assert lm.moe_lora_device_errors(shape, ws) == 0  # no shrink wait gave up
+    assert lm.moe_lora_device_errors(shape, ws) == 0
+    toks = full_size_tokens(n, wl, inp, shape, ws)
     ref = oracle_tokens(inp, toks)
-    # workloads 2-5 take the stated tolerance; the dense one (not among the
-    # stated workloads, I = 25600) the one scaled for its down-projection depth
-    ts = 1.0 if n <= 5 else dense_tol_scale(wl.I)
-    compare(y[toks], ref, f"workload {n}", ts)
+    compare(y[toks], ref, f"workload {n}, {len(toks)} tokens")
     none = torch.full_like(dev["lora_ids"], -1)
     y0, _, _ = run_gpu(dev, wl, lora_ids=none, workspace=ws)
     ref0 = oracle_tokens(inp, toks, lora_ids=np.full_like(inp.lora_ids, -1))
-    compare(y0[toks], ref0, f"workload {n} (no adapters)", ts)
+    compare(y0[toks], ref0, f"workload {n} (no adapters)")
     compare_delta(y[toks], y0[toks], ref, ref0, f"workload {n}")
     assert np.all(np.isfinite(y))
     del dev, ws
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("bm", [0, 16, 32, 64, 128, 256])
+def test_deep_intermediate_hi_lo(bm):
+    """I >= 4096: h reaches the down GEMM as bf16 hi + lo (the streaming
+    kernel, whatever block_m) -- the lo part is written and is the remainder
+    of h, and the layer meets the stated tolerance."""
+    import lora_moe_amd as lm
+    wl = synth.Workload("deep", T=40, H=512, I=4104, E=3, topk=2, L=3, r=16,
+                        lora_mode="uniform_with_none", seed=4)
+    inp = synth.make_inputs(wl)
+    full_check(inp, bm, f"deep I={wl.I} bm={bm}")
+    dev = to_device(inp)
+    _, shape, ws = run_gpu(dev, wl, bm)
+    t = lm.workspace_tensors(shape, ws)
+    assert t["h_lo"] is not None
+    pos = t["pos_of_pair"].cpu().numpy()
+    rows = pos[pos >= 0]
+    hi = t["h"][torch.from_numpy(rows).cuda().long()].float()
+    lo = t["h_lo"][torch.from_numpy(rows).cuda().long()].float()
+    # lo is what rounding h to bf16 left: at most half an ulp of hi
+    ulp = torch.where(hi != 0, hi.abs() * 2.0 ** -7, torch.full_like(hi, 2.0 ** -126))
+    assert bool((lo.abs() <= 0.5 * ulp + 1e-30).all())
+    assert float(lo.abs().max()) > 0
+
+
+def test_forward_needs_its_own_align():
+    """Each forward follows an align of its own (the align clears the split-K
+    shrink accumulators): align + forward twice on one workspace gives the
+    reference both times, at a decode shape whose shrinks split K."""
+    import lora_moe_amd as lm
+    wl = synth.Workload("forward-rule", T=16, H=2048, I=512, E=8, topk=2, L=4, r=16,
+                        lora_mode="uniform_with_none", seed=8)
+    inp = synth.make_inputs(wl)
+    dev = to_device(inp)
+    ref = oracle_tokens(inp, None)
+    shape = shape_for(wl)
+    ws = lm.alloc_workspace(shape)
+    for rep in range(2):
+        y, _, _ = run_gpu(dev, wl, workspace=ws)
+        compare(y, ref, f"align + forward, call {rep}")
