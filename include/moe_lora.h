@@ -223,6 +223,27 @@ int moe_lora_forward(const moe_lora_shape* shape, const uint16_t* x, const int32
                      const uint16_t* A_down, const uint16_t* B_down, void* workspace,
                      size_t ws_bytes, uint16_t* y, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): align +
+ * forward in one call, with the workspace in a static device array of
+ * MOE_LORA_NOALLOC_WORKSPACE_BYTES that the library holds on each GPU it
+ * runs on until the process ends.  Arguments as in moe_lora_forward (the
+ * caller still owns x, the ids, the weights and y); the same kernels and
+ * results as moe_lora_align + moe_lora_forward.  Returns
+ * MOE_LORA_EWORKSPACE, without launching anything, when the shape's
+ * workspace (moe_lora_workspace_bytes) exceeds that size -- decode batches
+ * and the GPT-OSS-20B-like layer fit, a 2048-token prefill does not.  Calls
+ * no allocating routine.  Every call on one GPU uses that GPU's one array:
+ * calls that overlap on a GPU (two streams, two host threads) race and give
+ * wrong results; order them on one stream.  The invalid-id count of these
+ * calls is not exposed (moe_lora_device_errors needs a caller workspace). */
+#define MOE_LORA_NOALLOC_WORKSPACE_BYTES (64u << 20)
+int moe_lora_forward_noalloc(const moe_lora_shape* shape, const uint16_t* x, const int32_t* topk_ids,
+                             const float* topk_weights, const int32_t* lora_ids, const uint16_t* W_gu,
+                             const uint16_t* W_down, const uint16_t* A_gu, const uint16_t* B_gu,
+                             const uint16_t* A_down, const uint16_t* B_down, uint16_t* y,
+                             void* stream);
+
 /* Number of invalid ids the last align on `workspace` met.  Synchronises
  * `stream` (the only call here that waits for the GPU). */
 int moe_lora_device_errors(const moe_lora_shape* shape, const void* workspace,

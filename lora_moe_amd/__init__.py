@@ -20,6 +20,7 @@ MOE_LORA_EALIGN = -2
 MOE_LORA_EWORKSPACE = -3
 MOE_LORA_EUNSUPPORTED = -4
 MOE_LORA_EHIP = -5
+MOE_LORA_NOALLOC_WORKSPACE_BYTES = 64 << 20  # the static workspace of moe_lora_forward_noalloc
 
 _lib = None
 
@@ -127,6 +128,8 @@ def load_library(path: str = LIB_PATH):
     lib.moe_lora_forward.restype = i32
     lib.moe_lora_forward_timed.argtypes = [sp] + [vp] * 11 + [ctypes.c_size_t, vp, vp, vp]
     lib.moe_lora_forward_timed.restype = i32
+    lib.moe_lora_forward_noalloc.argtypes = [sp] + [vp] * 11 + [vp]
+    lib.moe_lora_forward_noalloc.restype = i32
     lib.moe_lora_device_errors.argtypes = [sp, vp, ctypes.POINTER(ctypes.c_int32), vp]
     lib.moe_lora_device_errors.restype = i32
     lib.moe_lora_status_str.argtypes = [i32]
@@ -284,6 +287,21 @@ def moe_lora_forward(shape, x, topk_ids, topk_weights, lora_ids, W_gu, W_down, A
         _ptr(B_down, "B_down"), _ptr(workspace, "workspace"),
         workspace.numel() * workspace.element_size(), _ptr(y, "y"), _stream(stream),
         _prof(profiler)))
+
+
+def moe_lora_forward_noalloc(shape, x, topk_ids, topk_weights, lora_ids, W_gu, W_down, A_gu, B_gu,
+                             A_down, B_down, y, stream=None) -> None:
+    """Align + forward with the library's static workspace (for callers that
+    cannot allocate); shapes whose workspace exceeds
+    MOE_LORA_NOALLOC_WORKSPACE_BYTES raise MoeLoraError (EWORKSPACE)."""
+    check_operands(shape, x=x, topk_ids=topk_ids, topk_weights=topk_weights, lora_ids=lora_ids,
+                   W_gu=W_gu, W_down=W_down, A_gu=A_gu, B_gu=B_gu, A_down=A_down, B_down=B_down,
+                   y=y)
+    _check("moe_lora_forward_noalloc", load_library().moe_lora_forward_noalloc(
+        ctypes.byref(shape), _ptr(x, "x"), _ptr(topk_ids, "topk_ids"),
+        _ptr(topk_weights, "topk_weights"), _ptr(lora_ids, "lora_ids"), _ptr(W_gu, "W_gu"),
+        _ptr(W_down, "W_down"), _ptr(A_gu, "A_gu"), _ptr(B_gu, "B_gu"), _ptr(A_down, "A_down"),
+        _ptr(B_down, "B_down"), _ptr(y, "y"), _stream(stream)))
 
 
 def moe_lora_align_view(shape, workspace) -> dict:
