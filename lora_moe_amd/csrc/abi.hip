@@ -119,6 +119,8 @@ int make_layout(const moe_lora_shape* s, Layout* L) {
   L->off_tiles = take(sizeof(LoraTile) * L->max_tiles);
   L->off_zgu = take(sizeof(float) * L->cap_rows * L->r);
   L->off_zd = take(sizeof(float) * L->cap_rows * L->r);
+  L->off_zbgu = take(sizeof(uint16_t) * L->cap_rows * L->r);
+  L->off_zbd = take(sizeof(uint16_t) * L->cap_rows * L->r);
   L->off_h = take(sizeof(uint16_t) * L->cap_rows * L->I);
   L->off_hlo = L->hsplit ? take(sizeof(uint16_t) * L->cap_rows * L->I) : 0;
   L->off_d = take(sizeof(float) * L->dsplit * L->cap_rows * L->H);
@@ -333,7 +335,7 @@ int moe_lora_forward_timed(const moe_lora_shape* shape, const uint16_t* x, const
   WsPtrs w = ws_ptrs(workspace, L);
 
   prof_stage_begin(prof, ST_SHRINK_GU, st);
-  rc = launch_shrink(L, 0, x, A_gu, w.zgu, workspace, st);
+  rc = launch_shrink(L, 0, x, A_gu, w.zgu, w.zbgu, workspace, st);
   prof_stage_end(prof, ST_SHRINK_GU, st);
   if (rc) return rc;
   prof_stage_begin(prof, ST_GEMM_GU, st);
@@ -341,7 +343,7 @@ int moe_lora_forward_timed(const moe_lora_shape* shape, const uint16_t* x, const
   prof_stage_end(prof, ST_GEMM_GU, st);
   if (rc) return rc;
   prof_stage_begin(prof, ST_SHRINK_DOWN, st);
-  rc = launch_shrink(L, 1, w.h, A_down, w.zd, workspace, st);
+  rc = launch_shrink(L, 1, w.h, A_down, w.zd, w.zbd, workspace, st);
   prof_stage_end(prof, ST_SHRINK_DOWN, st);
   if (rc) return rc;
   prof_stage_begin(prof, ST_GEMM_DOWN, st);
@@ -445,7 +447,7 @@ int moe_lora_profiler_read(moe_lora_profiler* pr, float* stage_ms, int n, int* c
 void moe_lora_profiler_destroy(moe_lora_profiler* pr) {
   if (!pr) return;
   for (hipEvent_t e : pr->ev)
-    if (e) hipEventDestroy(e);
+    if (e) (void)hipEventDestroy(e);
   delete pr;
 }
 

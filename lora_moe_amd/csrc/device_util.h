@@ -69,18 +69,6 @@ __device__ __forceinline__ u32x4_t zero4() {
   return z;
 }
 
-// 8 fp32 values -> bf16 hi and lo parts, packed two per word
-__device__ __forceinline__ void split8(const float* v, u32x4_t& hi, u32x4_t& lo) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint16_t h0 = f32_to_bf16(v[2 * i]), h1 = f32_to_bf16(v[2 * i + 1]);
-    const uint16_t l0 = f32_to_bf16(v[2 * i] - bf16_to_f32(h0));
-    const uint16_t l1 = f32_to_bf16(v[2 * i + 1] - bf16_to_f32(h1));
-    hi[i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-    lo[i] = (uint32_t)l0 | ((uint32_t)l1 << 16);
-  }
-}
-
 __device__ __forceinline__ float silu_f32(float v) { return v / (1.0f + __expf(-v)); }
 
 // Workgroup barrier that orders LDS traffic only: each wavefront waits for

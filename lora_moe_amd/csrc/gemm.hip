@@ -305,6 +305,7 @@ int launch_gemm(const Layout& L, int mode, const uint16_t* in, const int32_t* lo
   gp.W = W;
   gp.B = B;
   gp.z = mode == 0 ? w.zgu : w.zd;
+  gp.zb = mode == 0 ? w.zbgu : w.zbd;
   gp.sorted = w.sorted;
   gp.bexp = w.bexp;
   gp.segstart = w.segstart;

@@ -32,7 +32,7 @@
 //     columns of one row, written with one 8-byte (h, bf16) or 16-byte (d,
 //     fp32) store;
 //   * epilogue: the expand (lora_expand) as masked MFMAs per (expert, adapter)
-//     segment with z split into bf16 hi + lo, then the SiLU gate (mode 0, gate
+//     segment with s*z rounded to bf16, then the SiLU gate (mode 0, gate
 //     and up columns in the same lane) or the top-k weight (mode 1); the rows'
 //     validity and weights are staged in LDS at the start.
 // A wavefront whose rows are all padding skips its MFMAs and stores but still
@@ -94,7 +94,9 @@ struct DmaCfg {
   static __device__ __forceinline__ int off(int row, int chunk) { return row * PROW + (swz(row, chunk) << 4); }
 };
 
-template <int MODE, class C, int WAVES_PER_SIMD>
+// EVENK: K is a multiple of the stage depth, so no copy needs clamping or
+// zeroing past K (and the chunk indices need not stay live in the loop).
+template <int MODE, class C, int WAVES_PER_SIMD, bool EVENK>
 __global__ __launch_bounds__(C::NT, WAVES_PER_SIMD) void grouped_gemm_dma_kernel(GemmParams p) {
   constexpr int BM = C::BM, BN = C::BN, BK = C::BK, NS = C::NS, MI = C::MI, NI = C::NI;
   constexpr int NCA = C::NCA, NCW = C::NCW, AROWS = C::AROWS, WROWS = C::WROWS;
@@ -157,46 +159,48 @@ __global__ __launch_bounds__(C::NT, WAVES_PER_SIMD) void grouped_gemm_dma_kernel
   // alchunk / wlchunk.
   const int lrow = lane / CPR, lslot = lane % CPR;
   uint32_t a_off[NCA];  // byte offsets into the A buffer (x or h)
-  int alchunk[NCA];
-  const uint16_t* b_src[NCW];
-  int wlchunk[NCW];
+  uint32_t w_off[NCW];  // element offsets into the expert's weights (N * K < 2^32)
+  int alchunk[EVENK ? 1 : NCA], wlchunk[EVENK ? 1 : NCW];
   const uint16_t* Wexp = p.W + (size_t)e * p.N * p.K;
   const buf_rsrc_t a_rs = make_rsrc(p.in, p.in_bytes);
 #pragma unroll
   for (int i = 0; i < NCA; ++i) {
     const int r = wave * AROWS + i * RPC + lrow;
-    alchunk[i] = C::swz(r, lslot);  // the swizzle is an involution
+    const int ch = C::swz(r, lslot);  // the swizzle is an involution
+    if (!EVENK) alchunk[i] = ch;
     const int grow = row0 + r;
     const int pr = p.sorted[grow];
     const int arow = MODE == 0 ? pr / p.topk : grow;  // x row of the token, or the h row
-    a_off[i] = pr < p.P ? (uint32_t)(arow * p.K + alchunk[i] * 8) * 2u : kBufNone;
+    a_off[i] = pr < p.P ? (uint32_t)(arow * p.K + ch * 8) * 2u : kBufNone;
   }
 #pragma unroll
   for (int i = 0; i < NCW; ++i) {
     const int r = wave * WROWS + i * RPC + lrow;
-    wlchunk[i] = C::swz(r, lslot);
-    b_src[i] = Wexp + (size_t)tile_col(r) * p.K + wlchunk[i] * 8;
+    const int ch = C::swz(r, lslot);
+    if (!EVENK) wlchunk[i] = ch;
+    w_off[i] = (uint32_t)tile_col(r) * (uint32_t)p.K + (uint32_t)(ch * 8);
   }
 
   const int ntile = (p.K + BK - 1) / BK;  // the last stage may be partial
-  const bool partial = (p.K % BK) != 0;
+  const bool partial = !EVENK && (p.K % BK) != 0;
   auto issue = [&](int s, auto nt_c) {
     constexpr bool NTL = decltype(nt_c)::value;
     char* A = smem + (s % NS) * C::STAGE;
     char* B = A + C::ATILE;
     const int k0 = s * BK;
     auto ldA = [&](int i) {
-      const int k = k0 + alchunk[i] * 8;
-      const int koff = k < p.K ? k0 : p.K - 8 - alchunk[i] * 8;  // clamped: a valid address
+      int koff = k0;
+      if (!EVENK && k0 + alchunk[i] * 8 >= p.K) koff = p.K - 8 - alchunk[i] * 8;  // clamped: a valid address
       const int roff = (wave * AROWS + i * RPC) * PROW;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rs, (lds_char*)(A + roff), 16, (int)(a_off[i] + (uint32_t)koff * 2u), 0, 0, 0);
     };
     auto ldW = [&](int i) {
-      const int k = k0 + wlchunk[i] * 8;
-      const int koff = k < p.K ? k0 : p.K - 8 - wlchunk[i] * 8;
+      int koff = k0;
+      if (!EVENK && k0 + wlchunk[i] * 8 >= p.K) koff = p.K - 8 - wlchunk[i] * 8;
       const int roff = (wave * WROWS + i * RPC) * PROW;
       // cache policy operand 2: non-temporal
-      __builtin_amdgcn_global_load_lds((const void*)(b_src[i] + koff), (lds_char*)(B + roff), 16, 0, NTL ? 2 : 0);
+      __builtin_amdgcn_global_load_lds((const void*)(Wexp + (w_off[i] + (uint32_t)koff)), (lds_char*)(B + roff), 16,
+                                       0, NTL ? 2 : 0);
     };
     // all A copies of the stage, then all W copies: at 256 x 256 this order
     // ran the Qwen3-MoE-like gate_up in 273 us against 283 us with each A
@@ -208,16 +212,18 @@ __global__ __launch_bounds__(C::NT, WAVES_PER_SIMD) void grouped_gemm_dma_kernel
   };
   // zero this lane's chunks of stage s that lie beyond K (after they landed)
   auto zero_tail = [&](int s) {
-    char* A = smem + (s % NS) * C::STAGE;
-    char* B = A + C::ATILE;
+    if constexpr (!EVENK) {
+      char* A = smem + (s % NS) * C::STAGE;
+      char* B = A + C::ATILE;
 #pragma unroll
-    for (int i = 0; i < NCA; ++i)
-      if (s * BK + alchunk[i] * 8 >= p.K)
-        *reinterpret_cast<u32x4_t*>(A + (wave * AROWS + i * RPC + lrow) * PROW + lslot * 16) = zero4();
+      for (int i = 0; i < NCA; ++i)
+        if (s * BK + alchunk[i] * 8 >= p.K)
+          *reinterpret_cast<u32x4_t*>(A + (wave * AROWS + i * RPC + lrow) * PROW + lslot * 16) = zero4();
 #pragma unroll
-    for (int i = 0; i < NCW; ++i)
-      if (s * BK + wlchunk[i] * 8 >= p.K)
-        *reinterpret_cast<u32x4_t*>(B + (wave * WROWS + i * RPC + lrow) * PROW + lslot * 16) = zero4();
+      for (int i = 0; i < NCW; ++i)
+        if (s * BK + wlchunk[i] * 8 >= p.K)
+          *reinterpret_cast<u32x4_t*>(B + (wave * WROWS + i * RPC + lrow) * PROW + lslot * 16) = zero4();
+    }
   };
 
   f32x16_t acc[MI][NI];
@@ -277,12 +283,40 @@ __global__ __launch_bounds__(C::NT, WAVES_PER_SIMD) void grouped_gemm_dma_kernel
   // must not wait for those reads.
   constexpr int KK = BK / 16;  // MFMA K slices per stage (even)
   constexpr int VM_AHEAD = (NCA + NCW) * (NS - 2) < 63 ? (NCA + NCW) * (NS - 2) : 63;
+  // weight rows of the wavefront's columns (the expand's B rows)
+  int ncol[NI];
+#pragma unroll
+  for (int ni = 0; ni < NI; ++ni) ncol[ni] = tile_col(wn * 64 + ni * 32 + l32);
+  // The expand of adapters 0..63 runs inside the K loop, one item per stage
+  // (gemm_expand.h): an item loaded during stage q is multiplied after the
+  // barrier of stage q + 1, by when the stage's wait has seen its loads land.
+  // Only where a wavefront holds two or more row blocks (with one, the
+  // 64 x 128 tile, the expand is short and the loop's extra work cost more:
+  // GPT-OSS-like gate_up 240 -> 249 us), not for a K with a remainder at
+  // 256 x 256 (the clamped copies need the registers), and only when the
+  // items fit in the stages; otherwise the batched expand runs after the
+  // loop (the Qwen3-MoE-like down GEMM, 12 stages for ~20 segments per
+  // wavefront: 183 us batched against 219 us with the leftover items after
+  // the loop one round trip each).
+  constexpr bool XPIPE = MI >= 2 && (EVENK || MI < 4);
+  ExpandItems<MI, NI> xi;
+  xi.nitems = 0;
+  xi.next = 0;
+  bool xpend = false;  // an item is loaded and not yet multiplied
   auto kloop = [&](auto live_c, auto nt_c) {
     constexpr bool LIVE = decltype(live_c)::value;
     // prologue: every ring slot gets a stage; wait for stage 0
 #pragma unroll
     for (int s = 0; s < NS; ++s)
       if (s < ntile) issue(s, nt_c);
+    if (LIVE && XPIPE) {
+      expand_items_init(xi, p, e, row0 + wrow, 0);
+      if (xi.nitems > ntile - 1) xi.nitems = -1;  // does not fit: batched, after the loop
+      if (xi.nitems > 0) {
+        expand_item_load(xi, p, e, row0 + wrow, 0, ncol);
+        xpend = true;
+      }
+    }
     __builtin_amdgcn_s_waitcnt(wait_vm(0));
     if (tid < BM) {
       row_ok[tid] = my_ok;
@@ -307,6 +341,11 @@ __global__ __launch_bounds__(C::NT, WAVES_PER_SIMD) void grouped_gemm_dma_kernel
       __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // fragment reads of stage q and zero writes done
       stage_barrier();
       if (q + NS < ntile) issue(q + NS, nt_c);  // into the slot stage q just released
+      if (LIVE && xpend) {
+        expand_item_mfma(xi, acc, row0 + wrow);
+        xpend = xi.next < xi.nitems;
+        if (xpend) expand_item_load(xi, p, e, row0 + wrow, 0, ncol);
+      }
       // last slice of stage q (its fragments are in registers), with the
       // first reads of stage q + 1
       if (LIVE) step((KK - 1) & 1, true, q + 1, 0);
@@ -328,11 +367,16 @@ __global__ __launch_bounds__(C::NT, WAVES_PER_SIMD) void grouped_gemm_dma_kernel
   }
   if (!live) return;
 
-  // LoRA expand: acc += s * z[rows of segment] * B[l][e][cols]^T per segment
-  int ncol[NI];
-#pragma unroll
-  for (int ni = 0; ni < NI; ++ni) ncol[ni] = tile_col(wn * 64 + ni * 32 + l32);
-  lora_expand<MI, NI, true, 4>(acc, p, e, row0 + wrow, ncol);
+  // LoRA expand: acc += s * z[rows of segment] * B[l][e][cols]^T per
+  // segment -- the items the K loop had no stage left for, then adapters 64
+  // and up
+  while (xpend) {
+    expand_item_mfma(xi, acc, row0 + wrow);
+    xpend = xi.next < xi.nitems;
+    if (xpend) expand_item_load(xi, p, e, row0 + wrow, 0, ncol);
+  }
+  const int lstart = (XPIPE && xi.nitems >= 0) ? 64 : 0;  // adapters the loop has not expanded
+  if (lstart < p.L) lora_expand<MI, NI, true, (MI <= 3 ? 8 : 4)>(acc, p, e, row0 + wrow, ncol, lstart);
 
   // epilogue: the products were formed as W x A^T, so element v of
   // acc[mi][ni] is row l32 of the 32-row block and column
@@ -390,21 +434,28 @@ __global__ __launch_bounds__(C::NT, WAVES_PER_SIMD) void grouped_gemm_dma_kernel
 
 template <class C, int WAVES_PER_SIMD>
 int launch_dma(const GemmParams& gp_in, int mode, int64_t cap_rows, hipStream_t st) {
-  static std::atomic<uint64_t> attr_done[2];
+  static std::atomic<uint64_t> attr_done[4];  // per kernel: mode x EVENK
   GemmParams gp = gp_in;
   gp.ncol = mode == 0 ? (gp.I + C::BN / 2 - 1) / (C::BN / 2) : (gp.N + C::BN - 1) / C::BN;
   gp.nrowt = (int)((cap_rows + C::BM - 1) / C::BM);
   const unsigned grid = (unsigned)gp.ncol * (unsigned)(mode == 0 ? gp.nrowt : (gp.nrowt + 7) / 8 * 8);
-  const void* fn = mode == 0 ? reinterpret_cast<const void*>(&grouped_gemm_dma_kernel<0, C, WAVES_PER_SIMD>)
-                             : reinterpret_cast<const void*>(&grouped_gemm_dma_kernel<1, C, WAVES_PER_SIMD>);
+  const bool even = gp.K % C::BK == 0;
+  const void* fn =
+      mode == 0 ? (even ? reinterpret_cast<const void*>(&grouped_gemm_dma_kernel<0, C, WAVES_PER_SIMD, true>)
+                        : reinterpret_cast<const void*>(&grouped_gemm_dma_kernel<0, C, WAVES_PER_SIMD, false>))
+                : (even ? reinterpret_cast<const void*>(&grouped_gemm_dma_kernel<1, C, WAVES_PER_SIMD, true>)
+                        : reinterpret_cast<const void*>(&grouped_gemm_dma_kernel<1, C, WAVES_PER_SIMD, false>));
   if (C::LDS > 64 * 1024) {  // more than the default 64 KB of dynamic LDS
-    const int rc = ensure_dynamic_lds(fn, C::LDS, attr_done[mode]);
+    const int rc = ensure_dynamic_lds(fn, C::LDS, attr_done[2 * mode + (even ? 1 : 0)]);
     if (rc) return rc;
   }
-  if (mode == 0)
-    grouped_gemm_dma_kernel<0, C, WAVES_PER_SIMD><<<grid, C::NT, C::LDS, st>>>(gp);
-  else
-    grouped_gemm_dma_kernel<1, C, WAVES_PER_SIMD><<<grid, C::NT, C::LDS, st>>>(gp);
+  if (mode == 0) {
+    if (even) grouped_gemm_dma_kernel<0, C, WAVES_PER_SIMD, true><<<grid, C::NT, C::LDS, st>>>(gp);
+    else grouped_gemm_dma_kernel<0, C, WAVES_PER_SIMD, false><<<grid, C::NT, C::LDS, st>>>(gp);
+  } else {
+    if (even) grouped_gemm_dma_kernel<1, C, WAVES_PER_SIMD, true><<<grid, C::NT, C::LDS, st>>>(gp);
+    else grouped_gemm_dma_kernel<1, C, WAVES_PER_SIMD, false><<<grid, C::NT, C::LDS, st>>>(gp);
+  }
   return MOE_LORA_OK;
 }
 

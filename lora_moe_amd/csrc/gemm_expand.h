@@ -19,57 +19,55 @@ namespace moelora {
 // side is the MFMA's first operand (the accumulators hold the tile
 // transposed); otherwise z is.
 //
-// Each rank slice of 16 is one MFMA K step.  z (fp32) of the lane's rows is
-// read and split into a bf16 pair hi + lo (hi = rne(s*z), lo = rne(s*z - hi))
-// once per slice and then masked per segment; the B rows of up to NB
-// segments are loaded together, so a batch waits for memory once.  Segments
-// are found with one load per adapter id across the lanes and a ballot.
+// Segments are found with one load per adapter id across the lanes and a
+// ballot, and taken NB at a time.  For each batch and each rank slice of 16
+// (one MFMA K step) the slice of z of the lane's rows and the B rows of the
+// batch's segments are loaded together -- one memory round trip per slice --
+// then s*z is rounded to bf16 (the shrink result enters the product at bf16
+// precision, like every other operand) and masked per segment.  The expand
+// runs once per tile with one workgroup per CU, so its round trips are time
+// the MFMA pipes wait: loading z and B together halved them.
 template <int MI, int NI, bool WA, int NB = 8>
 __device__ __forceinline__ void lora_expand(f32x16_t (&acc)[MI][NI], const GemmParams& p, int e,
-                                            int wrow0, const int (&ncol)[NI]) {
+                                            int wrow0, const int (&ncol)[NI], int lbeg = 0) {
   const int lane = threadIdx.x & 63, l32 = lane & 31, khalf = lane >> 5;
   const int S = p.L + 1;
   const int wrow1 = wrow0 + 32 * MI;
-  for (int l0 = 0; l0 < p.L; l0 += 64) {
+  for (int l0 = lbeg; l0 < p.L; l0 += 64) {
     const int lj = l0 + lane;
     int st = 0, cnt = 0;
     if (lj < p.L) {
       st = p.segstart[e * S + lj];
       cnt = p.segcnt[e * S + lj];
     }
-    const uint64_t hit = __ballot(cnt > 0 && st < wrow1 && st + cnt > wrow0);
-    if (!hit) continue;
-    for (int q0 = 0; q0 < p.r; q0 += 16) {
-      const int qa = q0 + 8 * khalf;
-      const bool qok = qa < p.r;
-      u32x4_t zh[MI], zl[MI];
+    uint64_t pending = __ballot(cnt > 0 && st < wrow1 && st + cnt > wrow0);
+    while (pending) {
+      int ids[NB];
+      int nb = 0;
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi) {
-        zh[mi] = zero4();
-        zl[mi] = zero4();
-        if (qok) {
-          const float4* zp = reinterpret_cast<const float4*>(p.z + (size_t)(wrow0 + 32 * mi + l32) * p.r + qa);
-          const float4 z0 = zp[0], z1 = zp[1];
-          float zv[8];
-          zv[0] = p.s * z0.x; zv[1] = p.s * z0.y; zv[2] = p.s * z0.z; zv[3] = p.s * z0.w;
-          zv[4] = p.s * z1.x; zv[5] = p.s * z1.y; zv[6] = p.s * z1.z; zv[7] = p.s * z1.w;
-          split8(zv, zh[mi], zl[mi]);
+      for (int b = 0; b < NB; ++b) {
+        ids[b] = 0;
+        if (pending) {
+          ids[b] = __builtin_ctzll(pending);
+          pending &= pending - 1;
+          nb = b + 1;
         }
       }
-      uint64_t pending = hit;
-      while (pending) {
-        int ids[NB];
-        int nb = 0;
+      for (int q0 = 0; q0 < p.r; q0 += 16) {
+        const int qa = q0 + 8 * khalf;
+        const bool qok = qa < p.r;
+        float4 z0[MI], z1[MI];
+        u32x4_t bfr[NB][NI];
 #pragma unroll
-        for (int b = 0; b < NB; ++b) {
-          ids[b] = 0;
-          if (pending) {
-            ids[b] = __builtin_ctzll(pending);
-            pending &= pending - 1;
-            nb = b + 1;
+        for (int mi = 0; mi < MI; ++mi) {
+          z0[mi] = make_float4(0.f, 0.f, 0.f, 0.f);
+          z1[mi] = z0[mi];
+          if (qok) {
+            const float4* zp = reinterpret_cast<const float4*>(p.z + (size_t)(wrow0 + 32 * mi + l32) * p.r + qa);
+            z0[mi] = zp[0];
+            z1[mi] = zp[1];
           }
         }
-        u32x4_t bfr[NB][NI];
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
           if (b < nb) {
@@ -77,6 +75,15 @@ __device__ __forceinline__ void lora_expand(f32x16_t (&acc)[MI][NI], const GemmP
 #pragma unroll
             for (int ni = 0; ni < NI; ++ni) bfr[b][ni] = qok ? ld16(Bl + (size_t)ncol[ni] * p.r + qa) : zero4();
           }
+        }
+        u32x4_t zh[MI];
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi) {
+          const float zv[8] = {p.s * z0[mi].x, p.s * z0[mi].y, p.s * z0[mi].z, p.s * z0[mi].w,
+                               p.s * z1[mi].x, p.s * z1[mi].y, p.s * z1[mi].z, p.s * z1[mi].w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            zh[mi][i] = (uint32_t)f32_to_bf16(zv[2 * i]) | ((uint32_t)f32_to_bf16(zv[2 * i + 1]) << 16);
         }
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
@@ -88,23 +95,91 @@ __device__ __forceinline__ void lora_expand(f32x16_t (&acc)[MI][NI], const GemmP
               const int sub0 = wrow0 + 32 * mi;
               if (sub0 >= send || sub0 + 32 <= sst) continue;  // this 32-row block misses the segment
               const int row = sub0 + l32;
-              const bool in = row >= sst && row < send;
-              const u32x4_t h = in ? zh[mi] : zero4(), lo = in ? zl[mi] : zero4();
+              const u32x4_t h = (row >= sst && row < send) ? zh[mi] : zero4();
 #pragma unroll
               for (int ni = 0; ni < NI; ++ni) {
-                if (WA) {
+                if (WA)
                   acc[mi][ni] = mfma_32x32x16(bfr[b][ni], h, acc[mi][ni]);
-                  acc[mi][ni] = mfma_32x32x16(bfr[b][ni], lo, acc[mi][ni]);
-                } else {
+                else
                   acc[mi][ni] = mfma_32x32x16(h, bfr[b][ni], acc[mi][ni]);
-                  acc[mi][ni] = mfma_32x32x16(lo, bfr[b][ni], acc[mi][ni]);
-                }
               }
             }
           }
         }
       }
     }
+  }
+}
+
+// The same expand as work items spread over a K loop, for adapters
+// [lbeg, lbeg + 64): item i is (rank slice i / nseg, segment i % nseg in
+// ascending adapter order) over the nseg segments that meet the wavefront's
+// rows.  A loaded item holds s*z of the lane's rows for the slice (bf16,
+// from the shrink) and the segment's B rows at the lane's columns; its
+// masked MFMAs run a K stage after its loads, so their latency passes under
+// the main loop's work instead of stalling the epilogue (one workgroup per
+// CU at 256 x 256 tiles leaves nothing else to run).  Weight side first, as
+// in lora_expand<..., WA = true>.
+template <int MI, int NI>
+struct ExpandItems {
+  uint64_t hit;  // bit l: adapter lbeg + l has a segment meeting the rows
+  int nseg, nitems, next;
+  int st, cnt;   // segment of adapter lbeg + lane
+  int l;         // adapter bit of the loaded item
+  u32x4_t z[MI];
+  u32x4_t b[NI];
+};
+
+template <int MI, int NI>
+__device__ __forceinline__ void expand_items_init(ExpandItems<MI, NI>& it, const GemmParams& p, int e,
+                                                  int wrow0, int lbeg) {
+  const int lane = threadIdx.x & 63, S = p.L + 1, lj = lbeg + lane;
+  it.st = 0;
+  it.cnt = 0;
+  if (lj < p.L) {
+    it.st = p.segstart[e * S + lj];
+    it.cnt = p.segcnt[e * S + lj];
+  }
+  it.hit = __ballot(it.cnt > 0 && it.st < wrow0 + 32 * MI && it.st + it.cnt > wrow0);
+  it.nseg = __builtin_popcountll(it.hit);
+  it.nitems = it.nseg * ((p.r + 15) >> 4);
+  it.next = 0;
+  it.l = 0;
+}
+
+template <int MI, int NI>
+__device__ __forceinline__ void expand_item_load(ExpandItems<MI, NI>& it, const GemmParams& p, int e,
+                                                 int wrow0, int lbeg, const int (&ncol)[NI]) {
+  const int lane = threadIdx.x & 63, l32 = lane & 31, khalf = lane >> 5;
+  const int q = it.next / it.nseg, j = it.next - q * it.nseg;
+  uint64_t m = it.hit;
+  for (int k = 0; k < j; ++k) m &= m - 1;
+  it.l = __builtin_ctzll(m);
+  const int qa = 16 * q + 8 * khalf;
+  const bool qok = qa < p.r;
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+    it.z[mi] = qok ? ld16(p.zb + (size_t)(wrow0 + 32 * mi + l32) * p.r + qa) : zero4();
+  const uint16_t* Bl = p.B + ((size_t)(lbeg + it.l) * p.E + e) * p.N * p.r;
+#pragma unroll
+  for (int ni = 0; ni < NI; ++ni) it.b[ni] = qok ? ld16(Bl + (size_t)ncol[ni] * p.r + qa) : zero4();
+  ++it.next;
+}
+
+template <int MI, int NI>
+__device__ __forceinline__ void expand_item_mfma(const ExpandItems<MI, NI>& it, f32x16_t (&acc)[MI][NI],
+                                                 int wrow0) {
+  const int l32 = threadIdx.x & 31;
+  const int sst = __builtin_amdgcn_readlane(it.st, it.l);
+  const int send = sst + __builtin_amdgcn_readlane(it.cnt, it.l);
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi) {
+    const int sub0 = wrow0 + 32 * mi;
+    if (sub0 >= send || sub0 + 32 <= sst) continue;  // this 32-row block misses the segment
+    const int row = sub0 + l32;
+    const u32x4_t h = (row >= sst && row < send) ? it.z[mi] : zero4();
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = mfma_32x32x16(it.b[ni], h, acc[mi][ni]);
   }
 }
 

@@ -37,7 +37,8 @@ struct Layout {
   int dsplit;  // K splits of the down GEMM (d holds one partial slab per split)
   int hsplit;  // h also stored as its bf16 remainder lo (I >= kHsplitMinI)
   size_t off_hdr, off_sorted, off_eoff, off_segstart, off_segcnt, off_bexp, off_pos;
-  size_t off_chunk, off_chunkerr, off_rank, off_tiles, off_zgu, off_zd, off_h, off_hlo, off_d, total;
+  size_t off_chunk, off_chunkerr, off_rank, off_tiles, off_zgu, off_zd, off_zbgu, off_zbd, off_h, off_hlo,
+      off_d, total;
 };
 
 // Fills `L` from the shape; returns MOE_LORA_OK or an error code.
@@ -64,6 +65,8 @@ struct WsPtrs {
   LoraTile* tiles;
   float* zgu;
   float* zd;
+  uint16_t* zbgu;  // bf16(s * z_gu), read by the LDS-tiled GEMMs' expand
+  uint16_t* zbd;   // bf16(s * z_d)
   uint16_t* h;
   uint16_t* hlo;  // nullptr unless hsplit
   float* d;
@@ -85,6 +88,8 @@ inline WsPtrs ws_ptrs(void* base, const Layout& L) {
   w.tiles = reinterpret_cast<LoraTile*>(b + L.off_tiles);
   w.zgu = reinterpret_cast<float*>(b + L.off_zgu);
   w.zd = reinterpret_cast<float*>(b + L.off_zd);
+  w.zbgu = reinterpret_cast<uint16_t*>(b + L.off_zbgu);
+  w.zbd = reinterpret_cast<uint16_t*>(b + L.off_zbd);
   w.h = reinterpret_cast<uint16_t*>(b + L.off_h);
   w.hlo = L.hsplit ? reinterpret_cast<uint16_t*>(b + L.off_hlo) : nullptr;
   w.d = reinterpret_cast<float*>(b + L.off_d);
@@ -99,6 +104,7 @@ struct GemmParams {
   const uint16_t* W;       // [E][N][K]
   const uint16_t* B;       // [L][E][N][r]
   const float* z;          // [cap_rows][r]
+  const uint16_t* zb;      // [cap_rows][r] bf16(s * z) (LDS-tiled family)
   const int32_t* sorted;
   const int32_t* bexp;
   const int32_t* segstart;  // [E][L+1] first row of each (expert, slot) segment
@@ -167,9 +173,15 @@ struct ShrinkPlan {
 };
 ShrinkPlan plan_shrink(const Layout& L, int K);
 
-// mode 0: gate_up shrink from x rows gathered by token; mode 1: down shrink from h rows
-int launch_shrink(const Layout& L, int mode, const uint16_t* in, const uint16_t* A, float* z, void* ws,
-                  hipStream_t st);
+// The LDS-tiled GEMM of this mode (0 gate_up, 1 down) runs, and its expand
+// reads z as bf16(s * z)
+inline bool tiled_expand(const Layout& L, int mode) { return L.bm >= 64 && !(mode == 1 && L.hsplit); }
+
+// mode 0: gate_up shrink from x rows gathered by token; mode 1: down shrink
+// from h rows.  z receives the fp32 sums; when tiled_expand(L, mode) also zb
+// receives bf16(s * z).
+int launch_shrink(const Layout& L, int mode, const uint16_t* in, const uint16_t* A, float* z, uint16_t* zb,
+                  void* ws, hipStream_t st);
 
 // mode 0: gate_up GEMM + expand + SiLU gate -> h; mode 1: down GEMM + expand + weight -> d
 int launch_gemm(const Layout& L, int mode, const uint16_t* x, const int32_t* lora_ids,

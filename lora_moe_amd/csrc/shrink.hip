@@ -34,6 +34,8 @@ struct ShrinkParams {
   const LoraTile* tiles;
   const int32_t* hdr;
   float* z;            // [cap_rows][r]
+  uint16_t* zb;        // [cap_rows][r] bf16(s * z), or nullptr
+  float s;
   int K, E, r, topk, splits, steps_per_split, nsteps, use_atomic;
   int ncb, cpb;        // column blocks per tile, z columns per block
 };
@@ -158,15 +160,31 @@ __global__ __launch_bounds__(256) void lora_shrink_kernel(ShrinkParams p) {
             if (row < tl.n && q < p.r && q < q0 + p.cpb) {
               const float v = acc[rf][nf][i] + red[0][row][nf * 16 + m];
               float* dst = p.z + (size_t)(tl.row0 + row) * p.r + q;
-              if (p.use_atomic)
+              if (p.use_atomic) {
                 __hip_atomic_fetch_add(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-              else
+              } else {
                 *dst = v;
+                if (p.zb) p.zb[(size_t)(tl.row0 + row) * p.r + q] = f32_to_bf16(p.s * v);
+              }
             }
           }
     }
     __syncthreads();  // red is reused by the next item
   }
+}
+
+// zb = bf16(s * z) for every row, after split-K shrinks (8 values per thread)
+__global__ __launch_bounds__(256) void zb_convert_kernel(const float* __restrict__ z, int64_t n8, float s,
+                                                         uint16_t* __restrict__ zb) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n8) return;
+  const float4 a = reinterpret_cast<const float4*>(z)[2 * i], b = reinterpret_cast<const float4*>(z)[2 * i + 1];
+  u32x4_t o;
+  o[0] = (uint32_t)f32_to_bf16(s * a.x) | ((uint32_t)f32_to_bf16(s * a.y) << 16);
+  o[1] = (uint32_t)f32_to_bf16(s * a.z) | ((uint32_t)f32_to_bf16(s * a.w) << 16);
+  o[2] = (uint32_t)f32_to_bf16(s * b.x) | ((uint32_t)f32_to_bf16(s * b.y) << 16);
+  o[3] = (uint32_t)f32_to_bf16(s * b.z) | ((uint32_t)f32_to_bf16(s * b.w) << 16);
+  reinterpret_cast<u32x4_t*>(zb)[i] = o;
 }
 
 template <int MODE, int RFS, int NFR, int U>
@@ -240,8 +258,8 @@ ShrinkPlan plan_shrink(const Layout& L, int K) {
   return sp;
 }
 
-int launch_shrink(const Layout& L, int mode, const uint16_t* in, const uint16_t* A, float* z, void* ws,
-                  hipStream_t st) {
+int launch_shrink(const Layout& L, int mode, const uint16_t* in, const uint16_t* A, float* z, uint16_t* zb,
+                  void* ws, hipStream_t st) {
   WsPtrs w = ws_ptrs(ws, L);
   const int K = mode == 0 ? L.H : L.I;
   ShrinkPlan pl = plan_shrink(L, K);
@@ -260,6 +278,9 @@ int launch_shrink(const Layout& L, int mode, const uint16_t* in, const uint16_t*
   sp.nsteps = (K + 63) / 64;
   sp.steps_per_split = (sp.nsteps + pl.splits - 1) / pl.splits;
   sp.use_atomic = pl.splits > 1;
+  const bool want_zb = tiled_expand(L, mode);
+  sp.zb = want_zb && !sp.use_atomic ? zb : nullptr;
+  sp.s = L.s;
   sp.ncb = shrink_col_blocks(L, pl.splits);
   sp.cpb = L.r / sp.ncb;
   const bool even = (K % 64) == 0;
@@ -272,6 +293,10 @@ int launch_shrink(const Layout& L, int mode, const uint16_t* in, const uint16_t*
     if (rfs == 4) launch_nfr<1, 4>(sp, even, pl.grid, st);
     else if (rfs == 2) launch_nfr<1, 2>(sp, even, pl.grid, st);
     else launch_nfr<1, 1>(sp, even, pl.grid, st);
+  }
+  if (want_zb && sp.use_atomic) {  // the split sums are complete only now
+    const int64_t n8 = L.cap_rows * (int64_t)L.r / 8;
+    zb_convert_kernel<<<(unsigned)((n8 + 255) / 256), 256, 0, st>>>(z, n8, L.s, zb);
   }
   return hipGetLastError() == hipSuccess ? MOE_LORA_OK : MOE_LORA_EHIP;
 }

@@ -22,6 +22,8 @@ pytestmark = pytest.mark.gpu
 
 
 def test_batch_sizes_1_to_64():
+    import gc
+
     import lora_moe_amd as lm
     times = []
     for T in range(1, 65):
@@ -33,24 +35,32 @@ def test_batch_sizes_1_to_64():
         y = torch.empty((T, wl.H), dtype=torch.bfloat16, device="cuda")
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        t0 = time.perf_counter()
-        a.record()
-        lm.moe_lora_align(shape, dev["topk_ids"], dev["lora_ids"], ws)
-        lm.moe_lora_forward(shape, dev["x"], dev["topk_ids"], dev["topk_weights"], dev["lora_ids"],
-                            dev["W_gu"], dev["W_down"], dev["A_gu"], dev["B_gu"], dev["A_down"],
-                            dev["B_down"], ws, y)
-        b.record()
+        gc.disable()  # time the two library calls, not a collector pause
+        try:
+            t0 = time.perf_counter()
+            a.record()
+            lm.moe_lora_align(shape, dev["topk_ids"], dev["lora_ids"], ws)
+            lm.moe_lora_forward(shape, dev["x"], dev["topk_ids"], dev["topk_weights"], dev["lora_ids"],
+                                dev["W_gu"], dev["W_down"], dev["A_gu"], dev["B_gu"], dev["A_down"],
+                                dev["B_down"], ws, y)
+            b.record()
+            host_ms = (time.perf_counter() - t0) * 1e3
+        finally:
+            gc.enable()
         torch.cuda.synchronize()
-        host_ms = (time.perf_counter() - t0) * 1e3
         times.append((T, a.elapsed_time(b), host_ms))
         compare(y.float().cpu().numpy().astype(np.float64), oracle_tokens(inp, None), f"T={T}")
     for T, dev_ms, host_ms in times:
-        log(f"T={T}: align + forward {dev_ms * 1e3:.1f} us on the device, {host_ms:.3f} ms host wall")
-    # no call after the first pays a load or compile: every later call's host
-    # wall time stays within a small multiple of the median
-    later = [h for _, _, h in times[1:]]
-    med = float(np.median(later))
-    assert max(later) < 20 * med + 1.0, f"slowest later call {max(later):.2f} ms vs median {med:.2f}"
+        log(f"T={T}: align + forward {dev_ms * 1e3:.1f} us on the device, {host_ms:.3f} ms to enqueue")
+    # no call after the first pays a module load or a compile (those take
+    # milliseconds to seconds): every later call enqueues within 2 ms, and its
+    # device time stays within 5x the median
+    later = times[1:]
+    med_dev = float(np.median([d for _, d, _ in later]))
+    worst_host = max(later, key=lambda t: t[2])
+    worst_dev = max(later, key=lambda t: t[1])
+    assert worst_host[2] < 2.0, f"T={worst_host[0]} took {worst_host[2]:.2f} ms to enqueue"
+    assert worst_dev[1] < 5 * med_dev, f"T={worst_dev[0]}: {worst_dev[1]:.3f} ms vs median {med_dev:.3f}"
 
 
 if __name__ == "__main__":  # for a kernel trace of this sequence alone
