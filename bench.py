@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=5, help="synthetic workload number 1..6")
     ap.add_argument("--block-m", type=int, default=0)
+    ap.add_argument("--no-tuning", action="store_true",
+                    help="the library's built-in configuration instead of the shipped tuning table")
     ap.add_argument("--others", default="1,2,3,4,6",
                     help="further workloads summarised under 'workloads' ('' for none)")
     ap.add_argument("--other-steps", type=int, default=10)
@@ -224,14 +226,14 @@ def cpu_baseline(inp, target_s):
                       f"{', cycled' if n > wl.T else ''}), fp64, {dt:.1f} s wall"}
 
 
-def run_other(lm, synth, n, steps, scratch):
+def run_other(lm, synth, n, steps, scratch, tuning):
     """Flushed median of one more workload (generated, timed, freed)."""
     import torch
     wl = synth.WORKLOADS[n]
     print(f"bench: workload {n} ({wl.name})", file=sys.stderr, flush=True)
     dev, inp = synth.device_inputs(wl, touched_only=True)
     work = synth.algorithmic_work(wl, inp.topk_ids, inp.lora_ids)
-    shape = lm.make_shape(wl.T, wl.H, wl.I, wl.E, wl.topk, wl.L, wl.r, 0, wl.scale)
+    shape = lm.make_shape(wl.T, wl.H, wl.I, wl.E, wl.topk, wl.L, wl.r, 0, wl.scale, tuning=tuning)
     ws = lm.alloc_workspace(shape)
     y = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda")
 
@@ -246,6 +248,7 @@ def run_other(lm, synth, n, steps, scratch):
     ts = flushed_calls(step, steps, scratch)
     med = statistics.median(ts)
     out = {"workload": wl.name, "block_m": lm.moe_lora_resolve_block_m(shape),
+           "knobs": {k: getattr(shape, k) for k in lm.KNOBS},
            "flushed_median_ms": med, "flushed_min_ms": min(ts), "tokens_per_s": wl.T / (med * 1e-3),
            "bound": binding(work), **layer_fracs(work, med)}
     del dev, ws, y
@@ -277,7 +280,8 @@ def main():
           flush=True)
     dev, inp = synth.device_inputs(wl, touched_only=True, keep_host=not args.no_cpu_baseline)
     work = synth.algorithmic_work(wl, inp.topk_ids, inp.lora_ids)
-    shape = lm.make_shape(wl.T, wl.H, wl.I, wl.E, wl.topk, wl.L, wl.r, args.block_m, wl.scale)
+    tuning = None if args.no_tuning else lm.load_tuning()
+    shape = lm.make_shape(wl.T, wl.H, wl.I, wl.E, wl.topk, wl.L, wl.r, args.block_m, wl.scale, tuning=tuning)
     bm = lm.moe_lora_resolve_block_m(shape)
     ws = lm.alloc_workspace(shape)
     y = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda")
@@ -342,7 +346,7 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "I": wl.I, "E": wl.E,
                    "topk": wl.topk, "L": wl.L, "r": wl.r,
-                   "block_m": bm, "seed": wl.seed},
+                   "block_m": bm, "seed": wl.seed, **{k: getattr(shape, k) for k in lm.KNOBS}},
         "roofline": roof,
         "timing": {"per_step": "one align + forward call after a 512 MB fill (L2 and MALL "
                                "cold), HIP events around the call; value and ms_per_step from "
@@ -401,7 +405,9 @@ def main():
     others = [int(w) for w in args.others.split(",") if w.strip()] if args.others else []
     if others:
         out["workloads"] = {"note": "flushed median of align + forward per workload, "
-                                    f"{args.other_steps} calls, block_m chosen by the library",
+                                    f"{args.other_steps} calls, configuration from "
+                                    + ("the library's built-in choice" if args.no_tuning
+                                       else "the shipped tuning table"),
                             args.workload: {"workload": wl.name, "block_m": bm,
                                             "flushed_median_ms": ms_per_step,
                                             "flushed_min_ms": min(call_ms),
@@ -409,7 +415,7 @@ def main():
                                             **layer_fracs(work, ms_per_step)}}
         for n in others:
             if n != args.workload:
-                out["workloads"][n] = run_other(lm, synth, n, args.other_steps, scratch)
+                out["workloads"][n] = run_other(lm, synth, n, args.other_steps, scratch, tuning)
     print(json.dumps(out), flush=True)
 
 

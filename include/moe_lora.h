@@ -46,6 +46,7 @@ extern "C" {
 /* Status codes. */
 #define MOE_LORA_OK 0
 #define MOE_LORA_EINVAL (-1)       /* null pointer, negative or zero size, topk > E, bad block_m */
+                                   /* or kernel configuration field                              */
 #define MOE_LORA_EALIGN (-2)       /* pointer not 16-byte aligned, H or I not a multiple of 8    */
 #define MOE_LORA_EWORKSPACE (-3)   /* workspace smaller than moe_lora_workspace_bytes()          */
 #define MOE_LORA_EUNSUPPORTED (-4) /* r not a multiple of 8 or r > 128; E*(L+1) > 14336; x or the  */
@@ -65,6 +66,18 @@ typedef struct moe_lora_shape {
   int32_t block_m;  /* rows per block shared by every op of the layer: one of     */
                     /* 16, 32, 64, 128, 192, 256, or 0 to choose it from shape    */
   float lora_scale; /* s above                                                    */
+  /* Kernel configuration; 0 in any field = the library's choice for the shape.
+   * moe_lora_tune_apply fills them from a tuning table (an offline sweep).    */
+  int32_t shrink_splits;  /* K splits of both shrinks, 1..64 (several: partial   */
+                          /* sums added with fp32 atomics)                       */
+  int32_t shrink_zblocks; /* work items per shrink tile across the r columns:    */
+                          /* 1 (all r), or 2..r/8 dividing r into multiples of 8 */
+  int32_t down_splits;    /* K splits of the streaming down GEMM (the one that   */
+                          /* runs for block_m <= 32 or I >= 4096), 1..8          */
+  int32_t tile_order;     /* workgroup order of the LDS-tiled GEMMs: 1 = row     */
+                          /* tile-major; 2 = each row tile's column tiles on one */
+                          /* XCD, row tiles interleaved over the 8 XCDs;         */
+                          /* 0 = 1 for gate_up and 2 for down                    */
 } moe_lora_shape;
 
 /* Device pointers into a workspace (see moe_lora_workspace_view). */
@@ -119,7 +132,9 @@ int moe_lora_resolve_block_m(const moe_lora_shape* shape);
  * the block_m measured fastest for it. */
 typedef struct {
   int32_t rows_per_expert, H, I, E, r, L; /* key */
-  int32_t block_m;                        /* value: 16, 32, 64, 128 or 256 */
+  int32_t block_m;                        /* value: 16, 32, 64, 128, 192 or 256 */
+  int32_t shrink_splits, shrink_zblocks, down_splits, tile_order; /* value: as in    */
+                                          /* moe_lora_shape (0 = the library's choice) */
 } moe_lora_tune_entry;
 
 /* block_m for `shape` chosen from a tuning table: the shape's own block_m
@@ -135,6 +150,15 @@ typedef struct {
  * is invalid.  Host only, pure: the table is read, not kept. */
 int moe_lora_tune_block_m(const moe_lora_shape* shape, const moe_lora_tune_entry* table, int32_t n,
                           float max_dist);
+
+/* The whole configuration from a tuning table: *out = *shape with block_m and
+ * the four knobs taken from the entry moe_lora_tune_block_m would pick (same
+ * distance, limit and validity rules; the shape's own non-zero fields win
+ * field by field).  With no entry in range *out = *shape.  Returns the
+ * block_m in effect, or a negative status (invalid shape, null out).  Host
+ * only, pure. */
+int moe_lora_tune_apply(const moe_lora_shape* shape, const moe_lora_tune_entry* table, int32_t n,
+                        float max_dist, moe_lora_shape* out);
 
 /* Bytes of device workspace that moe_lora_align / moe_lora_forward need for
  * this shape, or 0 when the shape is invalid.  Host only, pure. */

@@ -31,11 +31,14 @@ class MoeLoraError(RuntimeError):
         super().__init__(f"{func} failed: {moe_lora_status_str(code)} ({code})")
 
 
+KNOBS = ("shrink_splits", "shrink_zblocks", "down_splits", "tile_order")
+
+
 class moe_lora_shape(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("H", ctypes.c_int32), ("I", ctypes.c_int32),
                 ("E", ctypes.c_int32), ("topk", ctypes.c_int32), ("L", ctypes.c_int32),
                 ("r", ctypes.c_int32), ("block_m", ctypes.c_int32),
-                ("lora_scale", ctypes.c_float)]
+                ("lora_scale", ctypes.c_float)] + [(k, ctypes.c_int32) for k in KNOBS]
 
     def __repr__(self):
         return ("moe_lora_shape(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_)
@@ -59,37 +62,52 @@ class moe_lora_align_ptrs(ctypes.Structure):
 
 
 class moe_lora_tune_entry(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_int32) for n in ("rows_per_expert", "H", "I", "E", "r", "L", "block_m")]
+    _fields_ = [(n, ctypes.c_int32) for n in ("rows_per_expert", "H", "I", "E", "r", "L", "block_m")
+                + KNOBS]
 
 
-def make_shape(T, H, I, E, topk, L, r, block_m=0, lora_scale=1.0, tuning=None) -> moe_lora_shape:
-    """The shape struct; with block_m == 0 and a tuning table (load_tuning),
-    block_m is taken from the table (moe_lora_tune_block_m)."""
+def make_shape(T, H, I, E, topk, L, r, block_m=0, lora_scale=1.0, tuning=None,
+               **knobs) -> moe_lora_shape:
+    """The shape struct (knobs: shrink_splits, shrink_zblocks, down_splits,
+    tile_order; 0 = the library's choice).  With a tuning table
+    (load_tuning), every field left at 0 is taken from the table's nearest
+    entry (moe_lora_tune_apply)."""
     s = moe_lora_shape(int(T), int(H), int(I), int(E), int(topk), int(L), int(r), int(block_m),
-                       float(lora_scale))
-    if tuning is not None and not block_m:
-        bm = moe_lora_tune_block_m(s, tuning)
-        if bm > 0:
-            s.block_m = bm
+                       float(lora_scale), *(int(knobs.pop(k, 0)) for k in KNOBS))
+    if knobs:
+        raise TypeError(f"unknown shape fields {sorted(knobs)}")
+    if tuning is not None:
+        s = moe_lora_tune_apply(s, tuning)
     return s
 
 
 def load_tuning(path: str = TUNING_PATH):
     """Entries of a tile-configuration table written by ``lora_moe_amd.tune``
-    (JSON), as the C array moe_lora_tune_block_m reads."""
+    (JSON), as the C array moe_lora_tune_apply reads (knobs missing from an
+    entry are 0)."""
     import json
     with open(path) as f:
         doc = json.load(f)
     rows = doc["entries"]
     arr = (moe_lora_tune_entry * max(1, len(rows)))()
     for i, e in enumerate(rows):
-        arr[i] = moe_lora_tune_entry(*(int(e[n]) for n, _ in moe_lora_tune_entry._fields_))
+        arr[i] = moe_lora_tune_entry(*(int(e.get(n, 0)) for n, _ in moe_lora_tune_entry._fields_))
     return arr, len(rows)
 
 
 def moe_lora_tune_block_m(shape: moe_lora_shape, tuning, max_dist: float = 0.0) -> int:
     table, n = tuning
     return load_library().moe_lora_tune_block_m(ctypes.byref(shape), table, int(n), float(max_dist))
+
+
+def moe_lora_tune_apply(shape: moe_lora_shape, tuning, max_dist: float = 0.0) -> moe_lora_shape:
+    """A copy of ``shape`` with block_m and the knobs it leaves at 0 taken
+    from the nearest table entry."""
+    table, n = tuning
+    out = moe_lora_shape()
+    _check("moe_lora_tune_apply", min(0, load_library().moe_lora_tune_apply(
+        ctypes.byref(shape), table, int(n), float(max_dist), ctypes.byref(out))))
+    return out
 
 
 def load_library(path: str = LIB_PATH):
@@ -108,6 +126,9 @@ def load_library(path: str = LIB_PATH):
     lib.moe_lora_tune_block_m.argtypes = [sp, ctypes.POINTER(moe_lora_tune_entry), ctypes.c_int32,
                                           ctypes.c_float]
     lib.moe_lora_tune_block_m.restype = i32
+    lib.moe_lora_tune_apply.argtypes = [sp, ctypes.POINTER(moe_lora_tune_entry), ctypes.c_int32,
+                                        ctypes.c_float, sp]
+    lib.moe_lora_tune_apply.restype = i32
     lib.moe_lora_workspace_bytes.argtypes = [sp]
     lib.moe_lora_workspace_bytes.restype = ctypes.c_size_t
     lib.moe_lora_align.argtypes = [sp, vp, vp, vp, ctypes.c_size_t, vp]

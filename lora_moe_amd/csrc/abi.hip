@@ -31,6 +31,12 @@ static int check_shape(const moe_lora_shape* s) {
   const int64_t lim = 1LL << 32, blim = 1LL << 31;
   if ((int64_t)2 * s->I * s->H >= lim || (int64_t)s->T * s->H * 2 >= blim || cap * s->I * 2 >= blim)
     return MOE_LORA_EUNSUPPORTED;
+  // kernel configuration (0 = chosen from the shape)
+  if (s->shrink_splits < 0 || s->shrink_splits > 64) return MOE_LORA_EINVAL;
+  const int zb = s->shrink_zblocks;
+  if (zb < 0 || (zb > 1 && (s->r % zb || (s->r / zb) % 8))) return MOE_LORA_EINVAL;
+  if (s->down_splits < 0 || s->down_splits > 8) return MOE_LORA_EINVAL;
+  if (s->tile_order < 0 || s->tile_order > 2) return MOE_LORA_EINVAL;
   return MOE_LORA_OK;
 }
 
@@ -88,8 +94,15 @@ int make_layout(const moe_lora_shape* s, Layout* L) {
   // The streaming down GEMM splits K when its (row tile x 64-column) grid is
   // small (few experts with wide weights, e.g. dense layers): each split
   // writes its own partial slab of d and the combine adds the slabs in order.
+  L->hsplit = L->I >= kHsplitMinI;
+  L->shrink_splits = s->shrink_splits;
+  L->shrink_zblocks = s->shrink_zblocks;
+  L->tile_order = s->tile_order;
   L->dsplit = 1;
-  if (L->bm <= 32) {
+  if ((L->bm <= 32 || L->hsplit) && s->down_splits > 0) {
+    // the streaming down GEMM splits K in 128-wide chunks
+    L->dsplit = (int)std::min<int64_t>(s->down_splits, std::max<int64_t>(1, L->I / 128));
+  } else if (L->bm <= 32) {
     const int64_t tile_rows = L->bm >= 32 ? 32 : 16;
     // the split count is sized for ~1024 workgroups of an estimated tile
     // grid; at 16-row tiles it counts 64-column tiles (the measured best
@@ -99,7 +112,6 @@ int make_layout(const moe_lora_shape* s, Layout* L) {
     const int64_t chunks = std::max<int64_t>(1, L->I / 128);
     L->dsplit = (int)std::min<int64_t>(std::min<int64_t>(8, chunks), std::max<int64_t>(1, (1024 + tiles - 1) / tiles));
   }
-  L->hsplit = L->I >= kHsplitMinI;
   size_t o = 0;
   auto take = [&](size_t bytes) {
     size_t at = o;
@@ -172,11 +184,12 @@ int moe_lora_resolve_block_m(const moe_lora_shape* shape) {
   return rc ? rc : resolve_bm(shape);
 }
 
-int moe_lora_tune_block_m(const moe_lora_shape* shape, const moe_lora_tune_entry* table, int32_t n,
-                          float max_dist) {
+int moe_lora_tune_apply(const moe_lora_shape* shape, const moe_lora_tune_entry* table, int32_t n,
+                        float max_dist, moe_lora_shape* out) {
   int rc = check_shape(shape);
   if (rc) return rc;
-  if (shape->block_m) return shape->block_m;
+  if (!out) return MOE_LORA_EINVAL;
+  *out = *shape;
   const int64_t P = (int64_t)shape->T * shape->topk;
   const int64_t touched = std::max<int64_t>(1, std::min<int64_t>(shape->E, P));
   const double key[6] = {(double)((P + touched - 1) / touched), (double)shape->H, (double)shape->I,
@@ -205,12 +218,23 @@ int moe_lora_tune_block_m(const moe_lora_shape* shape, const moe_lora_tune_entry
     }
   }
   if (best >= 0) {
+    const moe_lora_tune_entry& t = table[best];
     moe_lora_shape s2 = *shape;
-    s2.block_m = table[best].block_m;
+    if (!s2.block_m) s2.block_m = t.block_m;
+    if (!s2.shrink_splits) s2.shrink_splits = t.shrink_splits;
+    if (!s2.shrink_zblocks) s2.shrink_zblocks = t.shrink_zblocks;
+    if (!s2.down_splits) s2.down_splits = t.down_splits;
+    if (!s2.tile_order) s2.tile_order = t.tile_order;
     Layout L;
-    if (make_layout(&s2, &L) == MOE_LORA_OK) return s2.block_m;
+    if (make_layout(&s2, &L) == MOE_LORA_OK) *out = s2;  // else: the entry does not fit this shape
   }
-  return resolve_bm(shape);
+  return resolve_bm(out);
+}
+
+int moe_lora_tune_block_m(const moe_lora_shape* shape, const moe_lora_tune_entry* table, int32_t n,
+                          float max_dist) {
+  moe_lora_shape out;
+  return moe_lora_tune_apply(shape, table, n, max_dist, &out);
 }
 
 size_t moe_lora_workspace_bytes(const moe_lora_shape* shape) {

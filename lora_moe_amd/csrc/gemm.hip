@@ -327,6 +327,7 @@ int launch_gemm(const Layout& L, int mode, const uint16_t* in, const int32_t* lo
   gp.bm = L.bm;
   gp.nsteps = (gp.K + 63) / 64;
   gp.ksplit = mode == 1 ? L.dsplit : 1;
+  gp.order = L.tile_order ? L.tile_order : (mode == 0 ? 1 : 2);
   gp.d_slab = L.cap_rows * (int64_t)L.H;
   gp.s = L.s;
   if (mode == 1 && L.hsplit) {

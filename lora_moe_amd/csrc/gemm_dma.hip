@@ -106,15 +106,15 @@ __global__ __launch_bounds__(C::NT, WAVES_PER_SIMD) void grouped_gemm_dma_kernel
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / C::WN, wn = wave % C::WN;
   const int l32 = lane & 31, khalf = lane >> 5;
-  // Tile of this workgroup.  mode 0: row tile-major.  mode 1: workgroup i
-  // runs on XCD i mod 8, and row tile m goes to XCD m mod 8 with all its
-  // column tiles, so that its A panel (h rows) is fetched into one L2 only.
-  // Down GEMMs with this order against the row tile-major one (two
-  // alternating runs on one box, us): GPT-OSS-like 106 -> 103, Qwen3-MoE-like
-  // 212 -> 205, DeepSeek-like 3277 -> 3257; the same order for gate_up was
-  // neutral to 3 % slower.
+  // Tile of this workgroup.  order 1 (gate_up by default): row tile-major.
+  // order 2 (down by default): workgroup i runs on XCD i mod 8, and row tile
+  // m goes to XCD m mod 8 with all its column tiles, so that its A panel (h
+  // rows) is fetched into one L2 only.  Down GEMMs with order 2 against
+  // order 1 (two alternating runs on one box, us): GPT-OSS-like 106 -> 103,
+  // Qwen3-MoE-like 212 -> 205, DeepSeek-like 3277 -> 3257; order 2 for
+  // gate_up was neutral to 3 % slower.  The shape's tile_order overrides.
   int mtile, ntc;
-  if (MODE == 1) {
+  if (p.order == 2) {
     const int x = blockIdx.x & 7, j = blockIdx.x >> 3;
     const int k = j / p.ncol;
     ntc = j - k * p.ncol;
@@ -124,7 +124,7 @@ __global__ __launch_bounds__(C::NT, WAVES_PER_SIMD) void grouped_gemm_dma_kernel
     ntc = blockIdx.x - mtile * p.ncol;
   }
   const int row0 = mtile * BM;
-  // (mode 1 rounds the row tiles up to a multiple of 8)
+  // (order 2 rounds the row tiles up to a multiple of 8)
   if (mtile >= p.nrowt || row0 >= p.hdr[HDR_NUM_PADDED]) return;
   int* row_ok = reinterpret_cast<int*>(smem + C::RING);
   float* row_w = reinterpret_cast<float*>(smem + C::RING + BM * 4);
@@ -438,7 +438,7 @@ int launch_dma(const GemmParams& gp_in, int mode, int64_t cap_rows, hipStream_t 
   GemmParams gp = gp_in;
   gp.ncol = mode == 0 ? (gp.I + C::BN / 2 - 1) / (C::BN / 2) : (gp.N + C::BN - 1) / C::BN;
   gp.nrowt = (int)((cap_rows + C::BM - 1) / C::BM);
-  const unsigned grid = (unsigned)gp.ncol * (unsigned)(mode == 0 ? gp.nrowt : (gp.nrowt + 7) / 8 * 8);
+  const unsigned grid = (unsigned)gp.ncol * (unsigned)(gp.order == 2 ? (gp.nrowt + 7) / 8 * 8 : gp.nrowt);
   const bool even = gp.K % C::BK == 0;
   const void* fn =
       mode == 0 ? (even ? reinterpret_cast<const void*>(&grouped_gemm_dma_kernel<0, C, WAVES_PER_SIMD, true>)

@@ -36,6 +36,8 @@ struct Layout {
   int64_t P, cap_rows, cap_blocks, NB, C, TS, max_tiles;
   int dsplit;  // K splits of the down GEMM (d holds one partial slab per split)
   int hsplit;  // h also stored as its bf16 remainder lo (I >= kHsplitMinI)
+  int shrink_splits, shrink_zblocks;  // requested by the shape (0: chosen by plan_shrink)
+  int tile_order;                     // requested order of the tiled GEMMs (0: per mode)
   size_t off_hdr, off_sorted, off_eoff, off_segstart, off_segcnt, off_bexp, off_pos;
   size_t off_chunk, off_chunkerr, off_rank, off_tiles, off_zgu, off_zd, off_zbgu, off_zbd, off_h, off_hlo,
       off_d, total;
@@ -118,6 +120,7 @@ struct GemmParams {
   int K, N, I, H, E, L, r, topk, P, bm, nsteps;
   int ncol, nrowt;  // tiled family: column tiles and row tiles of the launch
   int ksplit;       // streaming family, mode 1: K splits (d_out slab per split)
+  int order;        // tiled family: 1 row tile-major, 2 row tiles interleaved over XCDs
   int64_t d_slab;   // elements between the d_out slabs of consecutive splits
   float s;
 };

@@ -240,6 +240,7 @@ static int64_t shrink_tiles_est(const Layout& L) {
 // CUs that drew two whole tiles bound the kernel, and at the GPT-OSS-like
 // shape (364 tiles, r = 32) the two shrinks went 21.4 + 22.0 -> 18.7 + 20.0 us.
 static int shrink_col_blocks(const Layout& L, int splits) {
+  if (L.shrink_zblocks > 0) return L.shrink_zblocks;  // set by the shape (validated: r / blocks % 8 == 0)
   return (L.r % 16 == 0 && shrink_tiles_est(L) * splits < 1024) ? L.r / 16 : 1;
 }
 
@@ -252,6 +253,7 @@ ShrinkPlan plan_shrink(const Layout& L, int K) {
   // (no atomics, and the align then has no accumulators to clear)
   int splits = est >= 384 ? 1 : (int)std::max<int64_t>(1, 2048 / est);
   splits = std::min(splits, std::max(1, nsteps / 4));  // >= 4 steps: one per wavefront
+  if (L.shrink_splits > 0) splits = std::min(L.shrink_splits, nsteps);  // set by the shape
   sp.splits = splits;
   const int64_t items = L.max_tiles * splits * shrink_col_blocks(L, splits);
   sp.grid = (int)std::max<int64_t>(1, std::min<int64_t>(items, 4096));

@@ -182,6 +182,10 @@ def test_committed_tuning_table_is_valid(lib):
         wl = byname[e["workload"]]
         shape = lm.make_shape(wl.T, wl.H, wl.I, wl.E, wl.topk, wl.L, wl.r, 0, wl.scale, tuning=table)
         assert shape.block_m == e["block_m"]
+        for k in lm.KNOBS:
+            assert getattr(shape, k) == e.get(k, 0), (e["workload"], k)
+            if e.get(k, 0):  # a stored knob beat the library's own choice in the sweep
+                assert k in e["knob_ms"] and str(e[k]) in e["knob_ms"][k]
 
 
 # ------------------------------------------------------------------ views, operand checks, h hi + lo
@@ -266,3 +270,41 @@ def test_operand_checks_refuse_before_launch():
                           ok["W_gu"], ok["W_down"], ok["A_gu"], ok["B_gu"], ok["A_down"], ok["B_down"])
     with pytest.raises(ValueError, match="logits: shape"):
         lm.moe_lora_route(shape, torch.zeros(T, E + 1), ok["topk_ids"], ok["topk_weights"])
+
+
+def test_kernel_knob_validation(lib):
+    """Kernel configuration fields: 0 or an allowed value, else EINVAL; the
+    down-GEMM K split shows in the workspace view (streaming family only)."""
+    base = dict(T=40, H=256, I=512, E=4, topk=2, L=2, r=32)
+    ok = [dict(shrink_splits=64), dict(shrink_zblocks=4), dict(shrink_zblocks=2), dict(down_splits=8),
+          dict(tile_order=2)]
+    bad = [dict(shrink_splits=65), dict(shrink_splits=-1), dict(shrink_zblocks=3), dict(shrink_zblocks=8),
+           dict(down_splits=9), dict(tile_order=3)]
+    for k in ok:
+        assert lm.moe_lora_workspace_bytes(lm.make_shape(**base, **k)) > 0, k
+    for k in bad:
+        s = lm.make_shape(**base, **k)
+        assert lm.moe_lora_resolve_block_m(s) == lm.MOE_LORA_EINVAL, k
+        assert lm.moe_lora_workspace_bytes(s) == 0, k
+    v = lm.moe_lora_workspace_view(lm.make_shape(**base, block_m=16, down_splits=3), _fake_ws())
+    assert v.d_splits == 3
+    v = lm.moe_lora_workspace_view(lm.make_shape(**base, block_m=128, down_splits=3), _fake_ws())
+    assert v.d_splits == 1  # the tiled down GEMM does not split K
+    with pytest.raises(TypeError):
+        lm.make_shape(**base, no_such_knob=1)
+
+
+def test_tune_apply_fills_knobs(lib):
+    """moe_lora_tune_apply copies block_m and the knobs of the nearest entry
+    into the fields the shape leaves at 0."""
+    decode = lm.make_shape(16, 4096, 11008, 8, 2, 8, 32)
+    table = (lm.moe_lora_tune_entry * 1)(lm.moe_lora_tune_entry(4, 4096, 11008, 8, 32, 8, 16, 4, 2, 3, 0))
+    out = lm.moe_lora_tune_apply(decode, (table, 1))
+    assert (out.block_m, out.shrink_splits, out.shrink_zblocks, out.down_splits, out.tile_order) == (16, 4, 2, 3, 0)
+    own = lm.make_shape(16, 4096, 11008, 8, 2, 8, 32, shrink_splits=7)
+    assert lm.moe_lora_tune_apply(own, (table, 1)).shrink_splits == 7
+    assert lm.make_shape(16, 4096, 11008, 8, 2, 8, 32, tuning=(table, 1)).down_splits == 3
+    # an entry whose knobs do not fit the shape leaves it unchanged (r = 8: 2 z blocks invalid)
+    small = lm.make_shape(16, 4096, 11008, 8, 2, 8, 8)
+    t2 = (lm.moe_lora_tune_entry * 1)(lm.moe_lora_tune_entry(4, 4096, 11008, 8, 8, 8, 16, 0, 2, 0, 0))
+    assert lm.moe_lora_tune_apply(small, (t2, 1)).shrink_zblocks == 0

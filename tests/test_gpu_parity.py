@@ -340,3 +340,27 @@ def test_forward_needs_its_own_align():
     for rep in range(2):
         y, _, _ = run_gpu(dev, wl, workspace=ws)
         compare(y, ref, f"align + forward, call {rep}")
+
+
+@pytest.mark.parametrize("bm,knobs", [
+    (16, dict(shrink_splits=1)), (16, dict(shrink_splits=8, shrink_zblocks=2)), (32, dict(down_splits=3)),
+    (64, dict(shrink_splits=4, tile_order=2)), (128, dict(shrink_zblocks=1, tile_order=2)),
+    (192, dict(shrink_splits=2, shrink_zblocks=2, tile_order=1)), (256, dict(tile_order=1, shrink_splits=16)),
+    (256, dict(tile_order=2))])
+def test_kernel_knobs(bm, knobs):
+    """Non-default kernel configurations (shrink K splits and z column blocks,
+    down-GEMM K splits, tiled-GEMM workgroup order) give the same layer."""
+    wl = synth.Workload("knobs", T=150, H=1024, I=512, E=6, topk=2, L=3, r=16,
+                        lora_mode="uniform_with_none", seed=21)
+    inp = synth.make_inputs(wl)
+    import lora_moe_amd as lm
+    shape = lm.make_shape(wl.T, wl.H, wl.I, wl.E, wl.topk, wl.L, wl.r, bm, wl.scale, **knobs)
+    log(f"knobs bm={bm} {knobs}")
+    dev = to_device(inp)
+    ws = lm.alloc_workspace(shape)
+    y = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda")
+    lm.moe_lora_align(shape, dev["topk_ids"], dev["lora_ids"], ws)
+    lm.moe_lora_forward(shape, dev["x"], dev["topk_ids"], dev["topk_weights"], dev["lora_ids"], dev["W_gu"],
+                        dev["W_down"], dev["A_gu"], dev["B_gu"], dev["A_down"], dev["B_down"], ws, y)
+    torch.cuda.synchronize()
+    compare(y.float().cpu().numpy().astype(np.float64), oracle_tokens(inp, None), f"knobs bm={bm} {knobs}")

@@ -1,5 +1,10 @@
-"""The layer at the block_m the shipped tile-configuration table picks
-matches the fp64 reference, for a shape in the table's range but not in it."""
+"""The layer at the configuration the shipped tuning table picks matches the
+fp64 reference: for a shape in the table's range but not in it, and at full
+size for every entry whose stored knobs differ from the library's own
+choice."""
+import json
+
+import numpy as np
 import pytest
 
 import synth
@@ -34,3 +39,42 @@ def test_tune_sweep_writes_a_valid_table(tmp_path):
     shape = lm.make_shape(wl.T, wl.H, wl.I, wl.E, wl.topk, wl.L, wl.r, 0, wl.scale,
                           tuning=lm.load_tuning(str(out)))
     assert shape.block_m == e["block_m"]
+
+
+def tuned_entries():
+    import lora_moe_amd as lm
+    doc = json.load(open(lm.TUNING_PATH))
+    return [e["workload"] for e in doc["entries"] if any(e.get(k, 0) for k in lm.KNOBS)]
+
+
+@pytest.mark.parametrize("name", tuned_entries())
+def test_full_size_at_tuned_configuration(name):
+    """A shape whose tuned knobs beat the built-in choice in the sweep, run at
+    that configuration at full size against the reference (every token)."""
+    import torch
+
+    import lora_moe_amd as lm
+    from gpu_common import compare, compare_delta, log, oracle_tokens
+    wl = next(w for w in synth.WORKLOADS.values() if w.name == name)
+    shape = lm.make_shape(wl.T, wl.H, wl.I, wl.E, wl.topk, wl.L, wl.r, 0, wl.scale, tuning=lm.load_tuning())
+    knobs = {k: getattr(shape, k) for k in lm.KNOBS}
+    assert any(knobs.values())
+    log(f"{name} at the tuned configuration: block_m {shape.block_m} {knobs}")
+    dev, inp = synth.device_inputs(wl, touched_only=True, keep_host=True)
+
+    def run(lids):
+        ws = lm.alloc_workspace(shape)
+        y = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda")
+        lm.moe_lora_align(shape, dev["topk_ids"], lids, ws)
+        lm.moe_lora_forward(shape, dev["x"], dev["topk_ids"], dev["topk_weights"], lids, dev["W_gu"],
+                            dev["W_down"], dev["A_gu"], dev["B_gu"], dev["A_down"], dev["B_down"], ws, y)
+        torch.cuda.synchronize()
+        return y.float().cpu().numpy().astype(np.float64)
+
+    y = run(dev["lora_ids"])
+    ref = oracle_tokens(inp, None)
+    compare(y, ref, f"{name} tuned")
+    y0 = run(torch.full_like(dev["lora_ids"], -1))
+    ref0 = oracle_tokens(inp, None, lora_ids=np.full_like(inp.lora_ids, -1))
+    compare(y0, ref0, f"{name} tuned, no adapters")
+    compare_delta(y, y0, ref, ref0, f"{name} tuned")
