@@ -53,14 +53,16 @@ def test_batch_sizes_1_to_64():
     for T, dev_ms, host_ms in times:
         log(f"T={T}: align + forward {dev_ms * 1e3:.1f} us on the device, {host_ms:.3f} ms to enqueue")
     # no call after the first pays a module load or a compile (those take
-    # milliseconds to seconds): every later call enqueues within 2 ms, and its
-    # device time stays within 5x the median
+    # milliseconds to seconds and would hit every new T): at most two later
+    # calls take over 2 ms to enqueue or over 5x the median device time (a
+    # profiler or the host can stall a call or two; a per-length compile would
+    # stall all 63)
     later = times[1:]
     med_dev = float(np.median([d for _, d, _ in later]))
-    worst_host = max(later, key=lambda t: t[2])
-    worst_dev = max(later, key=lambda t: t[1])
-    assert worst_host[2] < 2.0, f"T={worst_host[0]} took {worst_host[2]:.2f} ms to enqueue"
-    assert worst_dev[1] < 5 * med_dev, f"T={worst_dev[0]}: {worst_dev[1]:.3f} ms vs median {med_dev:.3f}"
+    slow_host = [(T, round(h, 2)) for T, _, h in later if h > 2.0]
+    slow_dev = [(T, round(d, 3)) for T, d, _ in later if d > 5 * med_dev]
+    assert len(slow_host) <= 2, f"slow to enqueue: {slow_host}"
+    assert len(slow_dev) <= 2, f"slow on the device (median {med_dev:.3f} ms): {slow_dev}"
 
 
 if __name__ == "__main__":  # for a kernel trace of this sequence alone
