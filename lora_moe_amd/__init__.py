@@ -66,18 +66,25 @@ class moe_lora_tune_entry(ctypes.Structure):
                 + KNOBS]
 
 
+# An entry's tuned configuration applies to shapes within this distance of
+# its key (sum over rows per expert (x4), H, I, E, r, L of |log2 ratio|):
+# e.g. a shape with half or twice the entry's rows per expert and the same
+# sizes otherwise; farther shapes keep the built-in choice.
+TUNE_MAX_DIST = 4.0
+
+
 def make_shape(T, H, I, E, topk, L, r, block_m=0, lora_scale=1.0, tuning=None,
-               **knobs) -> moe_lora_shape:
+               max_dist=TUNE_MAX_DIST, **knobs) -> moe_lora_shape:
     """The shape struct (knobs: shrink_splits, shrink_zblocks, down_splits,
     tile_order; 0 = the library's choice).  With a tuning table
     (load_tuning), every field left at 0 is taken from the table's nearest
-    entry (moe_lora_tune_apply)."""
+    entry within max_dist (moe_lora_tune_apply)."""
     s = moe_lora_shape(int(T), int(H), int(I), int(E), int(topk), int(L), int(r), int(block_m),
                        float(lora_scale), *(int(knobs.pop(k, 0)) for k in KNOBS))
     if knobs:
         raise TypeError(f"unknown shape fields {sorted(knobs)}")
     if tuning is not None:
-        s = moe_lora_tune_apply(s, tuning)
+        s = moe_lora_tune_apply(s, tuning, max_dist)
     return s
 
 
