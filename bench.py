@@ -33,6 +33,24 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 FLUSH_MB = 512                 # > L2 (8 x 4 MB) + MALL (256 MB)
 
 
+class Flush:
+    """Evicts L2 and the MALL before a timed call: a FLUSH_MB write, then a
+    read of a second FLUSH_MB buffer, so the caches hold clean lines of
+    neither the layer's data nor anything dirty (a write alone leaves up to
+    ~288 MB of dirty lines whose write-back would land in the timed call).
+    ``dirty=True`` does the write only."""
+
+    def __init__(self, dirty=False):
+        import torch
+        self.w = torch.empty(FLUSH_MB << 20, dtype=torch.uint8, device="cuda")
+        self.r = None if dirty else torch.ones(FLUSH_MB << 18, dtype=torch.int32, device="cuda")
+
+    def __call__(self):
+        self.w.fill_(1)
+        if self.r is not None:
+            self.r.sum()
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -158,14 +176,14 @@ def read_probe(mb, iters=10):
     print(json.dumps(out), flush=True)
 
 
-def flushed_calls(step, iters, scratch, profiler=None):
-    """Per-call milliseconds of `iters` align + forward calls, each after a
-    fill of `scratch` (outside the events) that evicts L2 and the MALL."""
+def flushed_calls(step, iters, flush, profiler=None):
+    """Per-call milliseconds of `iters` align + forward calls, each after
+    `flush()` (outside the events) evicts L2 and the MALL."""
     import torch
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(iters)]
     for a, b in ev:
-        scratch.fill_(1)
+        flush()
         a.record()
         step(profiler)
         b.record()
@@ -226,7 +244,7 @@ def cpu_baseline(inp, target_s):
                       f"{', cycled' if n > wl.T else ''}), fp64, {dt:.1f} s wall"}
 
 
-def run_other(lm, synth, n, steps, scratch, tuning):
+def run_other(lm, synth, n, steps, flush, tuning):
     """Flushed median of one more workload (generated, timed, freed)."""
     import torch
     wl = synth.WORKLOADS[n]
@@ -245,7 +263,7 @@ def run_other(lm, synth, n, steps, scratch, tuning):
 
     for _ in range(3):
         step()
-    ts = flushed_calls(step, steps, scratch)
+    ts = flushed_calls(step, steps, flush)
     med = statistics.median(ts)
     out = {"workload": wl.name, "block_m": lm.moe_lora_resolve_block_m(shape),
            "knobs": {k: getattr(shape, k) for k in lm.KNOBS},
@@ -286,7 +304,7 @@ def main():
     ws = lm.alloc_workspace(shape)
     y = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda")
     stream = torch.cuda.current_stream()
-    scratch = torch.empty(FLUSH_MB << 20, dtype=torch.uint8, device="cuda")
+    flush = Flush()
 
     def step(prof=None, st=stream):
         lm.moe_lora_align(shape, dev["topk_ids"], dev["lora_ids"], ws, st, profiler=prof)
@@ -303,7 +321,7 @@ def main():
     # timed ones): the per-stage breakdown, and which stage dominates
     nbreak = max(1, min(args.steps, 10))
     prof = lm.Profiler(nbreak)
-    flushed_calls(step, nbreak, scratch, prof)
+    flushed_calls(step, nbreak, flush, prof)
     stage_ms, calls = prof.read()
     prof.close()
     per_stage = {k: v / max(calls, 1) for k, v in stage_ms.items()}
@@ -315,7 +333,7 @@ def main():
     prof = lm.Profiler(args.steps, [dom])
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    call_ms = flushed_calls(step, args.steps, scratch, prof)
+    call_ms = flushed_calls(step, args.steps, flush, prof)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     dom_ms, dom_calls = prof.read()
@@ -348,9 +366,10 @@ def main():
                    "topk": wl.topk, "L": wl.L, "r": wl.r,
                    "block_m": bm, "seed": wl.seed, **{k: getattr(shape, k) for k in lm.KNOBS}},
         "roofline": roof,
-        "timing": {"per_step": "one align + forward call after a 512 MB fill (L2 and MALL "
-                               "cold), HIP events around the call; value and ms_per_step from "
-                               "the median call", "median_ms": ms_per_step,
+        "timing": {"per_step": "one align + forward call after a 512 MB write and a read of "
+                               "another 512 MB (L2 and MALL cold and clean), HIP events around "
+                               "the call; value and ms_per_step from the median call",
+                   "median_ms": ms_per_step,
                    "min_ms": min(call_ms), "max_ms": max(call_ms),
                    "wall_s_timed_region": elapsed},
         "layer": {"alg_bytes": work["bytes"], "alg_flops": work["flops"], "bound": binding(work),
@@ -363,6 +382,11 @@ def main():
     if not args.no_extras:
         out["warm"] = {"ms_per_step": warm_calls(step, args.steps),
                        "note": "back-to-back calls, caches warm"}
+        dirty = Flush(dirty=True)
+        out["flushed_dirty"] = {"median_ms": statistics.median(flushed_calls(step, args.steps, dirty)),
+                                "note": "each call after the 512 MB write only (its dirty lines are "
+                                        "written back during the call)"}
+        del dirty
         # the path from router logits: moe_lora_route_align (router fused into
         # the align for small batches) + moe_lora_forward.  The logits are built
         # so the router reproduces the workload's routing: log(w) at each chosen
@@ -415,7 +439,7 @@ def main():
                                             **layer_fracs(work, ms_per_step)}}
         for n in others:
             if n != args.workload:
-                out["workloads"][n] = run_other(lm, synth, n, args.other_steps, scratch, tuning)
+                out["workloads"][n] = run_other(lm, synth, n, args.other_steps, flush, tuning)
     print(json.dumps(out), flush=True)
 
 
