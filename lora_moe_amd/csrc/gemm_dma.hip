@@ -36,7 +36,9 @@
 //     and up columns in the same lane) or the top-k weight (mode 1); the rows'
 //     validity and weights are staged in LDS at the start.
 // A wavefront whose rows are all padding skips its MFMAs and stores but still
-// copies its share of every stage.
+// copies its share of every stage.  256-row tiles with at most 64 real rows
+// run on a ring of thin stages (64 A rows + the W tile) that keeps two stages
+// in flight instead of one.
 #include <type_traits>
 
 #include "device_util.h"
@@ -85,6 +87,10 @@ struct DmaCfg {
   static_assert(NCA >= 1 && NCA * ROWS_PER_COPY == AROWS && NCW * ROWS_PER_COPY == WROWS, "copy layout");
   static_assert(LDS <= 160 * 1024, "LDS ring exceeds 160 KB");
   static_assert(NS >= 2, "ring needs two stages");
+  // thin ring for row tiles with at most TR real rows: stages of TR A rows
+  // and the whole W tile, TNS of them in the same LDS (3 at 256 x 256)
+  static constexpr int TR = 64, TATILE = TR * PROW, TSTAGE = TATILE + WTILE;
+  static constexpr int TNS = RING / TSTAGE;
 
   // chunk slot of logical chunk `chunk` in tile row `row`: consecutive 16-lane
   // phases of a fragment read cover 16 rows and all 64 banks
@@ -181,12 +187,22 @@ __global__ __launch_bounds__(C::NT, WAVES_PER_SIMD) void grouped_gemm_dma_kernel
     w_off[i] = (uint32_t)tile_col(r) * (uint32_t)p.K + (uint32_t)(ch * 8);
   }
 
+  // thin ring: wavefront w copies A rows [8w, 8w + 8) (one copy), W as usual
+  uint32_t a_off_t = kBufNone;
+  {
+    const int r = wave * RPC + lrow;
+    const int ch = C::swz(r, lslot);
+    const int pr = p.sorted[row0 + r];
+    const int arow = MODE == 0 ? pr / p.topk : row0 + r;
+    a_off_t = pr < p.P ? (uint32_t)(arow * p.K + ch * 8) * 2u : kBufNone;
+  }
   const int ntile = (p.K + BK - 1) / BK;  // the last stage may be partial
   const bool partial = !EVENK && (p.K % BK) != 0;
-  auto issue = [&](int s, auto nt_c) {
+  auto issue = [&](int s, auto nt_c, auto thin_c) {
     constexpr bool NTL = decltype(nt_c)::value;
-    char* A = smem + (s % NS) * C::STAGE;
-    char* B = A + C::ATILE;
+    constexpr bool THIN = decltype(thin_c)::value;
+    char* A = THIN ? smem + (s % C::TNS) * C::TSTAGE : smem + (s % NS) * C::STAGE;
+    char* B = A + (THIN ? C::TATILE : C::ATILE);
     const int k0 = s * BK;
     auto ldA = [&](int i) {
       int koff = k0;
@@ -205,8 +221,13 @@ __global__ __launch_bounds__(C::NT, WAVES_PER_SIMD) void grouped_gemm_dma_kernel
     // all A copies of the stage, then all W copies: at 256 x 256 this order
     // ran the Qwen3-MoE-like gate_up in 273 us against 283 us with each A
     // copy followed by its W copy (three alternating runs on one box)
+    if (THIN) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rs, (lds_char*)(A + wave * RPC * PROW), 16,
+                                               (int)(a_off_t + (uint32_t)k0 * 2u), 0, 0, 0);
+    } else {
 #pragma unroll
-    for (int i = 0; i < NCA; ++i) ldA(i);
+      for (int i = 0; i < NCA; ++i) ldA(i);
+    }
 #pragma unroll
     for (int i = 0; i < NCW; ++i) ldW(i);
   };
@@ -244,12 +265,15 @@ __global__ __launch_bounds__(C::NT, WAVES_PER_SIMD) void grouped_gemm_dma_kernel
   for (int mi = 0; mi < MI; ++mi)
     blk_live[mi] = __builtin_amdgcn_readfirstlane(p.sorted[row0 + wrow + 32 * mi] < p.P);
   u32x4_t af[2][MI], bf[2][NI];
-  auto frag = [&](int s, int kk, int set) {
-    const char* A = smem + (s % NS) * C::STAGE;
-    const char* B = A + C::ATILE;
+  // THIN: the ring holds tile rows [0, 64) only; the wavefronts that read
+  // it (rows from 0) use row blocks 0 and 1
+  auto frag = [&](int s, int kk, int set, auto thin_c) {
+    constexpr bool THIN = decltype(thin_c)::value;
+    const char* A = THIN ? smem + (s % C::TNS) * C::TSTAGE : smem + (s % NS) * C::STAGE;
+    const char* B = A + (THIN ? C::TATILE : C::ATILE);
     const int ch = 2 * kk + khalf;
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
+    for (int mi = 0; mi < (THIN ? C::TR / 32 : MI); ++mi)
       af[set][mi] = *reinterpret_cast<const u32x4_t*>(A + C::off(wrow + mi * 32 + l32, ch));
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni)
@@ -261,13 +285,14 @@ __global__ __launch_bounds__(C::NT, WAVES_PER_SIMD) void grouped_gemm_dma_kernel
   // conservative wait there costs nothing, and the reads overlap the rest.
   // The scheduling barriers keep this order (the scheduler would otherwise
   // sink the reads next to their use).
-  auto step = [&](int set, bool next, int qn, int kkn) {
+  auto step = [&](int set, bool next, int qn, int kkn, auto thin_c) {
+    constexpr bool THIN = decltype(thin_c)::value;
     acc[0][0] = mfma_32x32x16(bf[set][0], af[set][0], acc[0][0]);
     __builtin_amdgcn_sched_barrier(0);
-    if (next) frag(qn, kkn, set ^ 1);
+    if (next) frag(qn, kkn, set ^ 1, thin_c);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
+    for (int mi = 0; mi < (THIN ? C::TR / 32 : MI); ++mi)
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni)
         if ((mi | ni) && (mi == 0 || blk_live[mi]))
@@ -303,12 +328,15 @@ __global__ __launch_bounds__(C::NT, WAVES_PER_SIMD) void grouped_gemm_dma_kernel
   xi.nitems = 0;
   xi.next = 0;
   bool xpend = false;  // an item is loaded and not yet multiplied
-  auto kloop = [&](auto live_c, auto nt_c) {
+  auto kloop = [&](auto live_c, auto nt_c, auto thin_c) {
     constexpr bool LIVE = decltype(live_c)::value;
+    constexpr bool THIN = decltype(thin_c)::value;
+    constexpr int RNS = THIN ? C::TNS : NS;  // stages in the ring
+    constexpr int VMA = THIN ? (1 + NCW) * (C::TNS - 2) : VM_AHEAD;
     // prologue: every ring slot gets a stage; wait for stage 0
 #pragma unroll
-    for (int s = 0; s < NS; ++s)
-      if (s < ntile) issue(s, nt_c);
+    for (int s = 0; s < RNS; ++s)
+      if (s < ntile) issue(s, nt_c, thin_c);
     if (LIVE && XPIPE) {
       expand_items_init(xi, p, e, row0 + wrow, 0);
       if (xi.nitems > ntile - 1) xi.nitems = -1;  // does not fit: batched, after the loop
@@ -325,22 +353,22 @@ __global__ __launch_bounds__(C::NT, WAVES_PER_SIMD) void grouped_gemm_dma_kernel
     if (partial && ntile == 1) zero_tail(0);
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     stage_barrier();
-    if (LIVE) frag(0, 0, 0);
+    if (LIVE) frag(0, 0, 0, thin_c);
     for (int q = 0; q + 1 < ntile; ++q) {
 #pragma unroll
       for (int kk = 0; kk + 1 < KK; ++kk)
-        if (LIVE) step(kk & 1, true, q, kk + 1);
+        if (LIVE) step(kk & 1, true, q, kk + 1, thin_c);
       // own copies of stage q + 1 have landed (later stages may still fly);
       // the wait stays behind this stage's MFMAs
       __builtin_amdgcn_sched_barrier(0);
-      if (q + NS - 1 < ntile)
-        __builtin_amdgcn_s_waitcnt(wait_vm(VM_AHEAD));
+      if (q + RNS - 1 < ntile)
+        __builtin_amdgcn_s_waitcnt(wait_vm(VMA));
       else
         __builtin_amdgcn_s_waitcnt(wait_vm(0));
       if (partial && q + 1 == ntile - 1) zero_tail(q + 1);
       __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // fragment reads of stage q and zero writes done
       stage_barrier();
-      if (q + NS < ntile) issue(q + NS, nt_c);  // into the slot stage q just released
+      if (q + RNS < ntile) issue(q + RNS, nt_c, thin_c);  // into the slot stage q just released
       if (LIVE && xpend) {
         expand_item_mfma(xi, acc, row0 + wrow);
         xpend = xi.next < xi.nitems;
@@ -348,22 +376,38 @@ __global__ __launch_bounds__(C::NT, WAVES_PER_SIMD) void grouped_gemm_dma_kernel
       }
       // last slice of stage q (its fragments are in registers), with the
       // first reads of stage q + 1
-      if (LIVE) step((KK - 1) & 1, true, q + 1, 0);
+      if (LIVE) step((KK - 1) & 1, true, q + 1, 0, thin_c);
     }
     if (LIVE) {  // the last stage
 #pragma unroll
-      for (int kk = 0; kk + 1 < KK; ++kk) step(kk & 1, true, ntile - 1, kk + 1);
-      step((KK - 1) & 1, false, 0, 0);
+      for (int kk = 0; kk + 1 < KK; ++kk) step(kk & 1, true, ntile - 1, kk + 1, thin_c);
+      step((KK - 1) & 1, false, 0, 0, thin_c);
     }
   };
   typedef std::integral_constant<bool, true> yes;
   typedef std::integral_constant<bool, false> no;
-  if (live) {
-    if (w_once) kloop(yes(), yes());
-    else kloop(yes(), no());
+  // Thin row tiles (at most 64 real rows, the rest padding: an expert's
+  // last tile) fetch little besides the weight tile, so the per-CU fetch
+  // latency bounds them; their ring holds 64 A rows per stage, which makes
+  // room for three stages (two in flight) in the same LDS.  At the
+  // DeepSeek-like shape (89 of 359 row tiles are thin) the layer went
+  // 8.50 -> 8.26 ms (three alternating runs on one box, same outputs).
+  // 256-row tiles only, and K without a remainder (no zero_tail).
+  const bool thin = EVENK && BM == 256 && C::TNS >= 3 && p.sorted[row0 + C::TR] >= p.P;
+  if (thin) {
+    if (live) {
+      if (w_once) kloop(yes(), yes(), yes());
+      else kloop(yes(), no(), yes());
+    } else {
+      if (w_once) kloop(no(), yes(), yes());
+      else kloop(no(), no(), yes());
+    }
+  } else if (live) {
+    if (w_once) kloop(yes(), yes(), no());
+    else kloop(yes(), no(), no());
   } else {
-    if (w_once) kloop(no(), yes());
-    else kloop(no(), no());
+    if (w_once) kloop(no(), yes(), no());
+    else kloop(no(), no(), no());
   }
   if (!live) return;
 

@@ -1,5 +1,6 @@
 """The layer at the configuration the shipped tuning table picks matches the
-fp64 reference: for a shape in the table's range but not in it, and at full
+fp64 reference: for a shape near a table entry but not in it, for a shape
+far from every entry (the pick leaves the library's own choice), and at full
 size for every entry whose stored knobs differ from the library's own
 choice."""
 import json
@@ -13,14 +14,25 @@ from test_gpu_parity import full_check
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("n", [1])
-def test_layer_at_tuned_block_m(n):
+@pytest.mark.parametrize("n,T,near", [(3, 192, True), (1, None, False)])
+def test_layer_at_tuned_block_m(n, T, near):
+    """GPT-OSS-like at 192 tokens (24 rows per expert against the entry's 32)
+    takes that entry's block_m; the tiny shape is beyond the pick's distance
+    and keeps block_m 0, which the library resolves itself."""
     import lora_moe_amd as lm
     table = lm.load_tuning()
-    wl = synth.WORKLOADS[n]
+    inp = synth.make_inputs(n, T=T)
+    wl = inp.wl
     shape = lm.make_shape(wl.T, wl.H, wl.I, wl.E, wl.topk, wl.L, wl.r, 0, wl.scale, tuning=table)
-    assert shape.block_m in (16, 32, 64, 128, 192, 256)
-    full_check(synth.make_inputs(wl), shape.block_m, f"workload {n} at tuned block_m {shape.block_m}")
+    if near:
+        entries = json.load(open(lm.TUNING_PATH))["entries"]
+        entry = next(e for e in entries if e["workload"] == synth.WORKLOADS[n].name)
+        assert shape.block_m == entry["block_m"]
+    else:
+        assert shape.block_m == 0
+    bm = lm.moe_lora_resolve_block_m(shape)
+    assert bm in (16, 32, 64, 128, 192, 256)
+    full_check(inp, shape.block_m, f"workload {n} T={wl.T} at tuned block_m {bm}")
 
 
 def test_tune_sweep_writes_a_valid_table(tmp_path):
