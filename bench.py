@@ -72,6 +72,9 @@ def parse():
                     help="time a bf16 reduction and a device copy over this many MiB (attainable HBM rates)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="only run a plain device copy of this many MB (counter calibration)")
+    ap.add_argument("--gemm-probe", action="store_true",
+                    help="time the vendor bf16 GEMM on dense problems with the projections' flops, and this "
+                         "library's GEMM stages with equal experts (context for the MFMA roofline)")
     return ap.parse_args()
 
 
@@ -173,6 +176,81 @@ def read_probe(mb, iters=10):
         ms = e0.elapsed_time(e1) / iters
         out[f"{name}_ms"] = ms
         out[f"{name}_GBps"] = moved / (ms * 1e-3) / 1e9
+    print(json.dumps(out), flush=True)
+
+
+def gemm_probe(iters=20):
+    """Context for the MFMA roofline, printed as one JSON line.
+
+    vendor: torch.matmul (hipBLASLt) on dense bf16 problems x[M,K] . W[N,K]^T
+    with the flops of the DeepSeek-like projections (M = T*k = 65536 pairs;
+    gate_up N = 2I = 4096, K = H = 7168; down N = 7168, K = 2048) and of the
+    Qwen3-MoE-like ones (M = 16384), median of `iters` launches.
+    library: this library's gemm_gate_up and gemm_down stages (caller-owned
+    profiler) at the DeepSeek-like sizes with every expert equally loaded
+    (T = 8192 tokens spread evenly over 8 experts, top-8, so every row tile
+    is full) and with one expert (T = 65536, top-1): the grouped kernels
+    without the routed shape's ragged tiles.  Random inputs (N(0, 0.02))."""
+    import statistics
+    import torch
+    import lora_moe_amd as lm
+    torch.manual_seed(0)
+    out = {"vendor": [], "library": []}
+    for (what, M, N, K) in (("deepseek-like gate_up", 65536, 4096, 7168), ("deepseek-like down", 65536, 7168, 2048),
+                            ("qwen3moe-like gate_up", 16384, 1536, 2048), ("qwen3moe-like down", 16384, 2048, 768)):
+        a = torch.randn(M, K, device="cuda").to(torch.bfloat16)
+        b = torch.randn(N, K, device="cuda").to(torch.bfloat16)
+        for _ in range(3):
+            c = a @ b.t()
+        torch.cuda.synchronize()
+        ev = []
+        for _ in range(iters):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            c = a @ b.t()
+            e1.record()
+            ev.append((e0, e1))
+        torch.cuda.synchronize()
+        ms = statistics.median(x.elapsed_time(y) for x, y in ev)
+        tf = 2 * M * N * K / ms / 1e9
+        out["vendor"].append({"problem": what, "M": M, "N": N, "K": K, "ms": round(ms, 4),
+                              "TFLOPs": round(tf, 1), "frac_of_2500": round(tf / 2500, 4)})
+        del a, b, c
+    H, I, L, r = 7168, 2048, 8, 64
+    lm.load_library()
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    for T, k, E in ((8192, 8, 8), (65536, 1, 1)):
+        g = lambda *sh: (torch.randn(*sh, device="cuda") * 0.02).to(torch.bfloat16)
+        dev = dict(x=g(T, H), W_gu=g(E, 2 * I, H), W_down=g(E, H, I), A_gu=g(L, E, r, H), B_gu=g(L, E, 2 * I, r),
+                   A_down=g(L, E, r, I), B_down=g(L, E, H, r))
+        ids = torch.argsort(torch.rand(T, E, device="cuda"), dim=1)[:, :k].to(torch.int32).contiguous()
+        wts = torch.full((T, k), 1.0 / k, device="cuda")
+        lids = torch.randint(0, L, (T,), device="cuda", dtype=torch.int32)
+        y = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+        shape = lm.make_shape(T, H, I, E, k, L, r, 256, 1.0)
+        ws = lm.alloc_workspace(shape)
+        prof = lm.Profiler(iters)
+
+        def step(pr=None):
+            lm.moe_lora_align(shape, ids, lids, ws, profiler=pr)
+            lm.moe_lora_forward(shape, dev["x"], ids, wts, lids, dev["W_gu"], dev["W_down"], dev["A_gu"],
+                                dev["B_gu"], dev["A_down"], dev["B_down"], ws, y, profiler=pr)
+        for _ in range(2):
+            step()
+        for _ in range(iters):
+            scratch.fill_(1)
+            step(prof)
+        torch.cuda.synchronize()
+        st, calls = prof.read()
+        prof.close()
+        P = T * k
+        for stage, flops in (("gemm_gate_up", 2 * P * 2 * I * H), ("gemm_down", 2 * P * H * I)):
+            ms = st[stage] / calls
+            out["library"].append({"stage": stage, "T": T, "topk": k, "E": E, "block_m": 256, "ms": round(ms, 4),
+                                   "TFLOPs": round(flops / ms / 1e9, 1),
+                                   "frac_of_2500": round(flops / ms / 1e9 / 2500, 4)})
+        del dev, ws, y
+        torch.cuda.empty_cache()
     print(json.dumps(out), flush=True)
 
 
@@ -288,6 +366,9 @@ def main():
         return
     if args.read_probe_mb:
         read_probe(args.read_probe_mb)
+        return
+    if args.gemm_probe:
+        gemm_probe()
         return
     import lora_moe_amd as lm
     import synth
