@@ -185,6 +185,25 @@ def test_routing_extremes(bm):
     full_check(inp, bm, f"one expert bm={bm}")
 
 
+@pytest.mark.parametrize("H,I", [(256, 256), (264, 200)])
+def test_thin_tiles(H, I):
+    """block_m 256 with experts of exactly 1, 30, 64, 65, 200, 256, 300 and 513
+    rows: row tiles with at most 64 real rows (an expert's only tile, or the
+    last of 300 and 513) run on the tiled GEMM's thin ring when K is a
+    multiple of 64 in both GEMMs (H = I = 256), and on the full ring
+    otherwise (H = 264, I = 200); 65 and 200 rows and the full tiles always
+    take the full ring."""
+    counts = [1, 30, 64, 65, 200, 256, 300, 513]
+    wl = synth.Workload("thin", T=sum(counts), H=H, I=I, E=8, topk=1, L=4, r=16,
+                        lora_mode="uniform_with_none", seed=6)
+    inp = synth.make_inputs(wl)
+    ids = np.repeat(np.arange(len(counts), dtype=np.int32), counts)
+    np.random.default_rng(6).shuffle(ids)
+    inp.topk_ids[:, 0] = ids
+    inp.topk_weights[:] = 1.0
+    full_check(inp, 256, f"thin tiles H={H} I={I}")
+
+
 @pytest.mark.parametrize("T,E,L", [(200, 4, 100), (600, 64, 200)])
 @pytest.mark.parametrize("bm", [0, 32, 64, 128, 192, 256])
 def test_more_than_64_adapters(T, E, L, bm):
