@@ -317,8 +317,7 @@ __global__ __launch_bounds__(C::NT, WAVES_PER_SIMD) void grouped_gemm_dma_kernel
   // barrier of stage q + 1, by when the stage's wait has seen its loads land.
   // Only where a wavefront holds two or more row blocks (with one, the
   // 64 x 128 tile, the expand is short and the loop's extra work cost more:
-  // GPT-OSS-like gate_up 240 -> 249 us, and with the current loop the layer
-  // 0.397 -> 0.403 ms), not for a K with a remainder at
+  // GPT-OSS-like gate_up 240 -> 249 us), not for a K with a remainder at
   // 256 x 256 (the clamped copies need the registers), and only when the
   // items fit in the stages; otherwise the batched expand runs after the
   // loop (the Qwen3-MoE-like down GEMM, 12 stages for ~20 segments per
