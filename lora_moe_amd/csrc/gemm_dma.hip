@@ -392,22 +392,22 @@ __global__ __launch_bounds__(C::NT, WAVES_PER_SIMD) void grouped_gemm_dma_kernel
   // room for three stages (two in flight) in the same LDS.  At the
   // DeepSeek-like shape (89 of 359 row tiles are thin) the layer went
   // 8.50 -> 8.26 ms (three alternating runs on one box, same outputs).
-  // 256-row tiles only, and K without a remainder (no zero_tail).
-  const bool thin = EVENK && BM == 256 && C::TNS >= 3 && p.sorted[row0 + C::TR] >= p.P;
-  if (thin) {
+  // 256-row tiles only (the thin loop exists only for them), and K without
+  // a remainder (no zero_tail).
+  auto run = [&](auto thin_c) {
     if (live) {
-      if (w_once) kloop(yes(), yes(), yes());
-      else kloop(yes(), no(), yes());
+      if (w_once) kloop(yes(), yes(), thin_c);
+      else kloop(yes(), no(), thin_c);
     } else {
-      if (w_once) kloop(no(), yes(), yes());
-      else kloop(no(), no(), yes());
+      if (w_once) kloop(no(), yes(), thin_c);
+      else kloop(no(), no(), thin_c);
     }
-  } else if (live) {
-    if (w_once) kloop(yes(), yes(), no());
-    else kloop(yes(), no(), no());
+  };
+  if constexpr (BM == 256 && C::TNS >= 3) {
+    if (EVENK && p.sorted[row0 + C::TR] >= p.P) run(yes());
+    else run(no());
   } else {
-    if (w_once) kloop(no(), yes(), no());
-    else kloop(no(), no(), no());
+    run(no());
   }
   if (!live) return;
 
