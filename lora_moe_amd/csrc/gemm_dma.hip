@@ -319,11 +319,12 @@ __global__ __launch_bounds__(C::NT, WAVES_PER_SIMD) void grouped_gemm_dma_kernel
   // 64 x 128 tile, the expand is short and the loop's extra work cost more:
   // GPT-OSS-like gate_up 240 -> 249 us), not for a K with a remainder at
   // 256 x 256 (the clamped copies need the registers), and only when the
-  // items fit in the stages; otherwise the batched expand runs after the
-  // loop (the Qwen3-MoE-like down GEMM, 12 stages for ~20 segments per
-  // wavefront: 183 us batched against 219 us with the leftover items after
-  // the loop one round trip each).
+  // items fit in the stages give or take a few; otherwise the batched expand
+  // runs after the loop (the Qwen3-MoE-like down GEMM, 12 stages for ~20
+  // segments per wavefront: 183 us batched against 219 us with the leftover
+  // items after the loop one round trip each).
   constexpr bool XPIPE = MI >= 2 && (EVENK || MI < 4);
+  constexpr int kLeftover = 4;
   ExpandItems<MI, NI> xi;
   xi.nitems = 0;
   xi.next = 0;
@@ -339,7 +340,10 @@ __global__ __launch_bounds__(C::NT, WAVES_PER_SIMD) void grouped_gemm_dma_kernel
       if (s < ntile) issue(s, nt_c, thin_c);
     if (LIVE && XPIPE) {
       expand_items_init(xi, p, e, row0 + wrow, 0);
-      if (xi.nitems > ntile - 1) xi.nitems = -1;  // does not fit: batched, after the loop
+      // up to kLeftover items beyond the stages run one by one after the loop;
+      // more do not fit: all batched, after the loop (Qwen3-MoE-like gate_up,
+      // 32 stages for ~32 items per wavefront: 247 -> 238 us)
+      if (xi.nitems > ntile - 1 + kLeftover) xi.nitems = -1;
       if (xi.nitems > 0) {
         expand_item_load(xi, p, e, row0 + wrow, 0, ncol);
         xpend = true;
