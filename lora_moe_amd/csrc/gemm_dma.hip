@@ -328,6 +328,7 @@ __global__ __launch_bounds__(C::NT, WAVES_PER_SIMD) void grouped_gemm_dma_kernel
   ExpandItems<MI, NI> xi;
   xi.nitems = 0;
   xi.next = 0;
+  xi.lrest = 64;
   bool xpend = false;  // an item is loaded and not yet multiplied
   auto kloop = [&](auto live_c, auto nt_c, auto thin_c) {
     constexpr bool LIVE = decltype(live_c)::value;
@@ -341,9 +342,10 @@ __global__ __launch_bounds__(C::NT, WAVES_PER_SIMD) void grouped_gemm_dma_kernel
     if (LIVE && XPIPE) {
       expand_items_init(xi, p, e, row0 + wrow, 0);
       // up to kLeftover items beyond the stages run one by one after the loop;
-      // more do not fit: all batched, after the loop (Qwen3-MoE-like gate_up,
-      // 32 stages for ~32 items per wavefront: 247 -> 238 us)
-      if (xi.nitems > ntile - 1 + kLeftover) xi.nitems = -1;
+      // past that, the whole segments that fit the stages run in the loop
+      // and the rest batched after it (Qwen3-MoE-like gate_up, 32 stages for
+      // ~32 items per wavefront: 247 -> 238 us)
+      if (xi.nitems > ntile - 1 + kLeftover) expand_items_cap(xi, p, 0, ntile - 1);
       if (xi.nitems > 0) {
         expand_item_load(xi, p, e, row0 + wrow, 0, ncol);
         xpend = true;
@@ -423,7 +425,7 @@ __global__ __launch_bounds__(C::NT, WAVES_PER_SIMD) void grouped_gemm_dma_kernel
     xpend = xi.next < xi.nitems;
     if (xpend) expand_item_load(xi, p, e, row0 + wrow, 0, ncol);
   }
-  const int lstart = (XPIPE && xi.nitems >= 0) ? 64 : 0;  // adapters the loop has not expanded
+  const int lstart = XPIPE ? xi.lrest : 0;  // adapters the loop has not expanded
   if (lstart < p.L) lora_expand<MI, NI, true, (MI <= 3 ? 8 : 4)>(acc, p, e, row0 + wrow, ncol, lstart);
 
   // epilogue: the products were formed as W x A^T, so element v of

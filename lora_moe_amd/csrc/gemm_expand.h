@@ -112,9 +112,11 @@ __device__ __forceinline__ void lora_expand(f32x16_t (&acc)[MI][NI], const GemmP
 }
 
 // The same expand as work items spread over a K loop, for adapters
-// [lbeg, lbeg + 64): item i is (rank slice i / nseg, segment i % nseg in
-// ascending adapter order) over the nseg segments that meet the wavefront's
-// rows.  A loaded item holds s*z of the lane's rows for the slice (bf16,
+// [lbeg, lbeg + 64): item i is (segment i / ns in ascending adapter order,
+// rank slice i % ns, ns = r / 16) over the nseg segments that meet the
+// wavefront's rows; when the items outnumber the K stages, the loop keeps
+// the first whole segments and leaves the rest to the batched expand
+// (expand_items_cap).  A loaded item holds s*z of the lane's rows for the slice (bf16,
 // from the shrink) and the segment's B rows at the lane's columns; its
 // masked MFMAs run a K stage after its loads, so their latency passes under
 // the main loop's work instead of stalling the epilogue (one workgroup per
@@ -124,6 +126,7 @@ template <int MI, int NI>
 struct ExpandItems {
   uint64_t hit;  // bit l: adapter lbeg + l has a segment meeting the rows
   int nseg, nitems, next;
+  int lrest;     // first adapter left to the batched expand (lbeg + 64: none)
   int st, cnt;   // segment of adapter lbeg + lane
   int l;         // adapter bit of the loaded item
   u32x4_t z[MI];
@@ -145,13 +148,29 @@ __device__ __forceinline__ void expand_items_init(ExpandItems<MI, NI>& it, const
   it.nitems = it.nseg * ((p.r + 15) >> 4);
   it.next = 0;
   it.l = 0;
+  it.lrest = lbeg + 64;
+}
+
+// Keep the first whole segments whose items fit in `cap` (items run segment
+// by segment, rank slices within a segment); the rest go to the batched
+// expand from the adapter of the first segment left out.
+template <int MI, int NI>
+__device__ __forceinline__ void expand_items_cap(ExpandItems<MI, NI>& it, const GemmParams& p, int lbeg, int cap) {
+  const int ns = (p.r + 15) >> 4;
+  if (it.nitems <= cap) return;
+  const int keep = cap / ns;  // whole segments
+  uint64_t m = it.hit;
+  for (int k = 0; k < keep; ++k) m &= m - 1;
+  it.lrest = lbeg + __builtin_ctzll(m);
+  it.nitems = keep * ns;
 }
 
 template <int MI, int NI>
 __device__ __forceinline__ void expand_item_load(ExpandItems<MI, NI>& it, const GemmParams& p, int e,
                                                  int wrow0, int lbeg, const int (&ncol)[NI]) {
   const int lane = threadIdx.x & 63, l32 = lane & 31, khalf = lane >> 5;
-  const int q = it.next / it.nseg, j = it.next - q * it.nseg;
+  const int ns = (p.r + 15) >> 4;
+  const int j = it.next / ns, q = it.next - j * ns;  // segment j, rank slice q
   uint64_t m = it.hit;
   for (int k = 0; k < j; ++k) m &= m - 1;
   it.l = __builtin_ctzll(m);
