@@ -53,16 +53,19 @@ def test_batch_sizes_1_to_64():
     for T, dev_ms, host_ms in times:
         log(f"T={T}: align + forward {dev_ms * 1e3:.1f} us on the device, {host_ms:.3f} ms to enqueue")
     # no call after the first pays a module load or a compile (those take
-    # milliseconds to seconds and would hit every new T): at most two later
-    # calls take over 2 ms to enqueue or over 5x the median device time (a
-    # profiler or the host can stall a call or two; a per-length compile would
-    # stall all 63)
+    # milliseconds to seconds and would hit every new T, all 63 of them): the
+    # median later call enqueues in well under a millisecond, and at most
+    # eight take over 2 ms to enqueue or over 5x the median device time (the
+    # host can stall a few calls; under a kernel-trace profiler five of 63
+    # stalled for ~5 ms while it flushed its buffers)
     later = times[1:]
     med_dev = float(np.median([d for _, d, _ in later]))
+    med_host = float(np.median([h for _, _, h in later]))
     slow_host = [(T, round(h, 2)) for T, _, h in later if h > 2.0]
     slow_dev = [(T, round(d, 3)) for T, d, _ in later if d > 5 * med_dev]
-    assert len(slow_host) <= 2, f"slow to enqueue: {slow_host}"
-    assert len(slow_dev) <= 2, f"slow on the device (median {med_dev:.3f} ms): {slow_dev}"
+    assert med_host < 1.0, f"median enqueue {med_host:.3f} ms"
+    assert len(slow_host) <= 8, f"slow to enqueue: {slow_host}"
+    assert len(slow_dev) <= 8, f"slow on the device (median {med_dev:.3f} ms): {slow_dev}"
 
 
 if __name__ == "__main__":  # for a kernel trace of this sequence alone
