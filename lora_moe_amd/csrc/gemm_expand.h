@@ -176,9 +176,16 @@ __device__ __forceinline__ void expand_item_load(ExpandItems<MI, NI>& it, const 
   it.l = __builtin_ctzll(m);
   const int qa = 16 * q + 8 * khalf;
   const bool qok = qa < p.r;
+  // z only for the row blocks the segment meets (the others skip their
+  // MFMAs): DeepSeek-like layer 8.20 -> 8.12 ms, down GEMM 2.77 -> 2.71
+  const int sst = __builtin_amdgcn_readlane(it.st, it.l);
+  const int send = sst + __builtin_amdgcn_readlane(it.cnt, it.l);
 #pragma unroll
-  for (int mi = 0; mi < MI; ++mi)
-    it.z[mi] = qok ? ld16(p.zb + (size_t)(wrow0 + 32 * mi + l32) * p.r + qa) : zero4();
+  for (int mi = 0; mi < MI; ++mi) {
+    const int sub0 = wrow0 + 32 * mi;
+    it.z[mi] = zero4();
+    if (qok && sub0 < send && sub0 + 32 > sst) it.z[mi] = ld16(p.zb + (size_t)(sub0 + l32) * p.r + qa);
+  }
   const uint16_t* Bl = p.B + ((size_t)(lbeg + it.l) * p.E + e) * p.N * p.r;
 #pragma unroll
   for (int ni = 0; ni < NI; ++ni) it.b[ni] = qok ? ld16(Bl + (size_t)ncol[ni] * p.r + qa) : zero4();
