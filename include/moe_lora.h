@@ -78,6 +78,14 @@ typedef struct moe_lora_shape {
                           /* tile-major; 2 = each row tile's column tiles on one */
                           /* XCD, row tiles interleaved over the 8 XCDs;         */
                           /* 0 = 1 for gate_up and 2 for down                    */
+  int32_t expand_mode;    /* LoRA expand of the LDS-tiled GEMMs (block_m >= 64): */
+                          /* 2 = as extra K stages through the LDS ring, one per */
+                          /* 64 ranks of each (expert, adapter) segment meeting  */
+                          /* a row tile, taken where r is a multiple of 64,      */
+                          /* L <= 64 and the GEMM's K a multiple of 64 (the      */
+                          /* register form runs elsewhere); 1 = masked MFMAs on  */
+                          /* the accumulators from z and B in registers;         */
+                          /* 0 = 2 where it is taken, else 1                     */
 } moe_lora_shape;
 
 /* Device pointers into a workspace (see moe_lora_workspace_view). */
@@ -135,6 +143,7 @@ typedef struct {
   int32_t block_m;                        /* value: 16, 32, 64, 128, 192 or 256 */
   int32_t shrink_splits, shrink_zblocks, down_splits, tile_order; /* value: as in    */
                                           /* moe_lora_shape (0 = the library's choice) */
+  int32_t expand_mode;                    /* likewise                                  */
 } moe_lora_tune_entry;
 
 /* block_m for `shape` chosen from a tuning table: the shape's own block_m
@@ -152,7 +161,7 @@ int moe_lora_tune_block_m(const moe_lora_shape* shape, const moe_lora_tune_entry
                           float max_dist);
 
 /* The whole configuration from a tuning table: *out = *shape with block_m and
- * the four knobs taken from the entry moe_lora_tune_block_m would pick (same
+ * the five knobs taken from the entry moe_lora_tune_block_m would pick (same
  * distance, limit and validity rules; the shape's own non-zero fields win
  * field by field).  With no entry in range *out = *shape.  Returns the
  * block_m in effect, or a negative status (invalid shape, null out).  Host

@@ -31,7 +31,7 @@ class MoeLoraError(RuntimeError):
         super().__init__(f"{func} failed: {moe_lora_status_str(code)} ({code})")
 
 
-KNOBS = ("shrink_splits", "shrink_zblocks", "down_splits", "tile_order")
+KNOBS = ("shrink_splits", "shrink_zblocks", "down_splits", "tile_order", "expand_mode")
 
 
 class moe_lora_shape(ctypes.Structure):
@@ -76,7 +76,7 @@ TUNE_MAX_DIST = 4.0
 def make_shape(T, H, I, E, topk, L, r, block_m=0, lora_scale=1.0, tuning=None,
                max_dist=TUNE_MAX_DIST, **knobs) -> moe_lora_shape:
     """The shape struct (knobs: shrink_splits, shrink_zblocks, down_splits,
-    tile_order; 0 = the library's choice).  With a tuning table
+    tile_order, expand_mode; 0 = the library's choice).  With a tuning table
     (load_tuning), every field left at 0 is taken from the table's nearest
     entry within max_dist (moe_lora_tune_apply)."""
     s = moe_lora_shape(int(T), int(H), int(I), int(E), int(topk), int(L), int(r), int(block_m),

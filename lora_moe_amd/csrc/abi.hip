@@ -37,6 +37,7 @@ static int check_shape(const moe_lora_shape* s) {
   if (zb < 0 || (zb > 1 && (s->r % zb || (s->r / zb) % 8))) return MOE_LORA_EINVAL;
   if (s->down_splits < 0 || s->down_splits > 8) return MOE_LORA_EINVAL;
   if (s->tile_order < 0 || s->tile_order > 2) return MOE_LORA_EINVAL;
+  if (s->expand_mode < 0 || s->expand_mode > 2) return MOE_LORA_EINVAL;
   return MOE_LORA_OK;
 }
 
@@ -98,6 +99,7 @@ int make_layout(const moe_lora_shape* s, Layout* L) {
   L->shrink_splits = s->shrink_splits;
   L->shrink_zblocks = s->shrink_zblocks;
   L->tile_order = s->tile_order;
+  L->expand_mode = s->expand_mode;
   L->dsplit = 1;
   if ((L->bm <= 32 || L->hsplit) && s->down_splits > 0) {
     // the streaming down GEMM splits K in 128-wide chunks
@@ -225,6 +227,7 @@ int moe_lora_tune_apply(const moe_lora_shape* shape, const moe_lora_tune_entry* 
     if (!s2.shrink_zblocks) s2.shrink_zblocks = t.shrink_zblocks;
     if (!s2.down_splits) s2.down_splits = t.down_splits;
     if (!s2.tile_order) s2.tile_order = t.tile_order;
+    if (!s2.expand_mode) s2.expand_mode = t.expand_mode;
     Layout L;
     if (make_layout(&s2, &L) == MOE_LORA_OK) *out = s2;  // else: the entry does not fit this shape
   }

@@ -31,10 +31,15 @@
 //     holds the tile transposed: each lane ends with runs of 4 adjacent output
 //     columns of one row, written with one 8-byte (h, bf16) or 16-byte (d,
 //     fp32) store;
-//   * epilogue: the expand (lora_expand) as masked MFMAs per (expert, adapter)
-//     segment with s*z rounded to bf16, then the SiLU gate (mode 0, gate
-//     and up columns in the same lane) or the top-k weight (mode 1); the rows'
-//     validity and weights are staged in LDS at the start.
+//   * the LoRA expand adds s*z*B^T on the same accumulators, in one of two
+//     forms: as extra K stages through the ring (XD: one 64-deep stage per
+//     64 ranks of each (expert, adapter) segment that meets the row tile,
+//     z rows of the segment on the A side, its B rows on the W side), or
+//     from registers as masked MFMAs per segment (gemm_expand.h: work items
+//     inside the K loop, the rest after it);
+//   * epilogue: the SiLU gate (mode 0, gate and up columns in the same lane)
+//     or the top-k weight (mode 1); the rows' validity and weights are staged
+//     in LDS at the start.
 // A wavefront whose rows are all padding skips its MFMAs and stores but still
 // copies its share of every stage.  256-row tiles with at most 64 real rows
 // run on a ring of thin stages (64 A rows + the W tile) that keeps two stages
@@ -102,7 +107,8 @@ struct DmaCfg {
 
 // EVENK: K is a multiple of the stage depth, so no copy needs clamping or
 // zeroing past K (and the chunk indices need not stay live in the loop).
-template <int MODE, class C, int WAVES_PER_SIMD, bool EVENK>
+// XD (EVENK only): the expand as extra K stages (r a multiple of 64, L <= 64).
+template <int MODE, class C, int WAVES_PER_SIMD, bool EVENK, bool XD>
 __global__ __launch_bounds__(C::NT, WAVES_PER_SIMD) void grouped_gemm_dma_kernel(GemmParams p) {
   constexpr int BM = C::BM, BN = C::BN, BK = C::BK, NS = C::NS, MI = C::MI, NI = C::NI;
   constexpr int NCA = C::NCA, NCW = C::NCW, AROWS = C::AROWS, WROWS = C::WROWS;
@@ -198,11 +204,64 @@ __global__ __launch_bounds__(C::NT, WAVES_PER_SIMD) void grouped_gemm_dma_kernel
   }
   const int ntile = (p.K + BK - 1) / BK;  // the last stage may be partial
   const bool partial = !EVENK && (p.K % BK) != 0;
+  // XD: after the K stages, r / 64 expand stages per (expert, adapter)
+  // segment that meets the tile's rows, in ascending adapter order.  A side:
+  // s*z of the segment's rows (bf16, written by the shrink); the tile's other
+  // rows get an offset past the end of zb and copy zeros.  W side: the
+  // segment's B rows at the tile's columns.  The stages' MFMAs are the K
+  // loop's own, so the expand costs a stage per segment and 64 ranks instead
+  // of per-wavefront loads of z and B (which every wavefront of a row half or
+  // column quarter repeats).  Lane l holds the segment of adapter l.
+  int xs_st = 0, xs_cnt = 0, nst = ntile;  // nst: stages of the loop
+  uint64_t xs_rem = 0;                     // segments whose stages are not issued yet
+  if constexpr (XD) {
+    const int S = p.L + 1;
+    if (lane < p.L) {
+      xs_st = p.segstart[e * S + lane];
+      xs_cnt = p.segcnt[e * S + lane];
+    }
+    xs_rem = __ballot(xs_cnt > 0 && xs_st < row0 + BM && xs_st + xs_cnt > row0);
+    nst = ntile + __builtin_popcountll(xs_rem) * (p.r >> 6);
+  }
+  int xs_l = 0, xs_s0 = 0, xs_n = 0;  // adapter, first row and rows of the segment being issued
+  const buf_rsrc_t z_rs = make_rsrc(XD ? (const void*)p.zb : (const void*)p.in, XD ? p.zb_bytes : p.in_bytes);
   auto issue = [&](int s, auto nt_c, auto thin_c) {
     constexpr bool NTL = decltype(nt_c)::value;
     constexpr bool THIN = decltype(thin_c)::value;
     char* A = THIN ? smem + (s % C::TNS) * C::TSTAGE : smem + (s % NS) * C::STAGE;
     char* B = A + (THIN ? C::TATILE : C::ATILE);
+    if (XD && s >= ntile) {  // an expand stage (issued in order, so the segments are taken in turn)
+      const int jr = (p.r >> 6) == 1 ? 0 : ((s - ntile) & 1);  // which 64 ranks (r = 128: two stages)
+      if (jr == 0) {
+        xs_l = __builtin_ctzll(xs_rem);
+        xs_rem &= xs_rem - 1;
+        xs_s0 = __builtin_amdgcn_readlane(xs_st, xs_l);
+        xs_n = __builtin_amdgcn_readlane(xs_cnt, xs_l);
+      }
+      const int rb = jr * 64;
+      auto ldZ = [&](int r, char* dst) {
+        const int ch = C::swz(r, lslot);
+        const int grow = row0 + r;
+        const uint32_t off =
+            (uint32_t)(grow - xs_s0) < (uint32_t)xs_n ? (uint32_t)(grow * p.r + rb + ch * 8) * 2u : kBufNone;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(z_rs, (lds_char*)dst, 16, (int)off, 0, 0, 0);
+      };
+      if (THIN) {
+        ldZ(wave * RPC + lrow, A + wave * RPC * PROW);
+      } else {
+#pragma unroll
+        for (int i = 0; i < NCA; ++i) ldZ(wave * AROWS + i * RPC + lrow, A + (wave * AROWS + i * RPC) * PROW);
+      }
+      const uint16_t* Bs = p.B + ((size_t)xs_l * p.E + e) * p.N * p.r + rb;
+#pragma unroll
+      for (int i = 0; i < NCW; ++i) {
+        const int r = wave * WROWS + i * RPC + lrow;
+        const int ch = C::swz(r, lslot);
+        __builtin_amdgcn_global_load_lds((const void*)(Bs + (size_t)tile_col(r) * p.r + ch * 8),
+                                         (lds_char*)(B + (wave * WROWS + i * RPC) * PROW), 16, 0, 0);
+      }
+      return;  // as many copies as a K stage (the waits count them)
+    }
     const int k0 = s * BK;
     auto ldA = [&](int i) {
       int koff = k0;
@@ -323,7 +382,7 @@ __global__ __launch_bounds__(C::NT, WAVES_PER_SIMD) void grouped_gemm_dma_kernel
   // runs after the loop (the Qwen3-MoE-like down GEMM, 12 stages for ~20
   // segments per wavefront: 183 us batched against 219 us with the leftover
   // items after the loop one round trip each).
-  constexpr bool XPIPE = MI >= 2 && (EVENK || MI < 4);
+  constexpr bool XPIPE = !XD && MI >= 2 && (EVENK || MI < 4);
   constexpr int kLeftover = 4;
   ExpandItems<MI, NI> xi;
   xi.nitems = 0;
@@ -338,7 +397,7 @@ __global__ __launch_bounds__(C::NT, WAVES_PER_SIMD) void grouped_gemm_dma_kernel
     // prologue: every ring slot gets a stage; wait for stage 0
 #pragma unroll
     for (int s = 0; s < RNS; ++s)
-      if (s < ntile) issue(s, nt_c, thin_c);
+      if (s < nst) issue(s, nt_c, thin_c);
     if (LIVE && XPIPE) {
       expand_items_init(xi, p, e, row0 + wrow, 0);
       // up to kLeftover items beyond the stages run one by one after the loop;
@@ -360,21 +419,21 @@ __global__ __launch_bounds__(C::NT, WAVES_PER_SIMD) void grouped_gemm_dma_kernel
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     stage_barrier();
     if (LIVE) frag(0, 0, 0, thin_c);
-    for (int q = 0; q + 1 < ntile; ++q) {
+    for (int q = 0; q + 1 < nst; ++q) {
 #pragma unroll
       for (int kk = 0; kk + 1 < KK; ++kk)
         if (LIVE) step(kk & 1, true, q, kk + 1, thin_c);
       // own copies of stage q + 1 have landed (later stages may still fly);
       // the wait stays behind this stage's MFMAs
       __builtin_amdgcn_sched_barrier(0);
-      if (q + RNS - 1 < ntile)
+      if (q + RNS - 1 < nst)
         __builtin_amdgcn_s_waitcnt(wait_vm(VMA));
       else
         __builtin_amdgcn_s_waitcnt(wait_vm(0));
       if (partial && q + 1 == ntile - 1) zero_tail(q + 1);
       __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // fragment reads of stage q and zero writes done
       stage_barrier();
-      if (q + RNS < ntile) issue(q + RNS, nt_c, thin_c);  // into the slot stage q just released
+      if (q + RNS < nst) issue(q + RNS, nt_c, thin_c);  // into the slot stage q just released
       if (LIVE && xpend) {
         expand_item_mfma(xi, acc, row0 + wrow);
         xpend = xi.next < xi.nitems;
@@ -386,7 +445,7 @@ __global__ __launch_bounds__(C::NT, WAVES_PER_SIMD) void grouped_gemm_dma_kernel
     }
     if (LIVE) {  // the last stage
 #pragma unroll
-      for (int kk = 0; kk + 1 < KK; ++kk) step(kk & 1, true, ntile - 1, kk + 1, thin_c);
+      for (int kk = 0; kk + 1 < KK; ++kk) step(kk & 1, true, nst - 1, kk + 1, thin_c);
       step((KK - 1) & 1, false, 0, 0, thin_c);
     }
   };
@@ -425,7 +484,7 @@ __global__ __launch_bounds__(C::NT, WAVES_PER_SIMD) void grouped_gemm_dma_kernel
     xpend = xi.next < xi.nitems;
     if (xpend) expand_item_load(xi, p, e, row0 + wrow, 0, ncol);
   }
-  const int lstart = XPIPE ? xi.lrest : 0;  // adapters the loop has not expanded
+  const int lstart = XD ? p.L : XPIPE ? xi.lrest : 0;  // adapters the loop has not expanded
   if (lstart < p.L) lora_expand<MI, NI, true, (MI <= 3 ? 8 : 4)>(acc, p, e, row0 + wrow, ncol, lstart);
 
   // epilogue: the products were formed as W x A^T, so element v of
@@ -484,27 +543,34 @@ __global__ __launch_bounds__(C::NT, WAVES_PER_SIMD) void grouped_gemm_dma_kernel
 
 template <class C, int WAVES_PER_SIMD>
 int launch_dma(const GemmParams& gp_in, int mode, int64_t cap_rows, hipStream_t st) {
-  static std::atomic<uint64_t> attr_done[4];  // per kernel: mode x EVENK
+  static std::atomic<uint64_t> attr_done[6];  // per kernel: mode x (K with a remainder, even K, expand stages)
   GemmParams gp = gp_in;
   gp.ncol = mode == 0 ? (gp.I + C::BN / 2 - 1) / (C::BN / 2) : (gp.N + C::BN - 1) / C::BN;
   gp.nrowt = (int)((cap_rows + C::BM - 1) / C::BM);
   const unsigned grid = (unsigned)gp.ncol * (unsigned)(gp.order == 2 ? (gp.nrowt + 7) / 8 * 8 : gp.nrowt);
   const bool even = gp.K % C::BK == 0;
-  const void* fn =
-      mode == 0 ? (even ? reinterpret_cast<const void*>(&grouped_gemm_dma_kernel<0, C, WAVES_PER_SIMD, true>)
-                        : reinterpret_cast<const void*>(&grouped_gemm_dma_kernel<0, C, WAVES_PER_SIMD, false>))
-                : (even ? reinterpret_cast<const void*>(&grouped_gemm_dma_kernel<1, C, WAVES_PER_SIMD, true>)
-                        : reinterpret_cast<const void*>(&grouped_gemm_dma_kernel<1, C, WAVES_PER_SIMD, false>));
+  const int kind = !even ? 0 : gp.xstages ? 2 : 1;
+  const void* fn;
+  if (mode == 0)
+    fn = kind == 2 ? reinterpret_cast<const void*>(&grouped_gemm_dma_kernel<0, C, WAVES_PER_SIMD, true, true>)
+         : kind == 1 ? reinterpret_cast<const void*>(&grouped_gemm_dma_kernel<0, C, WAVES_PER_SIMD, true, false>)
+                     : reinterpret_cast<const void*>(&grouped_gemm_dma_kernel<0, C, WAVES_PER_SIMD, false, false>);
+  else
+    fn = kind == 2 ? reinterpret_cast<const void*>(&grouped_gemm_dma_kernel<1, C, WAVES_PER_SIMD, true, true>)
+         : kind == 1 ? reinterpret_cast<const void*>(&grouped_gemm_dma_kernel<1, C, WAVES_PER_SIMD, true, false>)
+                     : reinterpret_cast<const void*>(&grouped_gemm_dma_kernel<1, C, WAVES_PER_SIMD, false, false>);
   if (C::LDS > 64 * 1024) {  // more than the default 64 KB of dynamic LDS
-    const int rc = ensure_dynamic_lds(fn, C::LDS, attr_done[2 * mode + (even ? 1 : 0)]);
+    const int rc = ensure_dynamic_lds(fn, C::LDS, attr_done[3 * mode + kind]);
     if (rc) return rc;
   }
   if (mode == 0) {
-    if (even) grouped_gemm_dma_kernel<0, C, WAVES_PER_SIMD, true><<<grid, C::NT, C::LDS, st>>>(gp);
-    else grouped_gemm_dma_kernel<0, C, WAVES_PER_SIMD, false><<<grid, C::NT, C::LDS, st>>>(gp);
+    if (kind == 2) grouped_gemm_dma_kernel<0, C, WAVES_PER_SIMD, true, true><<<grid, C::NT, C::LDS, st>>>(gp);
+    else if (kind == 1) grouped_gemm_dma_kernel<0, C, WAVES_PER_SIMD, true, false><<<grid, C::NT, C::LDS, st>>>(gp);
+    else grouped_gemm_dma_kernel<0, C, WAVES_PER_SIMD, false, false><<<grid, C::NT, C::LDS, st>>>(gp);
   } else {
-    if (even) grouped_gemm_dma_kernel<1, C, WAVES_PER_SIMD, true><<<grid, C::NT, C::LDS, st>>>(gp);
-    else grouped_gemm_dma_kernel<1, C, WAVES_PER_SIMD, false><<<grid, C::NT, C::LDS, st>>>(gp);
+    if (kind == 2) grouped_gemm_dma_kernel<1, C, WAVES_PER_SIMD, true, true><<<grid, C::NT, C::LDS, st>>>(gp);
+    else if (kind == 1) grouped_gemm_dma_kernel<1, C, WAVES_PER_SIMD, true, false><<<grid, C::NT, C::LDS, st>>>(gp);
+    else grouped_gemm_dma_kernel<1, C, WAVES_PER_SIMD, false, false><<<grid, C::NT, C::LDS, st>>>(gp);
   }
   return MOE_LORA_OK;
 }

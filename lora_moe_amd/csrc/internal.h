@@ -38,6 +38,7 @@ struct Layout {
   int hsplit;  // h also stored as its bf16 remainder lo (I >= kHsplitMinI)
   int shrink_splits, shrink_zblocks;  // requested by the shape (0: chosen by plan_shrink)
   int tile_order;                     // requested order of the tiled GEMMs (0: per mode)
+  int expand_mode;                    // requested form of the tiled GEMMs' expand (0: chosen)
   size_t off_hdr, off_sorted, off_eoff, off_segstart, off_segcnt, off_bexp, off_pos;
   size_t off_chunk, off_chunkerr, off_rank, off_tiles, off_zgu, off_zd, off_zbgu, off_zbd, off_h, off_hlo,
       off_d, total;
@@ -123,6 +124,8 @@ struct GemmParams {
   int order;        // tiled family: 1 row tile-major, 2 row tiles interleaved over XCDs
   int64_t d_slab;   // elements between the d_out slabs of consecutive splits
   float s;
+  int xstages;        // tiled family: the expand as extra K stages through the LDS ring
+  uint32_t zb_bytes;  // size of zb in bytes (below 2^31 whenever xstages is set)
 };
 
 // ------------------------------------------------------------------ stage timing

@@ -42,8 +42,10 @@ def _sparse_pm1(rng, shape, per_row):
 
 # shapes of the bit-exact test: K multiple of 64 and rank 16; then K with a
 # remainder (1000 = 15*64 + 40, 520 = 8*64 + 8) and a rank that is not a
-# multiple of 16 (24), which exercise the masked K tails and rank columns
-SHAPES = {"even": dict(H=1024, I=512, r=16), "ragged": dict(H=1000, I=520, r=24)}
+# multiple of 16 (24), which exercise the masked K tails and rank columns;
+# rank 64, where the tiled GEMMs can run the expand as extra K stages
+SHAPES = {"even": dict(H=1024, I=512, r=16), "ragged": dict(H=1000, I=520, r=24),
+          "rank64": dict(H=1024, I=512, r=64)}
 
 
 def make(seed: int = 5, shape: str = "even") -> synth.Inputs:

@@ -19,8 +19,8 @@ def log(msg):
     sys.stdout.flush()
 
 
-def shape_for(wl, block_m=0):
-    return lm.make_shape(wl.T, wl.H, wl.I, wl.E, wl.topk, wl.L, wl.r, block_m, wl.scale)
+def shape_for(wl, block_m=0, **knobs):
+    return lm.make_shape(wl.T, wl.H, wl.I, wl.E, wl.topk, wl.L, wl.r, block_m, wl.scale, **knobs)
 
 
 def check_shapes(dev, wl):
@@ -31,11 +31,11 @@ def check_shapes(dev, wl):
         "B_down")})
 
 
-def run_gpu(dev, wl, block_m=0, lora_ids=None, workspace=None):
+def run_gpu(dev, wl, block_m=0, lora_ids=None, workspace=None, knobs=None):
     """align + forward through the C ABI; returns (y as fp64 numpy, shape, workspace)."""
     import torch
     check_shapes(dev, wl)
-    shape = shape_for(wl, block_m)
+    shape = shape_for(wl, block_m, **(knobs or {}))
     ws = workspace if workspace is not None else lm.alloc_workspace(shape)
     lids = dev["lora_ids"] if lora_ids is None else lora_ids
     y = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda")

@@ -277,9 +277,9 @@ def test_kernel_knob_validation(lib):
     down-GEMM K split shows in the workspace view (streaming family only)."""
     base = dict(T=40, H=256, I=512, E=4, topk=2, L=2, r=32)
     ok = [dict(shrink_splits=64), dict(shrink_zblocks=4), dict(shrink_zblocks=2), dict(down_splits=8),
-          dict(tile_order=2)]
+          dict(tile_order=2), dict(expand_mode=1), dict(expand_mode=2)]
     bad = [dict(shrink_splits=65), dict(shrink_splits=-1), dict(shrink_zblocks=3), dict(shrink_zblocks=8),
-           dict(down_splits=9), dict(tile_order=3)]
+           dict(down_splits=9), dict(tile_order=3), dict(expand_mode=3), dict(expand_mode=-1)]
     for k in ok:
         assert lm.moe_lora_workspace_bytes(lm.make_shape(**base, **k)) > 0, k
     for k in bad:
@@ -298,9 +298,10 @@ def test_tune_apply_fills_knobs(lib):
     """moe_lora_tune_apply copies block_m and the knobs of the nearest entry
     into the fields the shape leaves at 0."""
     decode = lm.make_shape(16, 4096, 11008, 8, 2, 8, 32)
-    table = (lm.moe_lora_tune_entry * 1)(lm.moe_lora_tune_entry(4, 4096, 11008, 8, 32, 8, 16, 4, 2, 3, 0))
+    table = (lm.moe_lora_tune_entry * 1)(lm.moe_lora_tune_entry(4, 4096, 11008, 8, 32, 8, 16, 4, 2, 3, 0, 1))
     out = lm.moe_lora_tune_apply(decode, (table, 1))
-    assert (out.block_m, out.shrink_splits, out.shrink_zblocks, out.down_splits, out.tile_order) == (16, 4, 2, 3, 0)
+    assert (out.block_m, out.shrink_splits, out.shrink_zblocks, out.down_splits, out.tile_order,
+            out.expand_mode) == (16, 4, 2, 3, 0, 1)
     own = lm.make_shape(16, 4096, 11008, 8, 2, 8, 32, shrink_splits=7)
     assert lm.moe_lora_tune_apply(own, (table, 1)).shrink_splits == 7
     assert lm.make_shape(16, 4096, 11008, 8, 2, 8, 32, tuning=(table, 1)).down_splits == 3

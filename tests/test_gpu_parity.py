@@ -86,21 +86,21 @@ def test_align_deterministic():
 
 # ------------------------------------------------------------------ layer, small shapes
 
-def full_check(inp, block_m=0, what="", scale=None, errors=0):
+def full_check(inp, block_m=0, what="", scale=None, errors=0, knobs=None):
     import lora_moe_amd as lm
     if scale is not None:
         inp = synth.Inputs(replace(inp.wl, scale=scale), **{k: v for k, v in inp.arrays().items()})
     wl = inp.wl
-    log(f"layer {what}: T={wl.T} H={wl.H} I={wl.I} E={wl.E} k={wl.topk} L={wl.L} r={wl.r} bm={block_m}")
+    log(f"layer {what}: T={wl.T} H={wl.H} I={wl.I} E={wl.E} k={wl.topk} L={wl.L} r={wl.r} bm={block_m} {knobs or ''}")
     dev = to_device(inp)
-    y, shape, ws = run_gpu(dev, wl, block_m)
+    y, shape, ws = run_gpu(dev, wl, block_m, knobs=knobs)
     # the invalid ids the align met
     assert lm.moe_lora_device_errors(shape, ws) == errors, what
     ref = oracle_tokens(inp, None)
     compare(y, ref, what)
     if (inp.lora_ids >= 0).any():
         none = torch.full_like(dev["lora_ids"], -1)
-        y0, _, _ = run_gpu(dev, wl, block_m, lora_ids=none, workspace=ws)
+        y0, _, _ = run_gpu(dev, wl, block_m, lora_ids=none, workspace=ws, knobs=knobs)
         ref0 = oracle_tokens(inp, None, lora_ids=np.full_like(inp.lora_ids, -1))
         compare(y0, ref0, what + " (no adapters)")
         compare_delta(y, y0, ref, ref0, what)
@@ -202,6 +202,64 @@ def test_thin_tiles(H, I):
     inp.topk_ids[:, 0] = ids
     inp.topk_weights[:] = 1.0
     full_check(inp, 256, f"thin tiles H={H} I={I}")
+
+
+def _expand_case(case):
+    """Workloads for the two forms of the tiled GEMMs' expand: (inputs, block_m)."""
+    if case == "thin":  # experts of 1 .. 513 rows at block_m 256, rank 64
+        counts = [1, 30, 64, 65, 200, 256, 300, 513]
+        wl = synth.Workload("expand-thin", T=sum(counts), H=256, I=256, E=8, topk=1, L=4, r=64,
+                            lora_mode="uniform_with_none", seed=7)
+        inp = synth.make_inputs(wl)
+        ids = np.repeat(np.arange(len(counts), dtype=np.int32), counts)
+        np.random.default_rng(7).shuffle(ids)
+        inp.topk_ids[:, 0] = ids
+        inp.topk_weights[:] = 1.0
+        return inp, 256
+    if case == "r128":  # two 64-rank stages per segment
+        wl = synth.Workload("expand-r128", T=300, H=256, I=512, E=4, topk=2, L=5, r=128,
+                            lora_mode="uniform_with_none", seed=8)
+        return synth.make_inputs(wl), 192
+    if case in ("L64", "L65"):  # one lane per adapter: 64 is the last the stage form takes
+        wl = synth.Workload("expand-" + case, T=700, H=256, I=256, E=2, topk=1, L=int(case[1:]), r=64,
+                            lora_mode="uniform_with_none", seed=9)
+        return synth.make_inputs(wl), 256
+    # gate_up K = 264 has a remainder (register expand), down K = 256 does not
+    wl = synth.Workload("expand-uneven", T=200, H=264, I=256, E=4, topk=2, L=3, r=64,
+                        lora_mode="uniform_with_none", seed=10)
+    return synth.make_inputs(wl), 128
+
+
+@pytest.mark.parametrize("mode", [1, 2])
+@pytest.mark.parametrize("case", ["thin", "r128", "L64", "L65", "uneven"])
+def test_expand_forms(case, mode):
+    """The tiled GEMMs' expand as extra K stages through the LDS ring
+    (expand_mode 2, taken where r is a multiple of 64, L <= 64 and K a
+    multiple of 64) and from registers (expand_mode 1) both match the oracle:
+    thin row tiles, 128 ranks (two stages per segment), 64 adapters with a
+    segment each in a tile (64 expand stages behind 4 K stages) and 65 (the
+    register form runs), and a gate_up K with a remainder beside a down K
+    without one."""
+    inp, bm = _expand_case(case)
+    full_check(inp, bm, f"expand {case}", knobs=dict(expand_mode=mode))
+
+
+@pytest.mark.parametrize("mode", [1, 2])
+@pytest.mark.parametrize("bm", [64, 128, 192, 256])
+def test_expand_forms_exact(bm, mode):
+    """Both expand forms at rank 64 give the exact small-integer layer bit for
+    bit (at block_m 256 the tiny routing's tiles run on the thin ring)."""
+    import lora_moe_amd as lm
+    import exact_inputs
+    inp = exact_inputs.make(shape="rank64")
+    wl = inp.wl
+    log(f"exact integers rank 64, bm={bm} expand_mode={mode}")
+    dev = to_device(inp)
+    y, shape, ws = run_gpu(dev, wl, bm, knobs=dict(expand_mode=mode))
+    assert lm.moe_lora_device_errors(shape, ws) == 0
+    want = exact_inputs.exact(oracle_tokens(inp, None))
+    bad = np.argwhere(y != want)
+    assert bad.size == 0, f"{len(bad)} outputs differ, first {bad[:3].tolist()}"
 
 
 @pytest.mark.parametrize("T,E,L", [(200, 4, 100), (600, 64, 200)])
