@@ -79,13 +79,14 @@ typedef struct moe_lora_shape {
                           /* XCD, row tiles interleaved over the 8 XCDs;         */
                           /* 0 = 1 for gate_up and 2 for down                    */
   int32_t expand_mode;    /* LoRA expand of the LDS-tiled GEMMs (block_m >= 64): */
-                          /* 2 = as extra K stages through the LDS ring, one per */
-                          /* 64 ranks of each (expert, adapter) segment meeting  */
-                          /* a row tile, taken where r is a multiple of 64,      */
-                          /* L <= 64 and the GEMM's K a multiple of 64 (the      */
-                          /* register form runs elsewhere); 1 = masked MFMAs on  */
-                          /* the accumulators from z and B in registers;         */
-                          /* 0 = 2 where it is taken, else 1                     */
+                          /* 2 = as extra K stages through the LDS ring over the */
+                          /* (expert, adapter) segments meeting a row tile (64   */
+                          /* ranks of one segment per stage, or 8/(r/8) segments */
+                          /* side by side when r < 64), taken where L <= 64 and  */
+                          /* the GEMM's K is a multiple of 64 (the register form */
+                          /* runs elsewhere); 1 = masked MFMAs on the            */
+                          /* accumulators from z and B in registers; 0 = 2 where */
+                          /* r >= 32 and 2 is taken, else 1                      */
 } moe_lora_shape;
 
 /* Device pointers into a workspace (see moe_lora_workspace_view). */

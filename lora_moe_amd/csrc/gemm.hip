@@ -330,16 +330,20 @@ int launch_gemm(const Layout& L, int mode, const uint16_t* in, const int32_t* lo
   gp.order = L.tile_order ? L.tile_order : (mode == 0 ? 1 : 2);
   gp.d_slab = L.cap_rows * (int64_t)L.H;
   gp.s = L.s;
-  // the LDS-tiled GEMMs' expand as extra K stages (gemm_dma.hip) where a
-  // stage holds whole 64-rank pieces of a segment (r a multiple of 64), the
+  // the LDS-tiled GEMMs' expand as extra K stages (gemm_dma.hip) where the
   // adapters fit one lane each (L <= 64), K has no remainder and zb is
-  // addressable through a buffer resource; expand_mode 1 keeps the register
-  // expand.  DeepSeek-like layer (r = 64, 256 x 256 tiles): 8.18 -> 7.93 ms
-  // (two alternating runs on one box; gate_up 4.49 -> 4.35, down 2.75 ->
-  // 2.57 ms).
+  // addressable through a buffer resource; by default from rank 32 on (at
+  // most two segments share a stage), where it was measured faster (flushed
+  // medians, one box, register expand -> stages): DeepSeek-like layer (r =
+  // 64) 8.27 -> 8.04 ms at 256 x 256 tiles, 8.72 -> 8.54 at 192 x 256, 9.28
+  // -> 8.98 at 128 x 128; GPT-OSS-like (r = 32, 64 x 128) 0.398 -> 0.391 ms.
+  // At rank 16 four segments share a stage, and the Qwen3-MoE-like layer's
+  // ~30 segments per 192-row tile made it slower (0.582 -> 0.624 ms).
+  // expand_mode 1 keeps the register expand, 2 asks for the stages at any rank.
   const int64_t zb_bytes = L.cap_rows * (int64_t)L.r * 2;
   gp.zb_bytes = (uint32_t)std::min<int64_t>(zb_bytes, 0x7fffffff);
-  gp.xstages = L.expand_mode != 1 && L.r % 64 == 0 && L.L <= 64 && gp.K % 64 == 0 && zb_bytes < (1LL << 31);
+  const bool want_stages = L.expand_mode == 2 || (L.expand_mode == 0 && L.r >= 32);
+  gp.xstages = want_stages && L.L <= 64 && gp.K % 64 == 0 && zb_bytes < (1LL << 31);
   if (mode == 1 && L.hsplit) {
     // h as hi + lo: the streaming kernel, on 16-row tiles at block_m 16 and
     // 32-row tiles otherwise (block_m is a multiple of 32 then)

@@ -204,46 +204,80 @@ __global__ __launch_bounds__(C::NT, WAVES_PER_SIMD) void grouped_gemm_dma_kernel
   }
   const int ntile = (p.K + BK - 1) / BK;  // the last stage may be partial
   const bool partial = !EVENK && (p.K % BK) != 0;
-  // XD: after the K stages, r / 64 expand stages per (expert, adapter)
-  // segment that meets the tile's rows, in ascending adapter order.  A side:
-  // s*z of the segment's rows (bf16, written by the shrink); the tile's other
-  // rows get an offset past the end of zb and copy zeros.  W side: the
-  // segment's B rows at the tile's columns.  The stages' MFMAs are the K
-  // loop's own, so the expand costs a stage per segment and 64 ranks instead
-  // of per-wavefront loads of z and B (which every wavefront of a row half or
-  // column quarter repeats).  Lane l holds the segment of adapter l.
-  int xs_st = 0, xs_cnt = 0, nst = ntile;  // nst: stages of the loop
-  uint64_t xs_rem = 0;                     // segments whose stages are not issued yet
+  // XD: after the K stages come expand stages over the (expert, adapter)
+  // segments that meet the tile's rows, in ascending adapter order: a stage
+  // holds 64 ranks of one segment (r >= 64: r / 64 stages per segment,
+  // rounded up), or 8 / (r / 8) segments side by side (r < 64: each its r / 8
+  // chunks of the 8 in a row piece).  A side: s*z of the segment's rows (bf16,
+  // written by the shrink); the tile's other rows and unused chunks get an
+  // offset past the end of zb and copy zeros.  W side: the segment's B rows at
+  // the tile's columns.  The stages' MFMAs are the K loop's own, so the expand
+  // costs stages instead of per-wavefront loads of z and B (which every
+  // wavefront of a row half or column quarter repeats).  Lane g holds the
+  // g-th segment's adapter, first row and row count.
+  int xg_l = 0, xg_st = 0, xg_n = 0, nseg = 0, nst = ntile;  // nst: stages of the loop
   if constexpr (XD) {
     const int S = p.L + 1;
+    int st = 0, cnt = 0;  // segment of adapter `lane`
     if (lane < p.L) {
-      xs_st = p.segstart[e * S + lane];
-      xs_cnt = p.segcnt[e * S + lane];
+      st = p.segstart[e * S + lane];
+      cnt = p.segcnt[e * S + lane];
     }
-    xs_rem = __ballot(xs_cnt > 0 && xs_st < row0 + BM && xs_st + xs_cnt > row0);
-    nst = ntile + __builtin_popcountll(xs_rem) * (p.r >> 6);
+    uint64_t hit = __ballot(cnt > 0 && st < row0 + BM && st + cnt > row0);
+    nseg = __builtin_popcountll(hit);
+    for (int g = 0; hit; ++g) {
+      const int l = __builtin_ctzll(hit);
+      hit &= hit - 1;
+      if (lane == g) xg_l = l;
+    }
+    xg_st = __shfl(st, xg_l, 64);
+    xg_n = __shfl(cnt, xg_l, 64);
+    const int cps = p.r >> 3;  // 16-byte chunks of a segment's z row
+    nst = ntile + (cps >= 8 ? nseg * ((cps + 7) >> 3) : (nseg + 8 / cps - 1) / (8 / cps));
   }
-  int xs_l = 0, xs_s0 = 0, xs_n = 0;  // adapter, first row and rows of the segment being issued
   const buf_rsrc_t z_rs = make_rsrc(XD ? (const void*)p.zb : (const void*)p.in, XD ? p.zb_bytes : p.in_bytes);
-  auto issue = [&](int s, auto nt_c, auto thin_c) {
+  auto issue = [&](int s, auto nt_c, auto thin_c) __attribute__((always_inline)) {
     constexpr bool NTL = decltype(nt_c)::value;
     constexpr bool THIN = decltype(thin_c)::value;
     char* A = THIN ? smem + (s % C::TNS) * C::TSTAGE : smem + (s % NS) * C::STAGE;
     char* B = A + (THIN ? C::TATILE : C::ATILE);
-    if (XD && s >= ntile) {  // an expand stage (issued in order, so the segments are taken in turn)
-      const int jr = (p.r >> 6) == 1 ? 0 : ((s - ntile) & 1);  // which 64 ranks (r = 128: two stages)
-      if (jr == 0) {
-        xs_l = __builtin_ctzll(xs_rem);
-        xs_rem &= xs_rem - 1;
-        xs_s0 = __builtin_amdgcn_readlane(xs_st, xs_l);
-        xs_n = __builtin_amdgcn_readlane(xs_cnt, xs_l);
-      }
-      const int rb = jr * 64;
+    if (XD && s >= ntile) {  // an expand stage
+      const int j = s - ntile, cps = p.r >> 3;
+      // r >= 64: ranks [64 q, 64 q + 64) of segment g (q = 0, or 1 for r = 72..128)
+      const int g1 = cps > 8 ? j >> 1 : j;
+      const int rc0 = cps > 8 ? (j & 1) * 8 : 0;
+      const int l1 = __builtin_amdgcn_readlane(xg_l, g1), a1 = __builtin_amdgcn_readlane(xg_st, g1),
+                n1 = __builtin_amdgcn_readlane(xg_n, g1);
+      const int per = cps >= 8 ? 1 : 8 / cps, g0 = j * per;  // r < 64: segments g0 .. g0 + per - 1
+      // segment (adapter, first row, rows; 0 rows: none) and rank chunk of
+      // logical chunk ch of the stage
+      auto chunk = [&](int ch, int& l, int& a, int& n, int& rc) {
+        if (cps >= 8) {
+          rc = rc0 + ch;
+          l = l1;
+          a = a1;
+          n = rc < cps ? n1 : 0;
+          if (rc >= cps) rc = 0;
+          return;
+        }
+        int u = 0;
+#pragma unroll
+        for (int v = 1; v < 8; ++v) u += ch >= v * cps;
+        rc = ch - u * cps;
+        const bool ok = u < per && g0 + u < nseg;
+        const int g = ok ? g0 + u : g0;  // a chunk without ranks reads the stage's first segment's B
+        // the exchanges run in every lane (a lane that skips one does not
+        // supply its value to the others)
+        l = __shfl(xg_l, g, 64);
+        a = __shfl(xg_st, g, 64);
+        const int ng = __shfl(xg_n, g, 64);
+        n = ok ? ng : 0;
+      };
       auto ldZ = [&](int r, char* dst) {
-        const int ch = C::swz(r, lslot);
+        int l, a, n, rc;
+        chunk(C::swz(r, lslot), l, a, n, rc);
         const int grow = row0 + r;
-        const uint32_t off =
-            (uint32_t)(grow - xs_s0) < (uint32_t)xs_n ? (uint32_t)(grow * p.r + rb + ch * 8) * 2u : kBufNone;
+        const uint32_t off = (uint32_t)(grow - a) < (uint32_t)n ? (uint32_t)(grow * p.r + rc * 8) * 2u : kBufNone;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(z_rs, (lds_char*)dst, 16, (int)off, 0, 0, 0);
       };
       if (THIN) {
@@ -252,12 +286,13 @@ __global__ __launch_bounds__(C::NT, WAVES_PER_SIMD) void grouped_gemm_dma_kernel
 #pragma unroll
         for (int i = 0; i < NCA; ++i) ldZ(wave * AROWS + i * RPC + lrow, A + (wave * AROWS + i * RPC) * PROW);
       }
-      const uint16_t* Bs = p.B + ((size_t)xs_l * p.E + e) * p.N * p.r + rb;
 #pragma unroll
       for (int i = 0; i < NCW; ++i) {
         const int r = wave * WROWS + i * RPC + lrow;
-        const int ch = C::swz(r, lslot);
-        __builtin_amdgcn_global_load_lds((const void*)(Bs + (size_t)tile_col(r) * p.r + ch * 8),
+        int l, a, n, rc;
+        chunk(C::swz(r, lslot), l, a, n, rc);  // a chunk without ranks: its z side is zero, any finite B will do
+        const uint16_t* Bs = p.B + ((size_t)l * p.E + e) * p.N * p.r;
+        __builtin_amdgcn_global_load_lds((const void*)(Bs + (size_t)tile_col(r) * p.r + rc * 8),
                                          (lds_char*)(B + (wave * WROWS + i * RPC) * PROW), 16, 0, 0);
       }
       return;  // as many copies as a K stage (the waits count them)

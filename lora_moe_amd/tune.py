@@ -67,7 +67,7 @@ def knob_candidates(wl, bm: int) -> dict:
         K["down_splits"] = [1, 2, 4, 8]
     if bm >= 64:  # the LDS-tiled GEMMs run
         K["tile_order"] = [1, 2]
-        if wl.r % 64 == 0 and wl.L <= 64:  # both forms of their expand exist
+        if wl.L <= 64:  # both forms of their expand can run
             K["expand_mode"] = [1, 2]
     return K
 

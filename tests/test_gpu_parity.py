@@ -224,6 +224,10 @@ def _expand_case(case):
         wl = synth.Workload("expand-" + case, T=700, H=256, I=256, E=2, topk=1, L=int(case[1:]), r=64,
                             lora_mode="uniform_with_none", seed=9)
         return synth.make_inputs(wl), 256
+    if case.startswith("rank"):  # ranks below 64 share a stage (8 / (r / 8) segments), 72 spills into a second
+        wl = synth.Workload("expand-" + case, T=400, H=256, I=256, E=3, topk=2, L=9, r=int(case[4:]),
+                            lora_mode="uniform_with_none", seed=11)
+        return synth.make_inputs(wl), 128
     # gate_up K = 264 has a remainder (register expand), down K = 256 does not
     wl = synth.Workload("expand-uneven", T=200, H=264, I=256, E=4, topk=2, L=3, r=64,
                         lora_mode="uniform_with_none", seed=10)
@@ -231,15 +235,17 @@ def _expand_case(case):
 
 
 @pytest.mark.parametrize("mode", [1, 2])
-@pytest.mark.parametrize("case", ["thin", "r128", "L64", "L65", "uneven"])
+@pytest.mark.parametrize("case", ["thin", "r128", "L64", "L65", "uneven", "rank8", "rank16", "rank24",
+                                  "rank40", "rank72"])
 def test_expand_forms(case, mode):
     """The tiled GEMMs' expand as extra K stages through the LDS ring
-    (expand_mode 2, taken where r is a multiple of 64, L <= 64 and K a
-    multiple of 64) and from registers (expand_mode 1) both match the oracle:
-    thin row tiles, 128 ranks (two stages per segment), 64 adapters with a
-    segment each in a tile (64 expand stages behind 4 K stages) and 65 (the
-    register form runs), and a gate_up K with a remainder beside a down K
-    without one."""
+    (expand_mode 2, taken where L <= 64 and K is a multiple of 64) and from
+    registers (expand_mode 1) both match the oracle: thin row tiles, 128 ranks
+    (two stages per segment), 64 adapters with a segment each in a tile (64
+    expand stages behind 4 K stages) and 65 (the register form runs), a
+    gate_up K with a remainder beside a down K without one, and ranks that
+    share a stage between segments (8, 16, 24 with two chunks unused, 40 with
+    three) or leave a second stage nearly empty (72)."""
     inp, bm = _expand_case(case)
     full_check(inp, bm, f"expand {case}", knobs=dict(expand_mode=mode))
 
