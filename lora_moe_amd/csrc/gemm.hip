@@ -351,6 +351,15 @@ int launch_gemm(const Layout& L, int mode, const uint16_t* in, const int32_t* lo
     else launch_rf<1, 1, true>(gp, L.cap_rows, st);
     return hipGetLastError() == hipSuccess ? MOE_LORA_OK : MOE_LORA_EHIP;
   }
+  // the LDS-tiled GEMMs address an expert's weights (and the A rows) through
+  // buffer resources, whose offsets stay below 2 GB; an expert whose W is
+  // larger runs on the streaming kernel (32-row tiles, block_m >= 64 is a
+  // multiple of 32)
+  if (L.bm >= 64 && !tiled_w_fits(L, mode)) {
+    if (mode == 0) launch_rf<0, 2>(gp, L.cap_rows, st);
+    else launch_rf<1, 2>(gp, L.cap_rows, st);
+    return hipGetLastError() == hipSuccess ? MOE_LORA_OK : MOE_LORA_EHIP;
+  }
   if (L.bm == 192) {
     const int rc = launch_gemm_dma192(gp, mode, L.cap_rows, st);
     if (rc) return rc;

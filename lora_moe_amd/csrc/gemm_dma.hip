@@ -18,9 +18,10 @@
 //     multiplies, without holding tiles in registers.  A stage is released by
 //     a single workgroup barrier per K step, placed after the last fragment
 //     read of the stage and before the last MFMAs that use it;
-//   * A rows come through a buffer resource: padding rows (past an expert's
-//     real pairs) get an offset past the end and copy zeros without touching
-//     memory;
+//   * A and W rows come through buffer resources (a 32-bit offset per lane;
+//     the host keeps an expert's W below 2 GB here): padding rows (past an
+//     expert's real pairs) get an offset past the end and copy zeros without
+//     touching memory;
 //   * a row tile that is its expert's only one reads the weight tile
 //     non-temporally (it is not reused by another row tile);
 //   * 16-byte chunks of each LDS row are XOR-swizzled so that fragment reads
@@ -59,6 +60,13 @@ typedef __attribute__((address_space(3))) char lds_char;
 // s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
 // 6:4, lgkmcnt 11:8); the fields not named are left at their maximum
 constexpr int wait_vm(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | (7 << 4) | (15 << 8); }
+
+// 16-byte copy into LDS through a buffer resource over [base, base + bytes).
+// (A resource built inside the kernels' generic copy lambda left this file's
+// host pass without the kernels' launch stubs; built here it does not.)
+__device__ __forceinline__ void buf_copy_lds(const void* base, uint32_t bytes, lds_char* dst, int off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(base, bytes), dst, 16, off, 0, 0, 0);
+}
 constexpr int kWaitLgkm0 = 15 | (3 << 14) | (7 << 4);
 
 // Workgroup barrier without the release/acquire fence of __syncthreads (that
@@ -174,6 +182,11 @@ __global__ __launch_bounds__(C::NT, WAVES_PER_SIMD) void grouped_gemm_dma_kernel
   uint32_t w_off[NCW];  // element offsets into the expert's weights (N * K < 2^32)
   int alchunk[EVENK ? 1 : NCA], wlchunk[EVENK ? 1 : NCW];
   const uint16_t* Wexp = p.W + (size_t)e * p.N * p.K;
+  // W rows come through a buffer resource too (one 32-bit offset per lane
+  // instead of a 64-bit address: DeepSeek-like layer 7.93-7.98 -> 7.80-7.82
+  // ms, gate_up 4.35-4.47 -> 4.24-4.26, two alternating runs on one box; the
+  // host keeps an expert's W below 2 GB here)
+  const buf_rsrc_t w_rs = make_rsrc(Wexp, (uint32_t)((size_t)p.N * p.K * 2));
   const buf_rsrc_t a_rs = make_rsrc(p.in, p.in_bytes);
 #pragma unroll
   for (int i = 0; i < NCA; ++i) {
@@ -286,14 +299,26 @@ __global__ __launch_bounds__(C::NT, WAVES_PER_SIMD) void grouped_gemm_dma_kernel
 #pragma unroll
         for (int i = 0; i < NCA; ++i) ldZ(wave * AROWS + i * RPC + lrow, A + (wave * AROWS + i * RPC) * PROW);
       }
+      if (cps >= 8) {  // one segment: its B rows through a buffer resource, like W
+        const uint16_t* b_base = p.B + ((size_t)l1 * p.E + e) * p.N * p.r;
 #pragma unroll
-      for (int i = 0; i < NCW; ++i) {
-        const int r = wave * WROWS + i * RPC + lrow;
-        int l, a, n, rc;
-        chunk(C::swz(r, lslot), l, a, n, rc);  // a chunk without ranks: its z side is zero, any finite B will do
-        const uint16_t* Bs = p.B + ((size_t)l * p.E + e) * p.N * p.r;
-        __builtin_amdgcn_global_load_lds((const void*)(Bs + (size_t)tile_col(r) * p.r + rc * 8),
-                                         (lds_char*)(B + (wave * WROWS + i * RPC) * PROW), 16, 0, 0);
+        for (int i = 0; i < NCW; ++i) {
+          const int r = wave * WROWS + i * RPC + lrow;
+          int l, a, n, rc;
+          chunk(C::swz(r, lslot), l, a, n, rc);  // a chunk without ranks: its z side is zero, any finite B will do
+          buf_copy_lds(b_base, (uint32_t)(p.N * p.r * 2), (lds_char*)(B + (wave * WROWS + i * RPC) * PROW),
+                       (tile_col(r) * p.r + rc * 8) * 2);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < NCW; ++i) {
+          const int r = wave * WROWS + i * RPC + lrow;
+          int l, a, n, rc;
+          chunk(C::swz(r, lslot), l, a, n, rc);
+          const uint16_t* Bs = p.B + ((size_t)l * p.E + e) * p.N * p.r;
+          __builtin_amdgcn_global_load_lds((const void*)(Bs + (size_t)tile_col(r) * p.r + rc * 8),
+                                           (lds_char*)(B + (wave * WROWS + i * RPC) * PROW), 16, 0, 0);
+        }
       }
       return;  // as many copies as a K stage (the waits count them)
     }
@@ -309,8 +334,8 @@ __global__ __launch_bounds__(C::NT, WAVES_PER_SIMD) void grouped_gemm_dma_kernel
       if (!EVENK && k0 + wlchunk[i] * 8 >= p.K) koff = p.K - 8 - wlchunk[i] * 8;
       const int roff = (wave * WROWS + i * RPC) * PROW;
       // cache policy operand 2: non-temporal
-      __builtin_amdgcn_global_load_lds((const void*)(Wexp + (w_off[i] + (uint32_t)koff)), (lds_char*)(B + roff), 16,
-                                       0, NTL ? 2 : 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rs, (lds_char*)(B + roff), 16, (int)((w_off[i] + (uint32_t)koff) * 2u),
+                                               0, 0, NTL ? 2 : 0);
     };
     // all A copies of the stage, then all W copies: at 256 x 256 this order
     // ran the Qwen3-MoE-like gate_up in 273 us against 283 us with each A

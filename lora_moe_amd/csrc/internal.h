@@ -181,7 +181,14 @@ ShrinkPlan plan_shrink(const Layout& L, int K);
 
 // The LDS-tiled GEMM of this mode (0 gate_up, 1 down) runs, and its expand
 // reads z as bf16(s * z)
-inline bool tiled_expand(const Layout& L, int mode) { return L.bm >= 64 && !(mode == 1 && L.hsplit); }
+// An expert's weights of the GEMM of `mode` fit a buffer resource (below 2 GB),
+// as the LDS-tiled GEMMs address them; larger ones run on the streaming kernel.
+inline bool tiled_w_fits(const Layout& L, int mode) {
+  return (mode == 0 ? 2 * (int64_t)L.I * L.H : (int64_t)L.H * L.I) * 2 < (1LL << 31);
+}
+inline bool tiled_expand(const Layout& L, int mode) {
+  return L.bm >= 64 && !(mode == 1 && L.hsplit) && tiled_w_fits(L, mode);
+}
 
 // mode 0: gate_up shrink from x rows gathered by token; mode 1: down shrink
 // from h rows.  z receives the fp32 sums; when tiled_expand(L, mode) also zb
