@@ -179,7 +179,7 @@ __global__ __launch_bounds__(C::NT, WAVES_PER_SIMD) void grouped_gemm_dma_kernel
   // alchunk / wlchunk.
   const int lrow = lane / CPR, lslot = lane % CPR;
   uint32_t a_off[NCA];  // byte offsets into the A buffer (x or h)
-  uint32_t w_off[NCW];  // element offsets into the expert's weights (N * K < 2^32)
+  uint32_t w_off[NCW];  // byte offsets into the expert's weights (below 2^31)
   int alchunk[EVENK ? 1 : NCA], wlchunk[EVENK ? 1 : NCW];
   const uint16_t* Wexp = p.W + (size_t)e * p.N * p.K;
   // W rows come through a buffer resource too (one 32-bit offset per lane
@@ -203,7 +203,7 @@ __global__ __launch_bounds__(C::NT, WAVES_PER_SIMD) void grouped_gemm_dma_kernel
     const int r = wave * WROWS + i * RPC + lrow;
     const int ch = C::swz(r, lslot);
     if (!EVENK) wlchunk[i] = ch;
-    w_off[i] = (uint32_t)tile_col(r) * (uint32_t)p.K + (uint32_t)(ch * 8);
+    w_off[i] = ((uint32_t)tile_col(r) * (uint32_t)p.K + (uint32_t)(ch * 8)) * 2u;
   }
 
   // thin ring: wavefront w copies A rows [8w, 8w + 8) (one copy), W as usual
@@ -323,26 +323,40 @@ __global__ __launch_bounds__(C::NT, WAVES_PER_SIMD) void grouped_gemm_dma_kernel
       return;  // as many copies as a K stage (the waits count them)
     }
     const int k0 = s * BK;
+    // With K a multiple of the stage depth the stage's K offset is the same
+    // for every lane and goes into the scalar offset operand, so a lane's
+    // offsets stay fixed over the loop (DeepSeek-like layer 7.96-8.05 ->
+    // 7.89-7.91 ms, two alternating runs on one box).  A padding row's
+    // offset is past the end of the buffer with or without it.
     auto ldA = [&](int i) {
-      int koff = k0;
-      if (!EVENK && k0 + alchunk[i] * 8 >= p.K) koff = p.K - 8 - alchunk[i] * 8;  // clamped: a valid address
       const int roff = (wave * AROWS + i * RPC) * PROW;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rs, (lds_char*)(A + roff), 16, (int)(a_off[i] + (uint32_t)koff * 2u), 0, 0, 0);
+      if constexpr (EVENK) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rs, (lds_char*)(A + roff), 16, (int)a_off[i], k0 * 2, 0, 0);
+      } else {
+        int koff = k0;
+        if (k0 + alchunk[i] * 8 >= p.K) koff = p.K - 8 - alchunk[i] * 8;  // clamped: a valid address
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rs, (lds_char*)(A + roff), 16, (int)(a_off[i] + (uint32_t)koff * 2u),
+                                                 0, 0, 0);
+      }
     };
     auto ldW = [&](int i) {
-      int koff = k0;
-      if (!EVENK && k0 + wlchunk[i] * 8 >= p.K) koff = p.K - 8 - wlchunk[i] * 8;
       const int roff = (wave * WROWS + i * RPC) * PROW;
       // cache policy operand 2: non-temporal
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rs, (lds_char*)(B + roff), 16, (int)((w_off[i] + (uint32_t)koff) * 2u),
-                                               0, 0, NTL ? 2 : 0);
+      if constexpr (EVENK) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rs, (lds_char*)(B + roff), 16, (int)w_off[i], k0 * 2, 0, NTL ? 2 : 0);
+      } else {
+        int koff = k0;
+        if (k0 + wlchunk[i] * 8 >= p.K) koff = p.K - 8 - wlchunk[i] * 8;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rs, (lds_char*)(B + roff), 16, (int)(w_off[i] + (uint32_t)koff * 2u),
+                                                 0, 0, NTL ? 2 : 0);
+      }
     };
     // all A copies of the stage, then all W copies: at 256 x 256 this order
     // ran the Qwen3-MoE-like gate_up in 273 us against 283 us with each A
     // copy followed by its W copy (three alternating runs on one box)
     if (THIN) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rs, (lds_char*)(A + wave * RPC * PROW), 16,
-                                               (int)(a_off_t + (uint32_t)k0 * 2u), 0, 0, 0);
+                                               (int)a_off_t, k0 * 2, 0, 0);
     } else {
 #pragma unroll
       for (int i = 0; i < NCA; ++i) ldA(i);
