@@ -250,6 +250,17 @@ def test_expand_forms(case, mode):
     full_check(inp, bm, f"expand {case}", knobs=dict(expand_mode=mode))
 
 
+def test_expert_weights_past_2gb():
+    """An expert whose gate_up weights take 2 GB (2I x H x 2 bytes = 2^31)
+    cannot be addressed through the LDS-tiled GEMM's buffer resources; at
+    block_m 256 its gate_up runs on the streaming kernel in 32-row tiles
+    (the down GEMM, I >= 4096, takes h as hi + lo on the same kernel).
+    3 GB of weights, four tokens."""
+    wl = synth.Workload("big-w", T=4, H=16384, I=32768, E=1, topk=1, L=2, r=16,
+                        lora_mode="uniform_with_none", seed=12)
+    full_check(synth.make_inputs(wl), 256, "expert weights past 2 GB")
+
+
 @pytest.mark.parametrize("mode", [1, 2])
 @pytest.mark.parametrize("bm", [64, 128, 192, 256])
 def test_expand_forms_exact(bm, mode):
