@@ -33,9 +33,10 @@
 //     columns of one row, written with one 8-byte (h, bf16) or 16-byte (d,
 //     fp32) store;
 //   * the LoRA expand adds s*z*B^T on the same accumulators, in one of two
-//     forms: as extra K stages through the ring (XD: one 64-deep stage per
-//     64 ranks of each (expert, adapter) segment that meets the row tile,
-//     z rows of the segment on the A side, its B rows on the W side), or
+//     forms: as extra K stages through the ring (XD: 64-deep stages over the
+//     (expert, adapter) segments that meet the row tile, 64 ranks of one
+//     segment or several smaller-rank segments side by side; z rows of the
+//     segment on the A side, its B rows on the W side), or
 //     from registers as masked MFMAs per segment (gemm_expand.h: work items
 //     inside the K loop, the rest after it);
 //   * epilogue: the SiLU gate (mode 0, gate and up columns in the same lane)
@@ -115,7 +116,7 @@ struct DmaCfg {
 
 // EVENK: K is a multiple of the stage depth, so no copy needs clamping or
 // zeroing past K (and the chunk indices need not stay live in the loop).
-// XD (EVENK only): the expand as extra K stages (r a multiple of 64, L <= 64).
+// XD (EVENK only): the expand as extra K stages (L <= 64).
 template <int MODE, class C, int WAVES_PER_SIMD, bool EVENK, bool XD>
 __global__ __launch_bounds__(C::NT, WAVES_PER_SIMD) void grouped_gemm_dma_kernel(GemmParams p) {
   constexpr int BM = C::BM, BN = C::BN, BK = C::BK, NS = C::NS, MI = C::MI, NI = C::NI;

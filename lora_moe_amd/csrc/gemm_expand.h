@@ -1,8 +1,9 @@
-// LoRA expand inside a grouped-GEMM epilogue, for the LDS-tiled GEMM
-// families: the expand output z * B is added to the base output on the
-// accumulators of the same kernel (vLLM blog "Multi-LoRA for MoE models",
-// sections "Implementing multi-LoRA inference for MoE models in vLLM" and
-// "Kernel optimizations").
+// LoRA expand from registers inside the LDS-tiled GEMMs: the expand output
+// z * B is added to the base output on the accumulators of the same kernel
+// (vLLM blog "Multi-LoRA for MoE models", sections "Implementing multi-LoRA
+// inference for MoE models in vLLM" and "Kernel optimizations").  This is the
+// form for ranks below 32 (or when the shape asks for it); from rank 32 the
+// tiled GEMMs run the expand as extra K stages of their own ring instead.
 #pragma once
 
 #include "device_util.h"
