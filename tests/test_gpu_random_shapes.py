@@ -1,0 +1,73 @@
+"""Seeded random layer shapes and kernel configurations against the fp64
+oracle (needs an MI355X).
+
+Sizes, ranks, adapter counts, adapter-id mixes, routing skew, block_m and
+every kernel knob are drawn together, so that combinations no targeted test
+names (an expand as K stages on a 192-row tile beside a K remainder, 70
+adapters on the thin ring, a single expert at block_m 256, ...) still meet
+the tolerance |gpu - ref| <= 1e-2 + 1e-2*|ref|, with and without adapters.
+The shapes are small: the oracle takes milliseconds per case."""
+import numpy as np
+import pytest
+
+import synth
+from gpu_common import compare, compare_delta, log, oracle_tokens, run_gpu, to_device
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+N_CASES = 128
+
+
+def draw(i):
+    """Case i: a Workload, its block_m and kernel knobs (all valid for the ABI)."""
+    rng = np.random.default_rng(1000 + i)
+    E = int(rng.integers(1, 17))
+    k = int(rng.integers(1, min(E, 4) + 1))
+    T = int(rng.integers(1, 300))
+    H = int(rng.integers(1, 80)) * 8
+    I = int(rng.integers(1, 80)) * 8
+    L = int(rng.choice([1, 2, 3, 8, 31, 64, 65, 70]))
+    r = int(rng.integers(1, 17)) * 8
+    bm = int(rng.choice([0, 16, 32, 64, 128, 192, 256]))
+    mode = str(rng.choice(["uniform", "uniform_with_none", "zipf", "none_fraction"]))
+    zb = [d for d in (0, 1, 2, 4) if d == 0 or (r % d == 0 and (r // d) % 8 == 0)]
+    knobs = {"expand_mode": int(rng.integers(0, 3)), "tile_order": int(rng.integers(0, 3)),
+             "shrink_splits": int(rng.choice([0, 0, 1, 2, 4, 16])), "shrink_zblocks": int(rng.choice(zb)),
+             "down_splits": int(rng.choice([0, 0, 1, 3]))}
+    wl = synth.Workload(f"random-{i}", T=T, H=H, I=I, E=E, topk=k, L=L, r=r, lora_mode=mode,
+                        none_fraction=0.2 if mode == "none_fraction" else 0.0,
+                        bias_std=float(rng.choice([0.0, 2.0])), seed=2000 + i)
+    return wl, bm, knobs
+
+
+@pytest.fixture(scope="module", autouse=True)
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import lora_moe_amd as lm
+    lm.load_library()
+
+
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_random_shape(i):
+    import lora_moe_amd as lm
+    wl, bm, knobs = draw(i)
+    shape = lm.make_shape(wl.T, wl.H, wl.I, wl.E, wl.topk, wl.L, wl.r, bm, wl.scale, **knobs)
+    assert lm.moe_lora_workspace_bytes(shape) > 0, (wl, bm, knobs)
+    what = (f"case {i}: T={wl.T} H={wl.H} I={wl.I} E={wl.E} k={wl.topk} L={wl.L} r={wl.r} "
+            f"{wl.lora_mode} bias={wl.bias_std} bm={bm} {knobs}")
+    log(what)
+    inp = synth.make_inputs(wl)
+    dev = to_device(inp)
+    y, shape, ws = run_gpu(dev, wl, bm, knobs=knobs)
+    assert lm.moe_lora_device_errors(shape, ws) == 0, what
+    ref = oracle_tokens(inp, None)
+    compare(y, ref, what)
+    if (inp.lora_ids >= 0).any():
+        none = torch.full_like(dev["lora_ids"], -1)
+        y0, _, _ = run_gpu(dev, wl, bm, lora_ids=none, workspace=ws, knobs=knobs)
+        ref0 = oracle_tokens(inp, None, lora_ids=np.full_like(inp.lora_ids, -1))
+        compare(y0, ref0, what + " (no adapters)")
+        compare_delta(y, y0, ref, ref0, what)
