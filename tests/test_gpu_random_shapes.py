@@ -71,3 +71,52 @@ def test_random_shape(i):
         ref0 = oracle_tokens(inp, None, lora_ids=np.full_like(inp.lora_ids, -1))
         compare(y0, ref0, what + " (no adapters)")
         compare_delta(y, y0, ref, ref0, what)
+
+
+N_LARGE = 16
+
+
+def draw_large(i):
+    """Larger case i: thousands of tokens, so experts span several row tiles
+    (weight reuse across tiles, the interleaved tile order's rounding, thin
+    last tiles), checked on sampled tokens."""
+    rng = np.random.default_rng(5000 + i)
+    E = int(rng.integers(2, 33))
+    k = int(rng.integers(1, min(E, 8) + 1))
+    T = int(rng.integers(1000, 8193))
+    H = int(rng.integers(8, 65)) * 8
+    I = int(rng.integers(8, 65)) * 8
+    L = int(rng.choice([4, 8, 16]))
+    r = int(rng.choice([16, 32, 64, 128]))
+    bm = int(rng.choice([0, 64, 128, 192, 256]))
+    mode = str(rng.choice(["uniform", "uniform_with_none", "zipf", "none_fraction"]))
+    knobs = {"expand_mode": int(rng.integers(0, 3)), "tile_order": int(rng.integers(0, 3))}
+    wl = synth.Workload(f"random-large-{i}", T=T, H=H, I=I, E=E, topk=k, L=L, r=r, lora_mode=mode,
+                        none_fraction=0.2 if mode == "none_fraction" else 0.0,
+                        bias_std=float(rng.choice([0.0, 1.0, 2.0])), seed=6000 + i)
+    return wl, bm, knobs
+
+
+@pytest.mark.parametrize("i", range(N_LARGE))
+def test_random_large_shape(i):
+    import lora_moe_amd as lm
+    from gpu_common import sample_tokens
+    wl, bm, knobs = draw_large(i)
+    shape = lm.make_shape(wl.T, wl.H, wl.I, wl.E, wl.topk, wl.L, wl.r, bm, wl.scale, **knobs)
+    assert lm.moe_lora_workspace_bytes(shape) > 0, (wl, bm, knobs)
+    what = (f"large case {i}: T={wl.T} H={wl.H} I={wl.I} E={wl.E} k={wl.topk} L={wl.L} r={wl.r} "
+            f"{wl.lora_mode} bias={wl.bias_std} bm={lm.moe_lora_resolve_block_m(shape)} {knobs}")
+    log(what)
+    inp = synth.make_inputs(wl, touched_only=True)
+    dev = to_device(inp)
+    y, shape, ws = run_gpu(dev, wl, bm, knobs=knobs)
+    assert lm.moe_lora_device_errors(shape, ws) == 0, what
+    toks = sample_tokens(wl.T, 256, seed=i)
+    ref = oracle_tokens(inp, toks)
+    compare(y[toks], ref, what)
+    none = torch.full_like(dev["lora_ids"], -1)
+    y0, _, _ = run_gpu(dev, wl, bm, lora_ids=none, workspace=ws, knobs=knobs)
+    ref0 = oracle_tokens(inp, toks, lora_ids=np.full_like(inp.lora_ids, -1))
+    compare(y0[toks], ref0, what + " (no adapters)")
+    if (inp.lora_ids[toks] >= 0).any():
+        compare_delta(y[toks], y0[toks], ref, ref0, what)
