@@ -120,3 +120,33 @@ def test_random_large_shape(i):
     compare(y0[toks], ref0, what + " (no adapters)")
     if (inp.lora_ids[toks] >= 0).any():
         compare_delta(y[toks], y0[toks], ref, ref0, what)
+
+
+N_ALIGN = 64
+
+
+def draw_align(i):
+    """Align case i: sizes on both sides of the single-workgroup path's 1024
+    pairs, skewed routing, duplicate experts in a token and invalid ids."""
+    rng = np.random.default_rng(9000 + i)
+    E = int(rng.integers(1, 301))
+    L = int(rng.integers(1, min(61, 14336 // E)))
+    k = int(rng.integers(1, min(E, 8) + 1))
+    T = int(rng.choice([int(rng.integers(1, 129)), int(rng.integers(129, 6001))]))
+    bm = int(rng.choice([16, 32, 64, 128, 192, 256]))
+    hot = rng.random() < 0.5
+    ids = rng.integers(0, E, (T, k))
+    if hot:  # most pairs on one expert
+        ids = np.where(rng.random((T, k)) < 0.6, int(rng.integers(0, E)), ids)
+    bad = rng.random((T, k)) < 0.02
+    ids = np.where(bad, rng.choice([-1, E, E + 7, -100], (T, k)), ids).astype(np.int32)
+    lids = rng.integers(-1, L, T)
+    lids = np.where(rng.random(T) < 0.02, rng.choice([L, -2, 999], T), lids).astype(np.int32)
+    return T, k, E, L, bm, ids, lids
+
+
+@pytest.mark.parametrize("i", range(N_ALIGN))
+def test_random_align(i):
+    from test_gpu_parity import check_align_exact
+    T, k, E, L, bm, ids, lids = draw_align(i)
+    check_align_exact(T, k, E, L, bm, ids, lids, f"random align {i}")
