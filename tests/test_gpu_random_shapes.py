@@ -150,3 +150,71 @@ def test_random_align(i):
     from test_gpu_parity import check_align_exact
     T, k, E, L, bm, ids, lids = draw_align(i)
     check_align_exact(T, k, E, L, bm, ids, lids, f"random align {i}")
+
+
+N_ROUTE = 48
+
+
+def draw_route(i):
+    """Router case i: expert counts on both sides of the router's 512-expert
+    path, k up to 64, ties, skewed biases and scattered non-finite logits."""
+    rng = np.random.default_rng(11000 + i)
+    E = int(rng.choice([int(rng.integers(1, 513)), int(rng.integers(513, 1025))]))
+    k = int(rng.integers(1, min(E, 64) + 1))
+    T = int(rng.integers(1, 400))
+    key = synth.stream_key(12000 + i, 0, T, E)
+    if rng.random() < 0.3:  # a coarse grid: many equal logits per token
+        lg = np.floor(synth.uniform(key, T * E) * 4.0) - 2.0
+    else:
+        lg = synth.normal(key, T * E) + rng.choice([0.0, 2.0]) * np.tile(synth.normal(
+            synth.stream_key(12000 + i, 1, T, E), E), T)
+    lg = np.asarray(lg, np.float64).reshape(T, E).astype(np.float32)
+    if rng.random() < 0.3:
+        bad = rng.random((T, E)) < 0.05
+        lg = np.where(bad, rng.choice([np.nan, np.inf, -np.inf], (T, E)).astype(np.float32), lg)
+        for t in rng.integers(0, T, 3):  # rows with fewer finite logits than k: -1 slots
+            keep = rng.permutation(E)[:int(rng.integers(0, k))]
+            row = np.full(E, rng.choice([np.nan, -np.inf]), np.float32)
+            row[keep] = lg[t, keep]
+            lg[t] = row
+    L = int(rng.integers(1, 9))
+    lids = rng.integers(-1, L, T).astype(np.int32)
+    bm = int(rng.choice([16, 32, 64, 128, 256]))
+    return np.ascontiguousarray(lg), k, L, lids, bm
+
+
+@pytest.mark.parametrize("i", range(N_ROUTE))
+def test_random_route(i):
+    """The router alone and the fused router + align: ids bit-exact and
+    weights within 1e-6 of the fp64 reference, the align's outputs bit-exact
+    against the reference align on the reference ids."""
+    import lora_moe_amd as lm
+    import oracle
+    from gpu_common import gpu_views
+    lg, k, L, lids, bm = draw_route(i)
+    T, E = lg.shape
+    what = f"random route {i}: T={T} E={E} k={k} L={L} bm={bm}"
+    log(what)
+    o = oracle.Oracle()
+    rids, rw = o.route(lg, k)
+    shape = lm.make_shape(T, 64, 64, E, k, L, 8, bm)
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    dlg = torch.from_numpy(lg).cuda()
+    lm.moe_lora_route(shape, dlg, ids, w)
+    torch.cuda.synchronize()
+    assert np.array_equal(ids.cpu().numpy(), rids), what
+    wg = w.cpu().numpy()
+    assert np.all(np.isfinite(wg)) and float(np.max(np.abs(wg - rw))) <= 1e-6, what
+    ws = lm.alloc_workspace(shape)
+    ids.fill_(-7)
+    w.zero_()
+    lm.moe_lora_route_align(shape, dlg, torch.from_numpy(lids).cuda(), ids, w, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(ids.cpu().numpy(), rids), what + " (fused)"
+    assert float(np.max(np.abs(w.cpu().numpy() - rw))) <= 1e-6, what + " (fused)"
+    got = gpu_views(shape, ws)
+    want = o.align(T, k, E, L, got["block_m"], rids, lids, got["cap_rows"], got["cap_blocks"])
+    for name in ("sorted_ids", "expert_off", "seg_start", "seg_cnt", "block_expert", "pos_of_pair"):
+        assert np.array_equal(got[name], want[name]), f"{what}: {name} differs"
+    assert got["num_padded"] == want["num_padded"] and got["err_count"] == want["err_count"], what
