@@ -419,8 +419,9 @@ __global__ __launch_bounds__(C::NT, WAVES_PER_SIMD) void grouped_gemm_dma_kernel
   // conservative wait there costs nothing, and the reads overlap the rest.
   // The scheduling barriers keep this order (the scheduler would otherwise
   // sink the reads next to their use).
-  auto step = [&](int set, bool next, int qn, int kkn, auto thin_c) {
+  auto step = [&](int set, bool next, int qn, int kkn, auto thin_c, auto all_c) {
     constexpr bool THIN = decltype(thin_c)::value;
+    constexpr bool ALL = decltype(all_c)::value;  // every row block holds real rows
     acc[0][0] = mfma_32x32x16(bf[set][0], af[set][0], acc[0][0]);
     __builtin_amdgcn_sched_barrier(0);
     if (next) frag(qn, kkn, set ^ 1, thin_c);
@@ -429,7 +430,7 @@ __global__ __launch_bounds__(C::NT, WAVES_PER_SIMD) void grouped_gemm_dma_kernel
     for (int mi = 0; mi < (THIN ? C::TR / 32 : MI); ++mi)
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni)
-        if ((mi | ni) && (mi == 0 || blk_live[mi]))
+        if ((mi | ni) && (mi == 0 || ALL || blk_live[mi]))
           acc[mi][ni] = mfma_32x32x16(bf[set][ni], af[set][mi], acc[mi][ni]);
   };
 
@@ -464,7 +465,7 @@ __global__ __launch_bounds__(C::NT, WAVES_PER_SIMD) void grouped_gemm_dma_kernel
   xi.next = 0;
   xi.lrest = 64;
   bool xpend = false;  // an item is loaded and not yet multiplied
-  auto kloop = [&](auto live_c, auto nt_c, auto thin_c) {
+  auto kloop = [&](auto live_c, auto nt_c, auto thin_c, auto all_c) {
     constexpr bool LIVE = decltype(live_c)::value;
     constexpr bool THIN = decltype(thin_c)::value;
     constexpr int RNS = THIN ? C::TNS : NS;  // stages in the ring
@@ -497,7 +498,7 @@ __global__ __launch_bounds__(C::NT, WAVES_PER_SIMD) void grouped_gemm_dma_kernel
     for (int q = 0; q + 1 < nst; ++q) {
 #pragma unroll
       for (int kk = 0; kk + 1 < KK; ++kk)
-        if (LIVE) step(kk & 1, true, q, kk + 1, thin_c);
+        if (LIVE) step(kk & 1, true, q, kk + 1, thin_c, all_c);
       // own copies of stage q + 1 have landed (later stages may still fly);
       // the wait stays behind this stage's MFMAs
       __builtin_amdgcn_sched_barrier(0);
@@ -516,12 +517,12 @@ __global__ __launch_bounds__(C::NT, WAVES_PER_SIMD) void grouped_gemm_dma_kernel
       }
       // last slice of stage q (its fragments are in registers), with the
       // first reads of stage q + 1
-      if (LIVE) step((KK - 1) & 1, true, q + 1, 0, thin_c);
+      if (LIVE) step((KK - 1) & 1, true, q + 1, 0, thin_c, all_c);
     }
     if (LIVE) {  // the last stage
 #pragma unroll
-      for (int kk = 0; kk + 1 < KK; ++kk) step(kk & 1, true, nst - 1, kk + 1, thin_c);
-      step((KK - 1) & 1, false, 0, 0, thin_c);
+      for (int kk = 0; kk + 1 < KK; ++kk) step(kk & 1, true, nst - 1, kk + 1, thin_c, all_c);
+      step((KK - 1) & 1, false, 0, 0, thin_c, all_c);
     }
   };
   typedef std::integral_constant<bool, true> yes;
@@ -534,13 +535,25 @@ __global__ __launch_bounds__(C::NT, WAVES_PER_SIMD) void grouped_gemm_dma_kernel
   // 8.50 -> 8.26 ms (three alternating runs on one box, same outputs).
   // 256-row tiles only (the thin loop exists only for them), and K without
   // a remainder (no zero_tail).
+  // Wavefronts whose row blocks all hold real rows (every wavefront of a
+  // full tile) run a copy of the loop without the per-block MFMA skip: its
+  // tests sat between the MFMAs of every K slice as scalar branches.
+  bool all_live = true;
+#pragma unroll
+  for (int mi = 1; mi < MI; ++mi) all_live = all_live && blk_live[mi];
   auto run = [&](auto thin_c) {
+    constexpr bool THIN = decltype(thin_c)::value;
     if (live) {
-      if (w_once) kloop(yes(), yes(), thin_c);
-      else kloop(yes(), no(), thin_c);
+      if (!THIN && all_live) {
+        if (w_once) kloop(yes(), yes(), thin_c, yes());
+        else kloop(yes(), no(), thin_c, yes());
+      } else {
+        if (w_once) kloop(yes(), yes(), thin_c, no());
+        else kloop(yes(), no(), thin_c, no());
+      }
     } else {
-      if (w_once) kloop(no(), yes(), thin_c);
-      else kloop(no(), no(), thin_c);
+      if (w_once) kloop(no(), yes(), thin_c, no());
+      else kloop(no(), no(), thin_c, no());
     }
   };
   if constexpr (BM == 256 && C::TNS >= 3) {
