@@ -43,9 +43,9 @@
 //     or the top-k weight (mode 1); the rows' validity and weights are staged
 //     in LDS at the start.
 // A wavefront whose rows are all padding skips its MFMAs and stores but still
-// copies its share of every stage.  256-row tiles with at most 64 real rows
-// run on a ring of thin stages (64 A rows + the W tile) that keeps two stages
-// in flight instead of one.
+// copies its share of every stage.  Row tiles with few real rows (at most 64
+// of 256, or 128 of 192) run on a ring of thin stages (those A rows + the W
+// tile) that keeps two stages in flight instead of one.
 #include <type_traits>
 
 #include "device_util.h"
@@ -79,7 +79,7 @@ __device__ __forceinline__ void stage_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <int BM_, int BN_, int BK_, int NS_>
+template <int BM_, int BN_, int BK_, int NS_, int TR_ = 0>
 struct DmaCfg {
   static constexpr int BM = BM_, BN = BN_;    // tile rows (pairs) and columns (weight rows)
   static constexpr int BK = BK_;              // K depth of one stage
@@ -91,7 +91,12 @@ struct DmaCfg {
   static constexpr int ATILE = BM * PROW;     // A tile (rows x K slice)
   static constexpr int WTILE = BN * PROW;     // W tile (weight rows x K slice)
   static constexpr int STAGE = ATILE + WTILE;
-  static constexpr int RING = NS * STAGE;
+  // thin ring for row tiles with at most TR real rows (0: none): stages of
+  // TR A rows and the whole W tile, three of them (two in flight) in the LDS
+  // of the ring
+  static constexpr int TR = TR_, TATILE = TR * PROW, TSTAGE = TATILE + WTILE;
+  static constexpr int TNS = TR > 0 ? 3 : 0;
+  static constexpr int RING = NS * STAGE > TNS * TSTAGE ? NS * STAGE : TNS * TSTAGE;
   static constexpr int LDS = RING + 2 * BM * 4;  // ring + per-row validity and top-k weight
   static constexpr int ROWS_PER_COPY = 1024 / PROW;
   static constexpr int AROWS = BM / NW, WROWS = BN / NW;  // tile rows each wavefront copies
@@ -101,10 +106,8 @@ struct DmaCfg {
   static_assert(NCA >= 1 && NCA * ROWS_PER_COPY == AROWS && NCW * ROWS_PER_COPY == WROWS, "copy layout");
   static_assert(LDS <= 160 * 1024, "LDS ring exceeds 160 KB");
   static_assert(NS >= 2, "ring needs two stages");
-  // thin ring for row tiles with at most TR real rows: stages of TR A rows
-  // and the whole W tile, TNS of them in the same LDS (3 at 256 x 256)
-  static constexpr int TR = 64, TATILE = TR * PROW, TSTAGE = TATILE + WTILE;
-  static constexpr int TNS = RING / TSTAGE;
+  static constexpr int TNCA = TR / (NW * ROWS_PER_COPY);  // thin A copies per wavefront per stage
+  static_assert(TR == 0 || (TR % 32 == 0 && TR < BM && TNCA * NW * ROWS_PER_COPY == TR), "thin ring rows");
 
   // chunk slot of logical chunk `chunk` in tile row `row`: consecutive 16-lane
   // phases of a fragment read cover 16 rows and all 64 banks
@@ -207,14 +210,16 @@ __global__ __launch_bounds__(C::NT, WAVES_PER_SIMD) void grouped_gemm_dma_kernel
     w_off[i] = ((uint32_t)tile_col(r) * (uint32_t)p.K + (uint32_t)(ch * 8)) * 2u;
   }
 
-  // thin ring: wavefront w copies A rows [8w, 8w + 8) (one copy), W as usual
-  uint32_t a_off_t = kBufNone;
-  {
-    const int r = wave * RPC + lrow;
+  // thin ring: wavefront w copies A rows [TNCA*8*w, TNCA*8*(w + 1)), W as usual
+  constexpr int TNCA = C::TNCA;
+  uint32_t a_off_t[TNCA > 0 ? TNCA : 1];
+#pragma unroll
+  for (int i = 0; i < TNCA; ++i) {
+    const int r = (wave * TNCA + i) * RPC + lrow;
     const int ch = C::swz(r, lslot);
     const int pr = p.sorted[row0 + r];
     const int arow = MODE == 0 ? pr / p.topk : row0 + r;
-    a_off_t = pr < p.P ? (uint32_t)(arow * p.K + ch * 8) * 2u : kBufNone;
+    a_off_t[i] = pr < p.P ? (uint32_t)(arow * p.K + ch * 8) * 2u : kBufNone;
   }
   const int ntile = (p.K + BK - 1) / BK;  // the last stage may be partial
   const bool partial = !EVENK && (p.K % BK) != 0;
@@ -295,7 +300,8 @@ __global__ __launch_bounds__(C::NT, WAVES_PER_SIMD) void grouped_gemm_dma_kernel
         __builtin_amdgcn_raw_ptr_buffer_load_lds(z_rs, (lds_char*)dst, 16, (int)off, 0, 0, 0);
       };
       if (THIN) {
-        ldZ(wave * RPC + lrow, A + wave * RPC * PROW);
+#pragma unroll
+        for (int i = 0; i < TNCA; ++i) ldZ((wave * TNCA + i) * RPC + lrow, A + (wave * TNCA + i) * RPC * PROW);
       } else {
 #pragma unroll
         for (int i = 0; i < NCA; ++i) ldZ(wave * AROWS + i * RPC + lrow, A + (wave * AROWS + i * RPC) * PROW);
@@ -356,8 +362,10 @@ __global__ __launch_bounds__(C::NT, WAVES_PER_SIMD) void grouped_gemm_dma_kernel
     // ran the Qwen3-MoE-like gate_up in 273 us against 283 us with each A
     // copy followed by its W copy (three alternating runs on one box)
     if (THIN) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rs, (lds_char*)(A + wave * RPC * PROW), 16,
-                                               (int)a_off_t, k0 * 2, 0, 0);
+#pragma unroll
+      for (int i = 0; i < TNCA; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rs, (lds_char*)(A + (wave * TNCA + i) * RPC * PROW), 16,
+                                                 (int)a_off_t[i], k0 * 2, 0, 0);
     } else {
 #pragma unroll
       for (int i = 0; i < NCA; ++i) ldA(i);
@@ -399,15 +407,16 @@ __global__ __launch_bounds__(C::NT, WAVES_PER_SIMD) void grouped_gemm_dma_kernel
   for (int mi = 0; mi < MI; ++mi)
     blk_live[mi] = __builtin_amdgcn_readfirstlane(p.sorted[row0 + wrow + 32 * mi] < p.P);
   u32x4_t af[2][MI], bf[2][NI];
-  // THIN: the ring holds tile rows [0, 64) only; the wavefronts that read
-  // it (rows from 0) use row blocks 0 and 1
+  // THIN: the ring holds tile rows [0, TR) only; the row blocks past TR are
+  // padding (their MFMAs are skipped) and at most TMI blocks are read
+  constexpr int TMI = C::TR / 32 < MI ? C::TR / 32 : MI;
   auto frag = [&](int s, int kk, int set, auto thin_c) {
     constexpr bool THIN = decltype(thin_c)::value;
     const char* A = THIN ? smem + (s % C::TNS) * C::TSTAGE : smem + (s % NS) * C::STAGE;
     const char* B = A + (THIN ? C::TATILE : C::ATILE);
     const int ch = 2 * kk + khalf;
 #pragma unroll
-    for (int mi = 0; mi < (THIN ? C::TR / 32 : MI); ++mi)
+    for (int mi = 0; mi < (THIN ? TMI : MI); ++mi)
       af[set][mi] = *reinterpret_cast<const u32x4_t*>(A + C::off(wrow + mi * 32 + l32, ch));
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni)
@@ -427,7 +436,7 @@ __global__ __launch_bounds__(C::NT, WAVES_PER_SIMD) void grouped_gemm_dma_kernel
     if (next) frag(qn, kkn, set ^ 1, thin_c);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int mi = 0; mi < (THIN ? C::TR / 32 : MI); ++mi)
+    for (int mi = 0; mi < (THIN ? TMI : MI); ++mi)
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni)
         if ((mi | ni) && (mi == 0 || ALL || blk_live[mi]))
@@ -469,7 +478,7 @@ __global__ __launch_bounds__(C::NT, WAVES_PER_SIMD) void grouped_gemm_dma_kernel
     constexpr bool LIVE = decltype(live_c)::value;
     constexpr bool THIN = decltype(thin_c)::value;
     constexpr int RNS = THIN ? C::TNS : NS;  // stages in the ring
-    constexpr int VMA = THIN ? (1 + NCW) * (C::TNS - 2) : VM_AHEAD;
+    constexpr int VMA = THIN ? (TNCA + NCW) * (C::TNS - 2) : VM_AHEAD;
     // prologue: every ring slot gets a stage; wait for stage 0
 #pragma unroll
     for (int s = 0; s < RNS; ++s)
@@ -509,11 +518,21 @@ __global__ __launch_bounds__(C::NT, WAVES_PER_SIMD) void grouped_gemm_dma_kernel
       if (partial && q + 1 == ntile - 1) zero_tail(q + 1);
       __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // fragment reads of stage q and zero writes done
       stage_barrier();
-      if (q + RNS < nst) issue(q + RNS, nt_c, thin_c);  // into the slot stage q just released
-      if (LIVE && xpend) {
-        expand_item_mfma(xi, acc, row0 + wrow);
-        xpend = xi.next < xi.nitems;
-        if (xpend) expand_item_load(xi, p, e, row0 + wrow, 0, ncol);
+      auto xitem = [&]() __attribute__((always_inline)) {
+        if (LIVE && xpend) {
+          expand_item_mfma(xi, acc, row0 + wrow);
+          xpend = xi.next < xi.nitems;
+          if (xpend) expand_item_load(xi, p, e, row0 + wrow, 0, ncol);
+        }
+      };
+      if constexpr (THIN) {
+        // the item's loads go before the copies, so that the wait above
+        // (which lets the youngest stage's copies fly) counts only copies
+        xitem();
+        if (q + RNS < nst) issue(q + RNS, nt_c, thin_c);  // into the slot stage q just released
+      } else {
+        if (q + RNS < nst) issue(q + RNS, nt_c, thin_c);
+        xitem();
       }
       // last slice of stage q (its fragments are in registers), with the
       // first reads of stage q + 1
@@ -527,14 +546,13 @@ __global__ __launch_bounds__(C::NT, WAVES_PER_SIMD) void grouped_gemm_dma_kernel
   };
   typedef std::integral_constant<bool, true> yes;
   typedef std::integral_constant<bool, false> no;
-  // Thin row tiles (at most 64 real rows, the rest padding: an expert's
+  // Thin row tiles (at most TR real rows, the rest padding: an expert's
   // last tile) fetch little besides the weight tile, so the per-CU fetch
-  // latency bounds them; their ring holds 64 A rows per stage, which makes
-  // room for three stages (two in flight) in the same LDS.  At the
-  // DeepSeek-like shape (89 of 359 row tiles are thin) the layer went
-  // 8.50 -> 8.26 ms (three alternating runs on one box, same outputs).
-  // 256-row tiles only (the thin loop exists only for them), and K without
-  // a remainder (no zero_tail).
+  // latency bounds them; their ring holds TR A rows per stage, which makes
+  // room for three stages (two in flight).  At the DeepSeek-like shape (89
+  // of 359 row tiles are thin at TR = 64) the layer went 8.50 -> 8.26 ms
+  // (three alternating runs on one box, same outputs).  K without a
+  // remainder only (no zero_tail).
   // Wavefronts whose row blocks all hold real rows (every wavefront of a
   // full tile) run a copy of the loop without the per-block MFMA skip: its
   // tests sat between the MFMAs of every K slice as scalar branches.
@@ -556,7 +574,7 @@ __global__ __launch_bounds__(C::NT, WAVES_PER_SIMD) void grouped_gemm_dma_kernel
       else kloop(no(), no(), thin_c, no());
     }
   };
-  if constexpr (BM == 256 && C::TNS >= 3) {
+  if constexpr (C::TR > 0) {
     if (EVENK && p.sorted[row0 + C::TR] >= p.P) run(yes());
     else run(no());
   } else {
@@ -667,7 +685,7 @@ int launch_dma(const GemmParams& gp_in, int mode, int64_t cap_rows, hipStream_t 
 
 // 256 x 256 tiles, 8 wavefronts, two 64-deep stages (128 KB of LDS)
 int launch_gemm_prefill(const GemmParams& gp, int mode, int64_t cap_rows, hipStream_t st) {
-  return launch_dma<DmaCfg<256, 256, 64, 2>, 2>(gp, mode, cap_rows, st);
+  return launch_dma<DmaCfg<256, 256, 64, 2, 64>, 2>(gp, mode, cap_rows, st);
 }
 
 // 128 x 128 tiles, 4 wavefronts, two 64-deep stages (64 KB of LDS, two
@@ -685,7 +703,7 @@ int launch_gemm_dma128(const GemmParams& gp, int mode, int64_t cap_rows, hipStre
 // tiles (two alternating runs on one box).  At the DeepSeek-like shape it was
 // slower (9.24 against 9.01 ms).
 int launch_gemm_dma192(const GemmParams& gp, int mode, int64_t cap_rows, hipStream_t st) {
-  return launch_dma<DmaCfg<192, 256, 64, 2>, 2>(gp, mode, cap_rows, st);
+  return launch_dma<DmaCfg<192, 256, 64, 2, 128>, 2>(gp, mode, cap_rows, st);
 }
 
 // 64 x 128 tiles, 4 wavefronts of 32 x 64 outputs, two 64-deep stages (48 KB
