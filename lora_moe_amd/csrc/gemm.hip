@@ -22,6 +22,9 @@
 // stream and is organised around HBM efficiency -- see the kernel comment.
 // Row tiles hold 16 or 32 rows of a single expert (expert runs are padded to
 // block_m, the tile's row count).
+#include <algorithm>
+#include <type_traits>
+
 #include "device_util.h"
 #include "internal.h"
 
@@ -107,10 +110,25 @@ __global__ __launch_bounds__(64 * NWV) void grouped_gemm_kernel(GemmParams p) {
   if (MODE == 1 && p.sorted[row0] >= p.P) return;
   const int e = p.bexp[row0 / p.bm];
 
+  // mode 0: this wavefront's column group (8 gate and 8 up columns).  With
+  // gbal the ceil(I / 8) groups are spread evenly over the workgroups, up to
+  // NWV each, and the wavefronts past a workgroup's count only stage row
+  // fragments: a single-expert layer has one row tile, and its
+  // ceil(I / 64) workgroups of 8 wavefronts (400 at I = 25600) left some
+  // CUs with twice the weight bytes of others.
+  int grp = (int)blockIdx.x * NWV + wave;
+  bool active = true;
+  if (MODE == 0 && p.gbal) {
+    const int ngrp = (p.I + 7) / 8;
+    const int g0 = (int)(((int64_t)blockIdx.x * ngrp) / gridDim.x);
+    const int g1 = (int)(((int64_t)(blockIdx.x + 1) * ngrp) / gridDim.x);
+    grp = g0 + wave;
+    active = grp < g1;
+  }
   // weight row held by fragment column c (0..15) of this wavefront
   auto wrow_of = [&](int c) -> int {
     if (MODE == 0) {
-      const int j = min((int)blockIdx.x * (NWV * 8) + wave * 8 + (c & 7), p.I - 1);
+      const int j = min(grp * 8 + (c & 7), p.I - 1);
       return c < 8 ? j : p.I + j;
     }
     return min((int)blockIdx.x * (NWV * 16) + wave * 16 + c, p.N - 1);
@@ -160,11 +178,16 @@ __global__ __launch_bounds__(64 * NWV) void grouped_gemm_kernel(GemmParams p) {
 
   u32x4_t rw[4], rx[XPT], rxl[XPT];
   uint2 rxh, rxhl;  // HALF: this thread's 8 bytes (hi, lo)
-  auto load = [&](int k0, bool masked) {
+  // ACT: the wavefront has a column group (every wavefront without gbal);
+  // the others stage row fragments and meet the barriers only
+  auto load = [&](int k0, bool masked, auto act_c) {
+    constexpr bool ACT = decltype(act_c)::value;
     const bool ok = !masked || piece * 8 < krem;
+    if constexpr (ACT) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      rw[i] = ok ? ld16_stream(Wexp + (woff[i] + (uint32_t)(kbase + k0 + piece * 8))) : zero4();
+      for (int i = 0; i < 4; ++i)
+        rw[i] = ok ? ld16_stream(Wexp + (woff[i] + (uint32_t)(kbase + k0 + piece * 8))) : zero4();
+    }
 #pragma unroll
     for (int j = 0; j < XPT; ++j)
     {
@@ -191,11 +214,14 @@ __global__ __launch_bounds__(64 * NWV) void grouped_gemm_kernel(GemmParams p) {
   // pieces to this chunk's shared buffer), then the next chunk's loads are
   // issued, then one barrier and the MFMAs of this chunk.  The buffer written
   // here was last read a chunk ago, before the previous barrier.
-  auto consume = [&](int next_k0, int next_kind) {  // kind: 0 none, 1 full, 2 masked remainder
+  auto consume = [&](int next_k0, int next_kind, auto act_c) {  // kind: 0 none, 1 full, 2 masked remainder
+    constexpr bool ACT = decltype(act_c)::value;
+    if constexpr (ACT) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int fr = 4 * i + (lane >> 4);
-      *reinterpret_cast<u32x4_t*>(&slice[fr * KC + ((piece ^ fr) << 3)]) = rw[i];
+      for (int i = 0; i < 4; ++i) {
+        const int fr = 4 * i + (lane >> 4);
+        *reinterpret_cast<u32x4_t*>(&slice[fr * KC + ((piece ^ fr) << 3)]) = rw[i];
+      }
     }
     uint16_t* xb = xl[buf];
     uint16_t* xbl = xll[HL ? buf : 0];
@@ -211,8 +237,9 @@ __global__ __launch_bounds__(64 * NWV) void grouped_gemm_kernel(GemmParams p) {
       }
     }
     buf ^= 1;
-    if (next_kind) load(next_k0, next_kind == 2);
+    if (next_kind) load(next_k0, next_kind == 2, act_c);
     lds_barrier();
+    if constexpr (!ACT) return;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const u32x4_t b =
@@ -227,18 +254,26 @@ __global__ __launch_bounds__(64 * NWV) void grouped_gemm_kernel(GemmParams p) {
     }
   };
 
-  if (nfull > 0) {
-    load(rot * KC, false);
-    int c = rot;
-    for (int q = 0; q + 1 < nfull; ++q) {  // steady state: unconditional refills
-      c = c + 1 == nfull ? 0 : c + 1;
-      consume(c * KC, 1);
+  auto kloop = [&](auto act_c) {
+    if (nfull > 0) {
+      load(rot * KC, false, act_c);
+      int c = rot;
+      for (int q = 0; q + 1 < nfull; ++q) {  // steady state: unconditional refills
+        c = c + 1 == nfull ? 0 : c + 1;
+        consume(c * KC, 1, act_c);
+      }
+      consume(nfull * KC, krem ? 2 : 0, act_c);
+    } else {
+      load(0, true, act_c);
     }
-    consume(nfull * KC, krem ? 2 : 0);
+    if (krem) consume(0, 0, act_c);
+  };
+  if (active) {
+    kloop(std::integral_constant<bool, true>());
   } else {
-    load(0, true);
+    kloop(std::integral_constant<bool, false>());
+    return;
   }
-  if (krem) consume(0, 0);
 
   // epilogue: lane (m, kq) holds rows rf*16 + 4*kq + i of fragment column m,
   // i.e. weight row wrow_of(m); the expand is added per lane for that row
@@ -261,7 +296,7 @@ __global__ __launch_bounds__(64 * NWV) void grouped_gemm_kernel(GemmParams p) {
                               p.B + (((size_t)l * p.E + e) * p.N + wr) * p.r, p.r);
       if (MODE == 0) {
         const float up = __shfl_xor(v, 8, 64);  // lane m < 8: gate; m + 8: its up
-        const int j = blockIdx.x * (NWV * 8) + wave * 8 + m;
+        const int j = grp * 8 + m;
         if (m < 8 && j < p.I) {
           const float hv = real ? silu_f32(v) * up : 0.f;
           const uint16_t hb = f32_to_bf16(hv);
@@ -280,6 +315,22 @@ void launch_nwv(const GemmParams& gp, int64_t cap_rows, hipStream_t st) {
   const int ncol = MODE == 0 ? (gp.I + NWV * 8 - 1) / (NWV * 8) : (gp.H + NWV * 16 - 1) / (NWV * 16);
   dim3 grid(ncol, (unsigned)((cap_rows + RF * 16 - 1) / (RF * 16)), MODE == 1 ? gp.ksplit : 1);
   grouped_gemm_kernel<MODE, RF, NWV, HL><<<grid, NWV * 64, 0, st>>>(gp);
+}
+
+// A single-expert gate_up whose pairs fit one 32-row tile (dense decode):
+// 16-wavefront workgroups, one per CU of the MI355X's 256, each taking an
+// even share (12 or 13 at I = 25600) of the ceil(I / 8) column groups.
+// Dense layer (T = 32, H = 5120), gate_up with 400 workgroups of 8 against
+// this (two alternating runs, us): I = 25600 109 -> 99, I = 20480 102 -> 81,
+// I = 16384 (256 workgroups of 8 before) 65 -> 66.
+void launch_gate_up_balanced(const GemmParams& gp_in, int64_t cap_rows, hipStream_t st) {
+  constexpr int NWV = 16, kCUs = 256;
+  GemmParams gp = gp_in;
+  gp.gbal = 1;
+  const int ngrp = (gp.I + 7) / 8;
+  const int G = std::max(std::min(kCUs, ngrp), (ngrp + NWV - 1) / NWV);  // at most NWV groups each
+  dim3 grid(G, (unsigned)((cap_rows + 31) / 32), 1);
+  grouped_gemm_kernel<0, 2, NWV, false><<<grid, NWV * 64, 0, st>>>(gp);
 }
 
 template <int MODE, int RF, bool HL = false>
@@ -330,6 +381,7 @@ int launch_gemm(const Layout& L, int mode, const uint16_t* in, const int32_t* lo
   gp.order = L.tile_order ? L.tile_order : (mode == 0 ? 1 : 2);
   gp.d_slab = L.cap_rows * (int64_t)L.H;
   gp.s = L.s;
+  gp.gbal = 0;
   // the LDS-tiled GEMMs' expand as extra K stages (gemm_dma.hip) where the
   // adapters fit one lane each (L <= 64), K has no remainder and zb is
   // addressable through a buffer resource; by default from rank 32 on (at
@@ -383,7 +435,8 @@ int launch_gemm(const Layout& L, int mode, const uint16_t* in, const int32_t* lo
   // 16- or 32-row tiles
   const int RF = L.bm >= 32 ? 2 : 1;
   if (mode == 0) {
-    if (RF == 2) launch_rf<0, 2>(gp, L.cap_rows, st);
+    if (RF == 2 && L.E == 1 && L.P <= 32) launch_gate_up_balanced(gp, L.cap_rows, st);
+    else if (RF == 2) launch_rf<0, 2>(gp, L.cap_rows, st);
     else launch_rf<0, 1>(gp, L.cap_rows, st);
   } else {
     if (RF == 2) launch_rf<1, 2>(gp, L.cap_rows, st);

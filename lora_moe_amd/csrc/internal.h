@@ -126,6 +126,8 @@ struct GemmParams {
   float s;
   int xstages;        // tiled family: the expand as extra K stages through the LDS ring
   uint32_t zb_bytes;  // size of zb in bytes (below 2^31 whenever xstages is set)
+  int gbal;           // streaming family, mode 0: column groups spread evenly over gridDim.x
+                      // workgroups (some wavefronts idle) instead of NWV per workgroup
 };
 
 // ------------------------------------------------------------------ stage timing

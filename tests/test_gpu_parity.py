@@ -133,6 +133,17 @@ def test_tiny_scale_and_seed():
     full_check(inp, 0, "tiny seed 3 scale 0.5", scale=0.5)
 
 
+@pytest.mark.parametrize("T,I", [(32, 25600), (32, 4104), (7, 200)])
+def test_dense_balanced_gate_up(T, I):
+    """One expert whose pairs fit one 32-row tile: the gate_up spreads its
+    ceil(I / 8) column groups evenly over the workgroups (12-13 each at I =
+    25600, 2-3 at 4104, one each at 200), the wavefronts past a workgroup's
+    share idle."""
+    wl = synth.Workload("dense-bal", T=T, H=512, I=I, E=1, topk=1, L=3, r=16,
+                        lora_mode="uniform_with_none")
+    full_check(synth.make_inputs(wl), 32, f"dense balanced T={T} I={I}")
+
+
 @pytest.mark.parametrize("bm", [0, 64, 128, 192, 256])
 @pytest.mark.parametrize("H,I,r", [(104, 104, 8), (104, 1000, 24), (1000, 104, 16), (2880, 2880, 64),
                                    (256, 512, 128), (64, 40, 8), (24, 16, 8)])
