@@ -73,7 +73,8 @@ typedef struct moe_lora_shape {
   int32_t shrink_zblocks; /* work items per shrink tile across the r columns:    */
                           /* 1 (all r), or 2..r/8 dividing r into multiples of 8 */
   int32_t down_splits;    /* K splits of the streaming down GEMM (the one that   */
-                          /* runs for block_m <= 32 or I >= 4096), 1..8          */
+                          /* runs for block_m <= 32 or I >= 4096), 1..64 (at     */
+                          /* most I / 128 are used)                              */
   int32_t tile_order;     /* workgroup order of the LDS-tiled GEMMs: 1 = row     */
                           /* tile-major; 2 = each row tile's column tiles on one */
                           /* XCD, row tiles interleaved over the 8 XCDs;         */

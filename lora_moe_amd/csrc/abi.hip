@@ -35,7 +35,7 @@ static int check_shape(const moe_lora_shape* s) {
   if (s->shrink_splits < 0 || s->shrink_splits > 64) return MOE_LORA_EINVAL;
   const int zb = s->shrink_zblocks;
   if (zb < 0 || (zb > 1 && (s->r % zb || (s->r / zb) % 8))) return MOE_LORA_EINVAL;
-  if (s->down_splits < 0 || s->down_splits > 8) return MOE_LORA_EINVAL;
+  if (s->down_splits < 0 || s->down_splits > 64) return MOE_LORA_EINVAL;
   if (s->tile_order < 0 || s->tile_order > 2) return MOE_LORA_EINVAL;
   if (s->expand_mode < 0 || s->expand_mode > 2) return MOE_LORA_EINVAL;
   return MOE_LORA_OK;

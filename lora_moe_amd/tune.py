@@ -64,7 +64,7 @@ def knob_candidates(wl, bm: int) -> dict:
     K = {"shrink_splits": [1, 2, 4, 8, 16],
          "shrink_zblocks": [d for d in (1, 2, 4, 8) if wl.r % d == 0 and (wl.r // d) % 8 == 0]}
     if bm <= 32 or wl.I >= 4096:  # the streaming down GEMM runs
-        K["down_splits"] = [1, 2, 4, 8]
+        K["down_splits"] = [1, 2, 4, 8, 10, 12, 16]
     if bm >= 64:  # the LDS-tiled GEMMs run
         K["tile_order"] = [1, 2]
         if wl.L <= 64:  # both forms of their expand can run

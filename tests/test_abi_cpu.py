@@ -276,10 +276,10 @@ def test_kernel_knob_validation(lib):
     """Kernel configuration fields: 0 or an allowed value, else EINVAL; the
     down-GEMM K split shows in the workspace view (streaming family only)."""
     base = dict(T=40, H=256, I=512, E=4, topk=2, L=2, r=32)
-    ok = [dict(shrink_splits=64), dict(shrink_zblocks=4), dict(shrink_zblocks=2), dict(down_splits=8),
+    ok = [dict(shrink_splits=64), dict(shrink_zblocks=4), dict(shrink_zblocks=2), dict(down_splits=8), dict(down_splits=64),
           dict(tile_order=2), dict(expand_mode=1), dict(expand_mode=2)]
     bad = [dict(shrink_splits=65), dict(shrink_splits=-1), dict(shrink_zblocks=3), dict(shrink_zblocks=8),
-           dict(down_splits=9), dict(tile_order=3), dict(expand_mode=3), dict(expand_mode=-1)]
+           dict(down_splits=65), dict(tile_order=3), dict(expand_mode=3), dict(expand_mode=-1)]
     for k in ok:
         assert lm.moe_lora_workspace_bytes(lm.make_shape(**base, **k)) > 0, k
     for k in bad:
