@@ -122,6 +122,41 @@ def test_random_large_shape(i):
         compare_delta(y[toks], y0[toks], ref, ref0, what)
 
 
+N_DENSE = 16
+
+
+def draw_dense(i):
+    """Dense case i: one expert and at most 32 pairs (one row tile), where
+    the gate_up spreads its ceil(I / 8) column groups evenly over the
+    workgroups; I up to 6000 gives 1 to 3 groups per workgroup, ragged."""
+    rng = np.random.default_rng(13000 + i)
+    k = 1
+    T = int(rng.integers(1, 33))
+    H = int(rng.integers(1, 65)) * 8
+    I = int(rng.integers(1, 751)) * 8
+    L = int(rng.choice([1, 3, 8]))
+    r = int(rng.choice([8, 16, 32, 64]))
+    bm = int(rng.choice([0, 32]))
+    mode = str(rng.choice(["uniform", "uniform_with_none"]))
+    wl = synth.Workload(f"random-dense-{i}", T=T, H=H, I=I, E=1, topk=k, L=L, r=r, lora_mode=mode,
+                        seed=14000 + i)
+    return wl, bm
+
+
+@pytest.mark.parametrize("i", range(N_DENSE))
+def test_random_dense(i):
+    import lora_moe_amd as lm
+    wl, bm = draw_dense(i)
+    what = f"dense case {i}: T={wl.T} H={wl.H} I={wl.I} L={wl.L} r={wl.r} {wl.lora_mode} bm={bm}"
+    log(what)
+    inp = synth.make_inputs(wl)
+    dev = to_device(inp)
+    y, shape, ws = run_gpu(dev, wl, bm)
+    assert lm.moe_lora_device_errors(shape, ws) == 0, what
+    ref = oracle_tokens(inp, None)
+    compare(y, ref, what)
+
+
 N_ALIGN = 64
 
 
