@@ -94,6 +94,27 @@ def test_bad_shapes(lib):
         assert rc == code, over
 
 
+def test_size_limits(lib):
+    """The index-width limits, each met alone: one under it is accepted, at
+    it refused with EUNSUPPORTED (x rows and the intermediate rows are read
+    through 32-bit byte offsets, one expert's weights through 32-bit element
+    offsets; cap = T*topk + 255*E rows)."""
+    small = dict(E=1, topk=1, L=1, r=8)
+    pairs = [  # (accepted, refused)
+        (dict(T=(1 << 24) - 1, H=64, I=8), dict(T=1 << 24, H=64, I=8)),          # T*H*2 vs 2^31
+        (dict(T=1, H=32768, I=65528), dict(T=1, H=32768, I=65536)),            # 2*I*H vs 2^32
+        (dict(T=(1 << 26) - 256, H=8, I=16), dict(T=(1 << 26) - 255, H=8, I=16)),  # cap*I*2 vs 2^31
+    ]
+    for ok, bad in pairs:
+        assert lm.moe_lora_workspace_bytes(lm.make_shape(**dict(small, **ok))) > 0, ok
+        s = lm.make_shape(**dict(small, **bad))
+        assert lm.moe_lora_resolve_block_m(s) == lm.MOE_LORA_EUNSUPPORTED, bad
+        assert lm.moe_lora_workspace_bytes(s) == 0, bad
+    # more pairs than 2^30
+    s = lm.make_shape(**dict(small, T=(1 << 26) + 1, H=8, I=8, E=16, topk=16))
+    assert lm.moe_lora_resolve_block_m(s) == lm.MOE_LORA_EUNSUPPORTED
+
+
 def test_null_and_workspace_checks_do_not_launch(lib):
     s = lm.make_shape(4, 64, 32, 4, 2, 2, 8)
     need = lm.moe_lora_workspace_bytes(s)
