@@ -18,9 +18,12 @@
 //   2. bucket scan: per key, exclusive prefix of the chunk counts (one
 //      wavefront per key) and the key total;
 //   3. offsets: one workgroup scans expert sizes (padded to block_m), writes
-//      segment starts, block -> expert map, pad sentinels and the list of
+//      segment starts, the block -> expert map of the runs and the list of
 //      shrink tiles (<= TS rows of one segment each);
 //   4. place: row of pair p = segment start + chunk prefix + rank.
+// The count pass also fills every row with the pad sentinel and every block
+// with -1 (a share per workgroup), so that the offsets pass, a single
+// workgroup, writes only what depends on the scan.
 // Small batches (at most 1024 pairs, decode) run all of it in one
 // single-workgroup kernel instead, with the counts and offsets in LDS.
 #include <algorithm>
@@ -152,12 +155,21 @@ __device__ __forceinline__ void clear_z_rows(int row, int r, int zero_gu, int ze
 __global__ __launch_bounds__(kAlignChunk) void align_count_kernel(
     const int32_t* __restrict__ topk_ids, const int32_t* __restrict__ lora_ids, int P, int k, int E,
     int L, int NB, int C, int32_t* __restrict__ chunk_cnt, int32_t* __restrict__ chunk_err,
-    int32_t* __restrict__ rank) {
+    int32_t* __restrict__ rank, int32_t* __restrict__ sorted, int32_t* __restrict__ bexp,
+    int64_t cap_rows, int64_t cap_blocks) {
   extern __shared__ __attribute__((aligned(16))) int lds[];
   int* wkeys = lds;                // [kAlignChunk]
   int* errs = wkeys + kAlignChunk; // [1]
   int* hist = errs + 1;            // [NB]
   const int tid = threadIdx.x, c = blockIdx.x;
+  // this workgroup's share of the sentinel fill (the place pass overwrites
+  // the real rows, the offsets pass the blocks of the runs)
+  {
+    const int64_t rs = (cap_rows + C - 1) / C, r0 = c * rs, r1 = min(cap_rows, r0 + rs);
+    for (int64_t row = r0 + tid; row < r1; row += blockDim.x) sorted[row] = P;
+    const int64_t bs = (cap_blocks + C - 1) / C, b0 = c * bs, b1 = min(cap_blocks, b0 + bs);
+    for (int64_t blk = b0 + tid; blk < b1; blk += blockDim.x) bexp[blk] = -1;
+  }
   for (int b = tid; b < NB; b += blockDim.x) hist[b] = 0;
   if (tid == 0) errs[0] = 0;
   const int p = c * kAlignChunk + tid;
@@ -198,16 +210,14 @@ __global__ __launch_bounds__(256) void align_bucket_scan_kernel(int NB, int C,
 }
 
 __global__ __launch_bounds__(1024) void align_offsets_kernel(
-    int P, int E, int L, int C, int bm, int64_t cap_rows, int64_t cap_blocks, int TS,
-    const int32_t* __restrict__ chunk_err, const int32_t* __restrict__ segcnt,
-    int32_t* __restrict__ hdr, int32_t* __restrict__ sorted, int32_t* __restrict__ eoff,
+    int E, int L, int C, int bm, int TS, const int32_t* __restrict__ chunk_err,
+    const int32_t* __restrict__ segcnt, int32_t* __restrict__ hdr, int32_t* __restrict__ eoff,
     int32_t* __restrict__ segstart, int32_t* __restrict__ bexp, LoraTile* __restrict__ tiles) {
   extern __shared__ int lds[];
   const int tid = threadIdx.x, nt = blockDim.x, S = L + 1, NB = E * S;
   int* scan = lds;              // [16]
   int* s_eoff = scan + 16;      // [E+1] run starts
-  int* s_n = s_eoff + E + 1;    // [E] real rows per expert
-  int* s_cnt = s_n + E;         // [NB] rows per (expert, slot)
+  int* s_cnt = s_eoff + E + 1;  // [NB] rows per (expert, slot); then the segment starts
   for (int b = tid; b < NB; b += nt) s_cnt[b] = segcnt[b];
   int errs = 0;
   for (int c = tid; c < C; c += nt) errs += chunk_err[c];
@@ -220,7 +230,6 @@ __global__ __launch_bounds__(1024) void align_offsets_kernel(
   for (int e = e0; e < e1; ++e) {
     int n = 0;
     for (int sl = 0; sl < S; ++sl) n += s_cnt[e * S + sl];
-    s_n[e] = n;
     local += (n + bm - 1) / bm * bm;
   }
   int total;
@@ -230,8 +239,10 @@ __global__ __launch_bounds__(1024) void align_offsets_kernel(
     eoff[e] = at;
     int n = 0;
     for (int sl = 0; sl < S; ++sl) {
+      const int cnt = s_cnt[e * S + sl];
       segstart[e * S + sl] = at + n;
-      n += s_cnt[e * S + sl];
+      s_cnt[e * S + sl] = at + n;  // start in place of the count (slot L ends the slots before it)
+      n += cnt;
     }
     at += (n + bm - 1) / bm * bm;
   }
@@ -242,27 +253,30 @@ __global__ __launch_bounds__(1024) void align_offsets_kernel(
   int nerr;
   block_exclusive_scan<true>(errs, scan, &nerr);  // also orders the s_eoff writes before the reads below
   const int num_padded = total;
-  write_pads_and_blocks(sorted, bexp, s_eoff, s_n, E, P, bm, cap_rows, cap_blocks);
+  // block -> expert map of the runs, a thread per expert (the count pass
+  // wrote -1 everywhere, the place pass writes the real rows; the padding
+  // rows keep the count pass's sentinel)
+  for (int e = tid; e < E; e += nt) {
+    const int a = s_eoff[e], b = s_eoff[e + 1];
+    for (int blk = a / bm; blk < b / bm; ++blk) bexp[blk] = e;
+  }
 
   // shrink tiles: segments (e, l < L) cut into pieces of <= TS rows; a
-  // thread owns consecutive segments, so their starts follow from the run
-  // start and the counts
+  // thread owns consecutive segments; segment (e, l) spans the starts of
+  // slots l and l + 1
   const int NS = E * L;
   const int perS = (NS + nt - 1) / nt;
   const int s0 = min(NS, tid * perS), s1 = min(NS, s0 + perS);
   int lt = 0;
-  for (int i = s0; i < s1; ++i) lt += (s_cnt[(i / L) * S + i % L] + TS - 1) / TS;
+  for (int i = s0; i < s1; ++i) {
+    const int b = (i / L) * S + i % L;
+    lt += (s_cnt[b + 1] - s_cnt[b] + TS - 1) / TS;
+  }
   int ntiles;
   int tb = block_exclusive_scan<true>(lt, scan, &ntiles);
-  int st = 0, cur_e = -1;
   for (int i = s0; i < s1; ++i) {
-    const int e = i / L, l = i % L;
-    if (e != cur_e) {  // first segment of this expert in the range
-      cur_e = e;
-      st = s_eoff[e];
-      for (int l2 = 0; l2 < l; ++l2) st += s_cnt[e * S + l2];
-    }
-    const int cnt = s_cnt[e * S + l];
+    const int e = i / L, l = i % L, b = e * S + l;
+    const int st = s_cnt[b], cnt = s_cnt[b + 1] - st;
     for (int o = 0; o < cnt; o += TS) {
       LoraTile tl;
       tl.e = e;
@@ -271,7 +285,6 @@ __global__ __launch_bounds__(1024) void align_offsets_kernel(
       tl.n = min(TS, cnt - o);
       tiles[tb++] = tl;
     }
-    st += cnt;
   }
   if (tid == 0) {
     hdr[HDR_NUM_PADDED] = num_padded;
@@ -456,20 +469,20 @@ int launch_align(const Layout& L, const int32_t* topk_ids, const int32_t* lora_i
   }
   prof_stage_begin(pr, ST_ALIGN_COUNT, st);
   align_count_kernel<<<C, kAlignChunk, (kAlignChunk + 1 + NB) * sizeof(int), st>>>(
-      topk_ids, lora_ids, P, L.k, L.E, L.L, NB, C, w.chunk, w.chunkerr, w.rank);
+      topk_ids, lora_ids, P, L.k, L.E, L.L, NB, C, w.chunk, w.chunkerr, w.rank, w.sorted, w.bexp, L.cap_rows,
+      L.cap_blocks);
   align_bucket_scan_kernel<<<(NB + 3) / 4, 256, 0, st>>>(NB, C, w.chunk, w.segcnt);
   prof_stage_end(pr, ST_ALIGN_COUNT, st);
   prof_stage_begin(pr, ST_ALIGN_PLACE, st);
-  const size_t off_lds = sizeof(int) * (16 + 2 * (size_t)L.E + 1 + NB);
-  if (off_lds > 64 * 1024) {  // above the default dynamic LDS limit (at most 115 KB here)
+  const size_t off_lds = sizeof(int) * (16 + (size_t)L.E + 1 + NB);
+  if (off_lds > 64 * 1024) {  // above the default dynamic LDS limit (at most 86 KB here)
     static std::atomic<uint64_t> attr_done{0};
     const int rc = ensure_dynamic_lds(reinterpret_cast<const void*>(&align_offsets_kernel), 160 * 1024,
                                       attr_done);
     if (rc) return rc;
   }
-  align_offsets_kernel<<<1, 1024, off_lds, st>>>(
-      P, L.E, L.L, C, L.bm, L.cap_rows, L.cap_blocks, (int)L.TS, w.chunkerr, w.segcnt, w.hdr,
-      w.sorted, w.eoff, w.segstart, w.bexp, w.tiles);
+  align_offsets_kernel<<<1, 1024, off_lds, st>>>(L.E, L.L, C, L.bm, (int)L.TS, w.chunkerr, w.segcnt, w.hdr,
+                                                  w.eoff, w.segstart, w.bexp, w.tiles);
   align_place_kernel<<<(P + 255) / 256, 256, 0, st>>>(topk_ids, lora_ids, P, L.k, L.E, L.L, C, L.r,
                                                       zero_gu, zero_d, w.chunk, w.rank, w.segstart,
                                                       w.sorted, w.pos, w.zgu, w.zd);
