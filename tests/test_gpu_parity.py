@@ -215,6 +215,26 @@ def test_thin_tiles(H, I):
     full_check(inp, 256, f"thin tiles H={H} I={I}")
 
 
+@pytest.mark.parametrize("r,mode", [(16, 1), (64, 1), (64, 2)])
+def test_thin_tiles_192(r, mode):
+    """block_m 192 with experts of 1, 96, 97, 127, 128, 129, 160, 192, 300
+    and 320 rows: tiles with at most 128 real rows (an expert's only tile,
+    or the last of 300 and 320 with 108 and 128) run on the 192 x 256
+    tile's thin ring of 128-row stages, the others on the full ring; rank 16
+    runs the register expand inside the loop (whose item loads the thin loop
+    issues before the stage's copies), rank 64 the register or the stage
+    form."""
+    counts = [1, 96, 97, 127, 128, 129, 160, 192, 300, 320]
+    wl = synth.Workload("thin192", T=sum(counts), H=256, I=256, E=len(counts), topk=1, L=5, r=r,
+                        lora_mode="uniform_with_none", seed=15)
+    inp = synth.make_inputs(wl)
+    ids = np.repeat(np.arange(len(counts), dtype=np.int32), counts)
+    np.random.default_rng(15).shuffle(ids)
+    inp.topk_ids[:, 0] = ids
+    inp.topk_weights[:] = 1.0
+    full_check(inp, 192, f"thin tiles 192 r={r} expand_mode={mode}", knobs=dict(expand_mode=mode))
+
+
 def _expand_case(case):
     """Workloads for the two forms of the tiled GEMMs' expand: (inputs, block_m)."""
     if case == "thin":  # experts of 1 .. 513 rows at block_m 256, rank 64
