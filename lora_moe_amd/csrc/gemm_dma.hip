@@ -531,12 +531,18 @@ __global__ __launch_bounds__(C::NT, WAVES_PER_SIMD) void grouped_gemm_dma_kernel
         xitem();
         if (q + RNS < nst) issue(q + RNS, nt_c, thin_c);  // into the slot stage q just released
       } else {
-        if (q + RNS < nst) issue(q + RNS, nt_c, thin_c);
+        // the second row half's wavefronts (the other wavefront on each
+        // SIMD) issue their copies after the slice, so that one wavefront
+        // of every SIMD multiplies while the other issues
+        if (!wm && q + RNS < nst) issue(q + RNS, nt_c, thin_c);
         xitem();
       }
       // last slice of stage q (its fragments are in registers), with the
       // first reads of stage q + 1
       if (LIVE) step((KK - 1) & 1, true, q + 1, 0, thin_c, all_c);
+      if constexpr (!THIN) {
+        if (wm && q + RNS < nst) issue(q + RNS, nt_c, thin_c);
+      }
     }
     if (LIVE) {  // the last stage
 #pragma unroll
